@@ -1,0 +1,271 @@
+"""Throughput of the owner-side Muon step on one MI355X.
+
+A step is the owner's whole per-step work on its share of matrices: momentum
+accumulation and Frobenius normalisation, ns_steps Newton-Schulz iterations
+(bf16 MFMA), the scaled parameter update (all in ``dmuon_muon_step``, with the
+gradients read in place from the owner's packed gradient buffer), then
+``dmuon_pack`` of the updated parameters into the packed buffer the owner
+broadcasts.  Inputs are seeded synthetic tensors already resident in HBM.
+
+Prints one JSON line.  ``value`` is algorithmic Newton-Schulz TFLOP/s over
+the whole step time (symmetric products counted as their upper triangle:
+m(m+1)n + m^2(m+1) + 2m^2 n per matrix per iteration).
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import faulthandler
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X dense fp32 MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "Muon step: NS TFLOP/s (% bf16 MFMA peak) + matrices/s on one owner's share"
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def ns_flops(m: int, n: int, k: int) -> dict:
+    """Algorithmic flops of k iterations on an m x n (m <= n) matrix."""
+    return {"gram": k * m * (m + 1) * n, "square": k * m * m * (m + 1),
+            "apply": k * 2 * m * m * n}
+
+
+class TraceEvents:
+    """One step's worth of timing events (torch's HIP events, created by a
+    first record) whose raw handles the traced step re-records."""
+
+    def __init__(self, n: int, stream):
+        import torch
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in self.ev:
+            e.record(stream)
+        self.handles = (ctypes.c_void_p * n)(*[e.cuda_event for e in self.ev])
+
+    def elapsed_ms(self, j: int) -> float:
+        return self.ev[j].elapsed_time(self.ev[j + 1])
+
+
+def owner_share(w, nsd):
+    shapes = w.shapes
+    if w.n_owners > 1:
+        owners, _ = nsd.partition_lpt([r * c for _, r, c in shapes], w.n_owners)
+        shapes = [s for s, o in zip(shapes, owners) if o == w.owner]
+    return shapes
+
+
+def cpu_baseline(w, shapes, ns_steps, budget_s: float):
+    """Times the fp64 oracle on a bounded sample of the workload's matrices
+    (one matrix per distinct shape, smallest first, while the budget lasts)."""
+    import numpy as np
+    from oracle import muon as ref
+    from synth import normal, update_scale
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    seen, sample = set(), []
+    for idx, (name, r, c) in enumerate(shapes):
+        if (r, c) not in seen:
+            seen.add((r, c))
+            sample.append((idx, name, r, c))
+    sample.sort(key=lambda s: s[2] * s[3])
+    cfg = ref.StepConfig(ns_steps=ns_steps)
+    flops, done, t_total = 0, [], 0.0
+    for idx, name, r, c in sample:
+        P = normal(w.wid, idx, 1, r, c, w.param_std, w.param_dtype)
+        G = normal(w.wid, idx, 0, r, c, w.grad_std, w.grad_dtype)
+        M = np.zeros((r, c), np.float32)
+        t0 = time.perf_counter()
+        ref.muon_step_matrix(P, G, M, update_scale(r, c), cfg)
+        dt = time.perf_counter() - t0
+        t_total += dt
+        flops += sum(ns_flops(min(r, c), max(r, c), ns_steps).values())
+        done.append(f"{name.split('.')[-1]} {r}x{c}")
+        log(f"cpu oracle {r}x{c}: {dt:.2f} s")
+        if t_total > budget_s:
+            break
+    return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "matrices_per_s": round(len(done) / t_total, 4),
+            "seconds": round(t_total, 3),
+            "sample": f"fp64 NumPy oracle, one step of {len(done)} matrices "
+                      f"({', '.join(done)}), algorithmic NS flops / wall time"}
+
+
+def main(argv=None) -> int:
+    faulthandler.enable()
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="4", help="workload id or name (synth.workloads)")
+    ap.add_argument("--ns-steps", type=int, default=None)
+    ap.add_argument("--fp32-ns", action="store_true", help="fp32 checking mode")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs the owner's step on one GPU; "
+                                   "--gpus above 1 is not supported"}))
+        return 2
+
+    import torch
+
+    import newton_schulz_dmuon_amd as nsd
+    from synth import update_scale, workload
+
+    key = int(args.workload) if args.workload.isdigit() else args.workload
+    w = workload(key)
+    K = args.ns_steps if args.ns_steps is not None else w.ns_steps
+    nsd.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    shapes = owner_share(w, nsd)
+    numels = [r * c for _, r, c in shapes]
+    offsets, total = nsd.pack_offsets(numels, 128)
+    pdt = torch.bfloat16 if w.param_dtype == "bf16" else torch.float32
+    gdt = torch.bfloat16 if w.grad_dtype == "bf16" else torch.float32
+    log(f"workload {w.name}: {len(shapes)} matrices, {sum(numels):,} elements, ns_steps {K}")
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234 + w.wid)
+    grad_packed = torch.empty(total, dtype=gdt, device=dev)
+    param_packed = torch.empty(total, dtype=pdt, device=dev)
+    P, G, M = [], [], []
+    for (name, r, c), off in zip(shapes, offsets):
+        g = grad_packed[off:off + r * c].view(r, c)
+        g.copy_(torch.randn(r, c, generator=gen, device=dev) * w.grad_std)
+        G.append(g)
+        P.append((torch.randn(r, c, generator=gen, device=dev) * w.param_std).to(pdt))
+        M.append(torch.zeros(r, c, dtype=torch.float32, device=dev))
+    scales = [update_scale(r, c) for _, r, c in shapes]
+    opts = nsd.StepOptions(ns_steps=K, ns_fp32=args.fp32_ns)
+    ws = nsd.Workspace()
+    ws_bytes = nsd.workspace_bytes(P, opts)
+    wsbuf = ws.get(ws_bytes, dev)
+    log(f"workspace {ws_bytes / 2**30:.2f} GiB")
+
+    lib = nsd.load()
+    arr, n = nsd.api.matrices(P, G, M, scales)
+    cfg = opts.to_c()
+    stream = torch.cuda.current_stream(dev)
+    n_launch = 3 + 3 * K if K > 0 else 3
+
+    def step(ev=None):
+        if ev is None:
+            rc = lib.dmuon_muon_step(arr, n, ctypes.byref(cfg), wsbuf.data_ptr(), wsbuf.numel(),
+                                     stream.cuda_stream)
+        else:
+            rc = lib.dmuon_muon_step_traced(arr, n, ctypes.byref(cfg), wsbuf.data_ptr(),
+                                            wsbuf.numel(), stream.cuda_stream, ev.handles,
+                                            len(ev.handles))
+        nsd._lib.check(rc)
+        nsd.pack(P, offsets, param_packed, stream=stream)
+
+    for i in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} done")
+
+    evs = [TraceEvents(n_launch + 1, stream) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms = dt * 1e3 / args.steps
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step")
+
+    # per-launch durations from the traced events
+    names = ["momentum_sumsq", "norm", "normalise_orient"] if K > 0 else \
+        ["momentum_sumsq", "norm", "update_direct"]
+    for k in range(K):
+        names += ["gram", "square", "final" if k == K - 1 else "apply"]
+    per = {nm: [] for nm in set(names)}
+    for ev in evs:
+        for j, nm in enumerate(names):
+            per[nm].append(ev.elapsed_ms(j))
+    avg = {nm: sum(v) / len(v) for nm, v in per.items()}
+
+    flops = {"gram": 0, "square": 0, "apply": 0}
+    for _, r, c in shapes:
+        for kk, v in ns_flops(min(r, c), max(r, c), K).items():
+            flops[kk] += v
+    ns_total = sum(flops.values())
+    ns_ms = sum(sum(v) for nm, v in per.items()
+                if nm in ("gram", "square", "apply", "final")) / args.steps
+    peak = PEAK_FP32_TFLOPS if args.fp32_ns else PEAK_BF16_TFLOPS
+    value = ns_total / (ms * 1e-3) / 1e12
+
+    stages = {}
+    if K > 0:
+        # per launch: one iteration's flops; apply and final share a shape
+        stages["gram"] = {"ms": avg["gram"], "tflops": flops["gram"] / K / (avg["gram"] * 1e-3) / 1e12}
+        stages["square"] = {"ms": avg["square"],
+                            "tflops": flops["square"] / K / (avg["square"] * 1e-3) / 1e12}
+        # Apply launches without the fused update (the dominant kernel); with
+        # ns_steps = 1 only the final launch exists
+        ap = per.get("apply") or per["final"]
+        apply_ms = sum(ap) / len(ap)
+        stages["apply"] = {"ms": apply_ms, "tflops": flops["apply"] / K / (apply_ms * 1e-3) / 1e12}
+        stages["final"] = {"ms": avg["final"],
+                           "tflops": flops["apply"] / K / (avg["final"] * 1e-3) / 1e12}
+    elem = sum(numels)
+    gbytes = {"momentum_sumsq": elem * (4 + 4 + (2 if w.grad_dtype == "bf16" else 4)),
+              "normalise_orient": elem * (4 + 2 * (4 if args.fp32_ns else 2))}
+    for nm, b in gbytes.items():
+        if nm in avg:
+            stages[nm] = {"ms": avg[nm], "gbs": b / (avg[nm] * 1e-3) / 1e9}
+    stages["norm"] = {"ms": avg["norm"]}
+    for v in stages.values():
+        for kk in list(v):
+            v[kk] = round(v[kk], 4)
+
+    roofline = None
+    if K > 0:
+        apply_flops = flops["apply"] / K
+        ach = apply_flops / (stages["apply"]["ms"] * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": "ns_gemm_kernel<Apply> (X <- aX + BX)",
+                    "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(ach / peak, 4), "traffic": None,
+                    "algorithmic_flops_per_launch": apply_flops}
+
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32" if args.fp32_ns else "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "matrices": len(shapes), "elements": elem,
+                   "ns_steps": K, "param_dtype": w.param_dtype, "grad_dtype": w.grad_dtype,
+                   "parallelism": "one owner's share on 1 GPU"},
+        "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "matrices_per_s": round(len(shapes) / (ms * 1e-3), 2),
+        "steps_per_s": round(1e3 / ms, 3),
+        "ns_kernels_ms": round(ns_ms, 4),
+        "ns_kernels_tflops": round(ns_total / (ns_ms * 1e-3) / 1e12, 3) if ns_ms else None,
+        "stages": stages,
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, shapes, K, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,196 @@
+/*
+ * dmuon.h -- C ABI of the MI355X (gfx950) owner-side Muon step.
+ *
+ * What is computed.  DMuon gives every Muon-target matrix parameter one owner
+ * rank; the owner holds the full parameter, receives the reduced gradient,
+ * and alone runs Newton-Schulz on it once per step (DMuon landing page,
+ * intro and "LLM Pretraining"; "Z2 vs Z3 Modes", "Byte cost per step").  This
+ * library is that owner's step over its list of matrices, on one GPU:
+ *
+ *   M <- mu*M + G                                  momentum accumulation
+ *   X <- U / (||U||_F + eps), U = M (or G + mu*M with Nesterov)
+ *        transposed to m x n, m = min(rows, cols) (wide orientation)
+ *   ns_steps times:  A = X X^T ;  X <- a X + (b A + c A^2) X
+ *   O = X back in rows x cols orientation
+ *   P <- P - lr * scale * O
+ *
+ * The pages name the iteration but print no coefficients, momentum rule,
+ * epsilon or scale; all are passed in (see dmuon_step_config).  The pack /
+ * unpack calls build the owner's single contiguous buffer of its matrices
+ * ("Z2 vs Z3 Modes", "The two packed-buffer lifecycles").  dmuon_partition_lpt
+ * is the balanced owner assignment (landing page, "MoE": balanced partition).
+ *
+ * Conventions for every call.
+ *   - Matrices are row-major and contiguous: element (i, j) of an r x c
+ *     matrix is at base[i*c + j].  Rows/cols are the PyTorch [out, in] shape.
+ *   - Device pointers must be 16-byte aligned; the workspace 256-byte aligned.
+ *   - The caller owns every buffer.  The library keeps no pointer after a
+ *     call returns; it does not allocate device memory.  It holds small
+ *     pinned host staging buffers for the per-call descriptor tables.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Device calls only
+ *     enqueue work and return; results are valid once the stream is
+ *     synchronised, and no buffer may be reused or freed before that.
+ *   - Return value: DMUON_OK (0) or a negative dmuon_status.  Every argument
+ *     is validated before the first launch: on an error nothing is enqueued
+ *     and no buffer is touched.  dmuon_last_error() gives a message (per
+ *     thread).  No C++ exception crosses this interface.
+ *   - Results are deterministic: the same inputs give bitwise equal outputs
+ *     (no floating-point atomics; every reduction has a fixed order).
+ */
+#ifndef DMUON_H
+#define DMUON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DMUON_ABI_VERSION 1
+
+typedef enum {
+  DMUON_OK = 0,
+  DMUON_ERR_INVALID_ARG = -1,       /* null pointer, bad size, bad value     */
+  DMUON_ERR_UNSUPPORTED_DTYPE = -2, /* dtype code unknown or not allowed     */
+  DMUON_ERR_ALIAS = -3,             /* an output overlaps another buffer     */
+  DMUON_ERR_WORKSPACE_TOO_SMALL = -4,
+  DMUON_ERR_MISALIGNED = -5,        /* pointer alignment rule broken         */
+  DMUON_ERR_HIP = -6                /* a HIP call or launch failed           */
+} dmuon_status;
+
+typedef enum { DMUON_BF16 = 0, DMUON_F32 = 1 } dmuon_dtype;
+
+/* Field selector of dmuon_pack / dmuon_unpack. */
+enum { DMUON_FIELD_PARAM = 0, DMUON_FIELD_GRAD = 1 };
+
+/* dmuon_step_config.flags */
+enum {
+  /* Keep X, A, B in fp32 through the Newton-Schulz chain (fp32 MFMA) instead
+   * of bf16.  A checking mode: slower, closer to exact arithmetic. */
+  DMUON_FLAG_NS_FP32 = 1u << 0,
+  /* Orthogonalise the look-ahead G + mu*M (after the momentum update)
+   * instead of M. */
+  DMUON_FLAG_NESTEROV = 1u << 1
+};
+
+/* One matrix of the owner's share. */
+typedef struct {
+  void *param;          /* rows x cols, param_dtype, updated in place        */
+  int32_t param_dtype;  /* DMUON_BF16 or DMUON_F32                           */
+  int32_t grad_dtype;   /* DMUON_BF16 or DMUON_F32                           */
+  const void *grad;     /* rows x cols, read only; may point into a packed
+                           gradient buffer                                   */
+  float *momentum;      /* rows x cols fp32 momentum buffer, updated in place */
+  void *orth_out;       /* NULL, or rows x cols in param_dtype: receives the
+                           Newton-Schulz output O                            */
+  int64_t rows, cols;   /* >= 1 each                                         */
+  float scale;          /* per-matrix update scale (finite)                  */
+  int32_t reserved;     /* must be 0                                         */
+  int64_t packed_offset;/* element offset of this matrix in the packed
+                           buffer (dmuon_pack / dmuon_unpack only)           */
+} dmuon_matrix;
+
+/* Step hyper-parameters.  The landing page's optimizer call uses lr = 0.02
+ * and ns_steps = 5 ("LLM Pretraining"); a, b, c, momentum and eps are not on
+ * the pages.  The public Muon quintic is (3.4445, -4.7750, 2.0315). */
+typedef struct {
+  float a, b, c;        /* iteration coefficients                            */
+  int32_t ns_steps;     /* 0 .. 64; 0 = normalised momentum update           */
+  float lr;             /* finite                                            */
+  float momentum;       /* mu, finite                                        */
+  float eps;            /* finite, >= 0                                      */
+  uint32_t flags;       /* DMUON_FLAG_*                                      */
+} dmuon_step_config;
+
+/* ABI version (DMUON_ABI_VERSION of the built library). */
+int dmuon_abi_version(void);
+
+/* Static text for a status code. */
+const char *dmuon_error_string(int status);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char *dmuon_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Host-only planning calls (no GPU needed).
+ */
+
+/* Balanced owner assignment, largest matrix first (landing page, "MoE").
+ * Matrices are visited by element count, largest first, equal counts in input
+ * order; each goes to the owner with the smallest load so far, equal loads to
+ * the lowest owner id.
+ *   numel[n]          element count of each matrix (>= 0)
+ *   owner_out[n]      receives the owner id of each matrix
+ *   load_out[n_owners] nullable; receives each owner's total element count
+ * Errors: INVALID_ARG for n < 0, n_owners < 1, negative numel, or a null
+ * array that n or n_owners requires. */
+int dmuon_partition_lpt(const int64_t *numel, int32_t n, int32_t n_owners,
+                        int32_t *owner_out, int64_t *load_out);
+
+/* Offsets of consecutive matrices in one packed buffer ("Z2 vs Z3 Modes",
+ * "The two packed-buffer lifecycles": one contiguous buffer per owner group).
+ * Matrix i starts at the end of matrix i-1 rounded up to a multiple of
+ * `align` elements; *total_out is the end of the last one rounded up too.
+ * Errors: INVALID_ARG for n < 0, align < 1, negative numel, null outputs. */
+int dmuon_pack_offsets(const int64_t *numel, int32_t n, int64_t align,
+                       int64_t *offset_out, int64_t *total_out);
+
+/* Bytes of device workspace dmuon_muon_step needs for these matrices and
+ * flags.  Host-only; validates like dmuon_muon_step except for pointers. */
+int dmuon_workspace_bytes(const dmuon_matrix *mats, int32_t n,
+                          const dmuon_step_config *cfg, size_t *out_bytes);
+
+/* ---------------------------------------------------------------------------
+ * Device calls.
+ */
+
+/* Copy the selected field (param or grad) of every matrix into `packed`:
+ *   packed[mats[i].packed_offset + r*cols + c] = field_i[r, c]
+ * Bit copy: packed_dtype must equal each matrix's field dtype.  Elements of
+ * `packed` outside the matrices are not written.
+ *   packed_numel  size of `packed` in elements; every matrix must fit.
+ * Errors: INVALID_ARG, UNSUPPORTED_DTYPE, MISALIGNED (packed + offset not
+ * 16-byte aligned), ALIAS (matrices overlap each other in `packed`, or
+ * `packed` overlaps a source), HIP. */
+int dmuon_pack(const dmuon_matrix *mats, int32_t n, int32_t field, void *packed,
+               int32_t packed_dtype, int64_t packed_numel, void *stream);
+
+/* Inverse of dmuon_pack: field_i[r, c] = packed[packed_offset + r*cols + c].
+ * For the grad field this writes through the (const) grad pointer: the
+ * caller must own that memory as writable. */
+int dmuon_unpack(const dmuon_matrix *mats, int32_t n, int32_t field,
+                 const void *packed, int32_t packed_dtype, int64_t packed_numel,
+                 void *stream);
+
+/* One owner-side Muon step over n matrices (n = 0 is a no-op).
+ *   workspace  device scratch of at least dmuon_workspace_bytes(); its
+ *              contents on entry do not matter and are undefined on exit.
+ * Writes: every param, momentum and (non-null) orth_out.  Reads: grads.
+ * Errors: INVALID_ARG (null pointer, rows/cols < 1, ns_steps out of range,
+ * non-finite lr/momentum/scale, eps < 0, unknown flag, reserved != 0),
+ * UNSUPPORTED_DTYPE, MISALIGNED, ALIAS (a written buffer overlaps any other
+ * buffer of the call, the workspace included), WORKSPACE_TOO_SMALL, HIP. */
+int dmuon_muon_step(const dmuon_matrix *mats, int32_t n,
+                    const dmuon_step_config *cfg, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/* dmuon_muon_step that also records caller-created HIP events (hipEvent_t,
+ * passed as void*) on `stream`, for per-kernel timing: events[0] before the
+ * first launch and events[j] right after the j-th launch.  Launch order:
+ * momentum + sum of squares, norm, then either the direct update
+ * (ns_steps = 0) or normalise/orient followed by Gram, Square, Apply for each
+ * iteration (the last Apply carries the parameter update).  Only the first
+ * n_events are recorded; n_events = 0 makes this dmuon_muon_step.
+ * Errors: those of dmuon_muon_step; INVALID_ARG for n_events < 0 or a NULL
+ * list with n_events > 0; HIP if an event cannot be recorded. */
+int dmuon_muon_step_traced(const dmuon_matrix *mats, int32_t n,
+                           const dmuon_step_config *cfg, void *workspace,
+                           size_t workspace_bytes, void *stream,
+                           void *const *events, int32_t n_events);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DMUON_H */

@@ -1,0 +1,9 @@
+"""MI355X (gfx950) owner-side DMuon Muon step.
+
+The computation lives in ``libdmuon.so`` (C ABI: ``include/dmuon.h``), built
+from the HIP sources in ``csrc/``.  This package is its thin binding.
+"""
+
+from ._lib import DmuonError, load  # noqa: F401
+from .api import (QUINTIC, StepOptions, Workspace, muon_step, pack, pack_offsets,  # noqa: F401
+                  partition_lpt, unpack, workspace_bytes)

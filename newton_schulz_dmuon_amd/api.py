@@ -1,0 +1,160 @@
+"""Python face of ``libdmuon.so`` over torch tensors.
+
+PyTorch only supplies device memory and the current HIP stream; every step of
+the owner's Muon update runs in the library's HIP kernels.  Each function
+here only fills the C structs and checks the returned status.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+from . import _lib
+from ._lib import DmuonError, Matrix, StepConfig, check, load
+
+# Public Muon quintic (Jordan et al., 2024); the DMuon pages print none.
+QUINTIC = (3.4445, -4.7750, 2.0315)
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.bfloat16:
+        return _lib.BF16
+    if t.dtype == torch.float32:
+        return _lib.F32
+    raise DmuonError(_lib.ERR_UNSUPPORTED_DTYPE, f"tensor dtype {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise DmuonError(_lib.ERR_INVALID_ARG, "tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream_handle(device, stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+@dataclass
+class StepOptions:
+    """``dmuon_step_config``.  ``lr`` and ``ns_steps`` defaults are the ones in
+    the DMuon landing page's optimizer call ("LLM Pretraining")."""
+
+    a: float = QUINTIC[0]
+    b: float = QUINTIC[1]
+    c: float = QUINTIC[2]
+    ns_steps: int = 5
+    lr: float = 0.02
+    momentum: float = 0.95
+    eps: float = 1e-7
+    nesterov: bool = False
+    ns_fp32: bool = False
+
+    def to_c(self) -> StepConfig:
+        flags = (_lib.FLAG_NESTEROV if self.nesterov else 0) | \
+                (_lib.FLAG_NS_FP32 if self.ns_fp32 else 0)
+        return StepConfig(self.a, self.b, self.c, int(self.ns_steps), self.lr,
+                          self.momentum, self.eps, flags)
+
+
+def matrices(params, grads=None, momenta=None, scales=None, orth_out=None,
+             packed_offsets=None):
+    """Builds the ``dmuon_matrix`` array from parallel tensor lists."""
+    n = len(params)
+    arr = (Matrix * max(n, 1))()
+    for i in range(n):
+        p = params[i]
+        if p.dim() != 2:
+            raise DmuonError(_lib.ERR_INVALID_ARG, f"matrix {i} is not 2-D")
+        g = grads[i] if grads is not None else None
+        m = momenta[i] if momenta is not None else None
+        o = orth_out[i] if orth_out is not None else None
+        arr[i] = Matrix(
+            _ptr(p), _dtype_code(p), _dtype_code(g) if g is not None else _dtype_code(p),
+            _ptr(g), _ptr(m), _ptr(o), p.shape[0], p.shape[1],
+            float(scales[i]) if scales is not None else 1.0, 0,
+            int(packed_offsets[i]) if packed_offsets is not None else 0)
+    return arr, n
+
+
+def workspace_bytes(params, opts: StepOptions) -> int:
+    arr, n = matrices(params)
+    out = ctypes.c_size_t(0)
+    cfg = opts.to_c()
+    check(load().dmuon_workspace_bytes(arr, n, ctypes.byref(cfg), ctypes.byref(out)))
+    return out.value
+
+
+class Workspace:
+    """Device scratch for ``muon_step``, grown on demand (PyTorch allocates)."""
+
+    def __init__(self):
+        self.buf = None
+
+    def get(self, nbytes: int, device):
+        import torch
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+            self.buf = None
+            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        return self.buf
+
+
+def muon_step(params: Sequence, grads: Sequence, momenta: Sequence, scales: Sequence[float],
+              opts: StepOptions = StepOptions(), orth_out: Optional[Sequence] = None,
+              workspace: Optional[Workspace] = None, stream=None) -> None:
+    """One owner-side Muon step over the matrices, in place on ``params`` and
+    ``momenta`` (and ``orth_out`` when given).  Enqueued on ``stream`` (the
+    current stream by default); synchronise before reading the results."""
+    n = len(params)
+    if n == 0:
+        return
+    device = params[0].device
+    arr, n = matrices(params, grads, momenta, scales, orth_out)
+    cfg = opts.to_c()
+    lib = load()
+    need = ctypes.c_size_t(0)
+    check(lib.dmuon_workspace_bytes(arr, n, ctypes.byref(cfg), ctypes.byref(need)))
+    ws = (workspace or Workspace()).get(need.value, device)
+    check(lib.dmuon_muon_step(arr, n, ctypes.byref(cfg), ws.data_ptr(), ws.numel(),
+                              _stream_handle(device, stream)))
+
+
+def pack(tensors: Sequence, offsets: Sequence[int], packed, stream=None) -> None:
+    """``packed[offsets[i] + r*cols + c] = tensors[i][r, c]`` (bit copy)."""
+    arr, n = matrices(tensors, packed_offsets=offsets)
+    check(load().dmuon_pack(arr, n, _lib.FIELD_PARAM, _ptr(packed), _dtype_code(packed),
+                            packed.numel(), _stream_handle(packed.device, stream)))
+
+
+def unpack(packed, tensors: Sequence, offsets: Sequence[int], stream=None) -> None:
+    """``tensors[i][r, c] = packed[offsets[i] + r*cols + c]`` (bit copy)."""
+    arr, n = matrices(tensors, packed_offsets=offsets)
+    check(load().dmuon_unpack(arr, n, _lib.FIELD_PARAM, _ptr(packed), _dtype_code(packed),
+                              packed.numel(), _stream_handle(packed.device, stream)))
+
+
+def partition_lpt(numels: Sequence[int], n_owners: int):
+    """Balanced ownership: ``(owner_of_matrix, load_of_owner)``."""
+    n = len(numels)
+    arr = (ctypes.c_int64 * max(n, 1))(*[int(x) for x in numels])
+    owners = (ctypes.c_int32 * max(n, 1))()
+    loads = (ctypes.c_int64 * max(n_owners, 1))()
+    check(load().dmuon_partition_lpt(arr, n, n_owners, owners, loads))
+    return list(owners[:n]), list(loads[:max(n_owners, 0)])
+
+
+def pack_offsets(numels: Sequence[int], align: int = 128):
+    """Aligned offsets of consecutive matrices in one buffer: ``(offsets, total)``."""
+    n = len(numels)
+    arr = (ctypes.c_int64 * max(n, 1))(*[int(x) for x in numels])
+    offs = (ctypes.c_int64 * max(n, 1))()
+    total = ctypes.c_int64(0)
+    check(load().dmuon_pack_offsets(arr, n, int(align), offs, ctypes.byref(total)))
+    return list(offs[:n]), total.value

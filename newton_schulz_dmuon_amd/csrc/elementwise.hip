@@ -1,0 +1,222 @@
+// Memory-bound stages of the owner's Muon step on gfx950: momentum + sum of
+// squares, the norm, normalise + cast + wide orientation, the direct update
+// (ns_steps = 0) and the packed-buffer copies.
+//
+// Every kernel here moves each byte once; they are bound by HBM bandwidth.
+// Loads and stores are 16-byte vectors where the layout allows, consecutive
+// lanes touch consecutive addresses, and the reductions run in a fixed order
+// in fp64 so the result does not depend on scheduling.
+
+#include "device_common.h"
+
+namespace dmuon {
+
+namespace {
+
+constexpr int kEwThreads = 256;
+constexpr int kEwPerThread = static_cast<int>(kEwChunk / kEwThreads);  // 32
+static_assert(kEwPerThread % 4 == 0, "4-wide vectors");
+
+__device__ __forceinline__ double block_sum_f64(double v, double *lds) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_down(v, off, 64);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) lds[wave] = v;
+  __syncthreads();
+  double s = 0.0;
+  if (threadIdx.x == 0)
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) s += lds[w];
+  return s;  // valid in thread 0
+}
+
+// Four consecutive grad values at flat index i (i multiple of 4).
+__device__ __forceinline__ f32x4 load_grad4(const void *g, int32_t dt, int64_t i) {
+  f32x4 r;
+  if (dt == kBF16) {
+    const uint2 v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(g) + i);
+    r[0] = __uint_as_float(v.x << 16);
+    r[1] = __uint_as_float(v.x & 0xffff0000u);
+    r[2] = __uint_as_float(v.y << 16);
+    r[3] = __uint_as_float(v.y & 0xffff0000u);
+  } else {
+    const float4 v = *reinterpret_cast<const float4 *>(static_cast<const float *>(g) + i);
+    r[0] = v.x; r[1] = v.y; r[2] = v.z; r[3] = v.w;
+  }
+  return r;
+}
+
+// M <- mu*M + G over one chunk; partial sum of U^2, U = M or G + mu*M.
+__global__ __launch_bounds__(kEwThreads) void momentum_sumsq_kernel(
+    const MatDev *__restrict__ mats, int32_t nmat, StepScalars s) {
+  __shared__ double red[kEwThreads / 64];
+  const int64_t w = blockIdx.x;
+  const int32_t mi = find_range(nmat, w, [&](int32_t i) { return mats[i].ew_first; });
+  const MatDev &d = mats[mi];
+  const int64_t numel = d.rows * d.cols;
+  const int64_t base = (w - d.ew_first) * kEwChunk;
+  const float mu = s.mu;
+  double acc = 0.0;
+#pragma unroll
+  for (int k = 0; k < kEwPerThread / 4; ++k) {
+    const int64_t i = base + (static_cast<int64_t>(k) * kEwThreads + threadIdx.x) * 4;
+    if (i + 4 <= numel) {
+      float4 mv = *reinterpret_cast<const float4 *>(d.mom + i);
+      const f32x4 g = load_grad4(d.grad, d.grad_dt, i);
+      mv.x = fmaf(mu, mv.x, g[0]);
+      mv.y = fmaf(mu, mv.y, g[1]);
+      mv.z = fmaf(mu, mv.z, g[2]);
+      mv.w = fmaf(mu, mv.w, g[3]);
+      *reinterpret_cast<float4 *>(d.mom + i) = mv;
+      float u0 = mv.x, u1 = mv.y, u2 = mv.z, u3 = mv.w;
+      if (s.nesterov) {
+        u0 = fmaf(mu, mv.x, g[0]); u1 = fmaf(mu, mv.y, g[1]);
+        u2 = fmaf(mu, mv.z, g[2]); u3 = fmaf(mu, mv.w, g[3]);
+      }
+      acc += (double)u0 * u0 + (double)u1 * u1 + (double)u2 * u2 + (double)u3 * u3;
+    } else {
+      for (int64_t j = i; j < numel && j < i + 4; ++j) {
+        const float g = load_elem(d.grad, d.grad_dt, j);
+        const float m = fmaf(mu, d.mom[j], g);
+        d.mom[j] = m;
+        const float u = s.nesterov ? fmaf(mu, m, g) : m;
+        acc += (double)u * u;
+      }
+    }
+  }
+  const double tot = block_sum_f64(acc, red);
+  if (threadIdx.x == 0) d.partials[w - d.ew_first] = tot;
+}
+
+// inv_norm = 1 / (sqrt(sum of the partials, in index order per thread) + eps)
+__global__ __launch_bounds__(256) void finalize_norm_kernel(const MatDev *__restrict__ mats,
+                                                            float eps) {
+  __shared__ double red[4];
+  const MatDev &d = mats[blockIdx.x];
+  double acc = 0.0;
+  for (int32_t i = threadIdx.x; i < d.ew_count; i += 256) acc += d.partials[i];
+  const double tot = block_sum_f64(acc, red);
+  if (threadIdx.x == 0) *d.inv_norm = static_cast<float>(1.0 / (sqrt(tot) + (double)eps));
+}
+
+// X0 = U * inv_norm in wide orientation, written as X (m_p x n_p) and X^T
+// (n_p x m_p), zero outside the m x n corner.  One 64 x 64 tile of X per
+// work-group, staged through LDS so both writes are row-contiguous.
+template <typename T>
+__global__ __launch_bounds__(256) void normalise_orient_kernel(
+    const MatDev *__restrict__ mats, int32_t nmat, StepScalars s) {
+  constexpr int TT = static_cast<int>(kTrTile);
+  __shared__ float tile[TT][TT + 1];
+  const int64_t w = blockIdx.x;
+  const int32_t mi = find_range(nmat, w, [&](int32_t i) { return mats[i].tr_first; });
+  const MatDev &d = mats[mi];
+  const int64_t t = w - d.tr_first;
+  const int64_t tiles_n = d.np / TT;
+  const int64_t i0 = (t / tiles_n) * TT, j0 = (t % tiles_n) * TT;  // X coords
+  const int64_t ur0 = d.transposed ? j0 : i0, uc0 = d.transposed ? i0 : j0;
+  const float inv = *d.inv_norm;
+  const float mu = s.mu;
+  // load U block (rows ur0.., cols uc0..) of the r x c caller matrix
+  for (int e = threadIdx.x; e < TT * TT; e += 256) {
+    const int p = e / TT, q = e % TT;
+    const int64_t ur = ur0 + p, uc = uc0 + q;
+    float v = 0.f;
+    if (ur < d.rows && uc < d.cols) {
+      const int64_t idx = ur * d.cols + uc;
+      float u = d.mom[idx];
+      if (s.nesterov) u = fmaf(mu, u, load_elem(d.grad, d.grad_dt, idx));
+      v = u * inv;
+    }
+    tile[p][q] = v;
+  }
+  __syncthreads();
+  T *X = static_cast<T *>(d.x[0]);
+  T *XT = static_cast<T *>(d.xt[0]);
+  for (int e = threadIdx.x; e < TT * TT; e += 256) {
+    const int a = e / TT, b = e % TT;
+    // X[i0 + a][j0 + b]
+    const float vx = d.transposed ? tile[b][a] : tile[a][b];
+    WsType<T>::st(X, (i0 + a) * d.np + j0 + b, vx);
+    // X^T[j0 + a][i0 + b] = X[i0 + b][j0 + a]
+    const float vt = d.transposed ? tile[a][b] : tile[b][a];
+    WsType<T>::st(XT, (j0 + a) * d.mp + i0 + b, vt);
+  }
+}
+
+// ns_steps = 0: O = U * inv_norm (already r x c), P -= lr*scale*O.
+__global__ __launch_bounds__(kEwThreads) void update_direct_kernel(
+    const MatDev *__restrict__ mats, int32_t nmat, StepScalars s) {
+  const int64_t w = blockIdx.x;
+  const int32_t mi = find_range(nmat, w, [&](int32_t i) { return mats[i].ew_first; });
+  const MatDev &d = mats[mi];
+  const int64_t numel = d.rows * d.cols;
+  const int64_t base = (w - d.ew_first) * kEwChunk;
+  const float inv = *d.inv_norm;
+  const float step = s.lr * d.scale;
+  for (int k = 0; k < kEwPerThread; ++k) {
+    const int64_t i = base + static_cast<int64_t>(k) * kEwThreads + threadIdx.x;
+    if (i >= numel) break;
+    float u = d.mom[i];
+    if (s.nesterov) u = fmaf(s.mu, u, load_elem(d.grad, d.grad_dt, i));
+    const float o = u * inv;
+    if (d.orth) store_elem(d.orth, d.param_dt, i, o);
+    store_elem(d.param, d.param_dt, i, fmaf(-step, o, load_elem(d.param, d.param_dt, i)));
+  }
+}
+
+constexpr int kPackThreads = 256;
+
+// Byte copies of a batch of matrices; 16-byte vectors for the body, bytes
+// for a tail shorter than 16.  Base pointers are 16-byte aligned.
+__global__ __launch_bounds__(kPackThreads) void pack_copy_kernel(PackBatch b) {
+  const int64_t w = blockIdx.x;
+  const int32_t ci = find_range(b.n, w, [&](int32_t i) { return b.first_block[i]; });
+  const int64_t begin = (w - b.first_block[ci]) * kPackBlockBytes;
+  const int64_t end = min(begin + kPackBlockBytes, b.bytes[ci]);
+  const char *src = static_cast<const char *>(b.src[ci]);
+  char *dst = static_cast<char *>(b.dst[ci]);
+  const int64_t vend = begin + ((end - begin) & ~static_cast<int64_t>(15));
+  for (int64_t o = begin + static_cast<int64_t>(threadIdx.x) * 16; o < vend;
+       o += kPackThreads * 16)
+    *reinterpret_cast<uint4 *>(dst + o) = *reinterpret_cast<const uint4 *>(src + o);
+  for (int64_t o = vend + threadIdx.x; o < end; o += kPackThreads) dst[o] = src[o];
+}
+
+}  // namespace
+
+hipError_t launch_momentum_sumsq(const MatDev *mats, int32_t nmat, int64_t total_chunks,
+                                 StepScalars s, hipStream_t st) {
+  hipLaunchKernelGGL(momentum_sumsq_kernel, dim3((uint32_t)total_chunks), dim3(kEwThreads), 0,
+                     st, mats, nmat, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize_norm(const MatDev *mats, int32_t nmat, float eps, hipStream_t st) {
+  hipLaunchKernelGGL(finalize_norm_kernel, dim3((uint32_t)nmat), dim3(256), 0, st, mats, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_normalise_orient(const MatDev *mats, int32_t nmat, int64_t total_tiles,
+                                   StepScalars s, bool fp32, hipStream_t st) {
+  if (fp32)
+    hipLaunchKernelGGL(normalise_orient_kernel<float>, dim3((uint32_t)total_tiles), dim3(256),
+                       0, st, mats, nmat, s);
+  else
+    hipLaunchKernelGGL(normalise_orient_kernel<uint16_t>, dim3((uint32_t)total_tiles),
+                       dim3(256), 0, st, mats, nmat, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_update_direct(const MatDev *mats, int32_t nmat, int64_t total_chunks,
+                                StepScalars s, hipStream_t st) {
+  hipLaunchKernelGGL(update_direct_kernel, dim3((uint32_t)total_chunks), dim3(kEwThreads), 0,
+                     st, mats, nmat, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_batch(const PackBatch &b, hipStream_t st) {
+  if (b.n == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_copy_kernel, dim3((uint32_t)b.first_block[b.n]), dim3(kPackThreads),
+                     0, st, b);
+  return hipGetLastError();
+}
+
+}  // namespace dmuon

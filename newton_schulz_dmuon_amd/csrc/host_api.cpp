@@ -1,0 +1,554 @@
+// C ABI of the owner-side Muon step: argument validation, the per-call plan
+// (orientation, padding, workspace layout, grouped launch tables) and the
+// launch sequence.  Every check runs before the first HIP call, so a
+// rejected call has no effect on any buffer.
+
+#include <algorithm>
+#include <cstdarg>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "../../include/dmuon.h"
+#include "internal.h"
+
+namespace dmuon {
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+int hip_fail(hipError_t e, const char *what) {
+  return fail(DMUON_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+int64_t elem_size(int32_t dt) { return dt == DMUON_F32 ? 4 : 2; }
+
+bool dtype_ok(int32_t dt) { return dt == DMUON_BF16 || dt == DMUON_F32; }
+
+constexpr int64_t kMaxDim = int64_t(1) << 31;
+constexpr int64_t kMaxNumel = int64_t(1) << 40;
+
+// ---------------------------------------------------------------- aliasing --
+struct Interval {
+  uintptr_t lo, hi;  // [lo, hi)
+  bool written;
+  const char *what;
+  int32_t index;
+};
+
+// Fails if a written interval overlaps any other interval.
+int check_aliasing(std::vector<Interval> &iv) {
+  std::sort(iv.begin(), iv.end(), [](const Interval &x, const Interval &y) {
+    return x.lo != y.lo ? x.lo < y.lo : x.hi < y.hi;
+  });
+  uintptr_t max_any = 0, max_written = 0;
+  const Interval *any_at = nullptr, *wr_at = nullptr;
+  for (const Interval &x : iv) {
+    if (x.hi <= x.lo) continue;
+    if (x.written && any_at && x.lo < max_any)
+      return fail(DMUON_ERR_ALIAS, "%s of matrix %d overlaps %s of matrix %d", x.what, x.index,
+                  any_at->what, any_at->index);
+    if (!x.written && wr_at && x.lo < max_written)
+      return fail(DMUON_ERR_ALIAS, "%s of matrix %d overlaps %s of matrix %d", x.what, x.index,
+                  wr_at->what, wr_at->index);
+    if (x.hi > max_any) { max_any = x.hi; any_at = &x; }
+    if (x.written && x.hi > max_written) { max_written = x.hi; wr_at = &x; }
+  }
+  return DMUON_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// ------------------------------------------------------------- validation --
+int validate_config(const dmuon_step_config *cfg) {
+  if (!cfg) return fail(DMUON_ERR_INVALID_ARG, "cfg is NULL");
+  if (cfg->ns_steps < 0 || cfg->ns_steps > 64)
+    return fail(DMUON_ERR_INVALID_ARG, "ns_steps %d outside [0, 64]", cfg->ns_steps);
+  const float vals[] = {cfg->a, cfg->b, cfg->c, cfg->lr, cfg->momentum, cfg->eps};
+  for (float v : vals)
+    if (!std::isfinite(v)) return fail(DMUON_ERR_INVALID_ARG, "non-finite step coefficient");
+  if (cfg->eps < 0.f) return fail(DMUON_ERR_INVALID_ARG, "eps < 0");
+  const uint32_t known = DMUON_FLAG_NS_FP32 | DMUON_FLAG_NESTEROV;
+  if (cfg->flags & ~known) return fail(DMUON_ERR_INVALID_ARG, "unknown flag bits 0x%x", cfg->flags & ~known);
+  return DMUON_OK;
+}
+
+int validate_shapes(const dmuon_matrix *mats, int32_t n) {
+  if (n < 0) return fail(DMUON_ERR_INVALID_ARG, "n < 0");
+  if (n > 0 && !mats) return fail(DMUON_ERR_INVALID_ARG, "mats is NULL");
+  for (int32_t i = 0; i < n; ++i) {
+    const dmuon_matrix &d = mats[i];
+    if (d.rows < 1 || d.cols < 1 || d.rows >= kMaxDim || d.cols >= kMaxDim ||
+        d.rows * d.cols > kMaxNumel)
+      return fail(DMUON_ERR_INVALID_ARG, "matrix %d: bad shape %lld x %lld", i,
+                  (long long)d.rows, (long long)d.cols);
+    if (!dtype_ok(d.param_dtype) || !dtype_ok(d.grad_dtype))
+      return fail(DMUON_ERR_UNSUPPORTED_DTYPE, "matrix %d: dtype codes %d/%d", i, d.param_dtype,
+                  d.grad_dtype);
+    if (d.reserved != 0) return fail(DMUON_ERR_INVALID_ARG, "matrix %d: reserved != 0", i);
+    if (!std::isfinite(d.scale)) return fail(DMUON_ERR_INVALID_ARG, "matrix %d: scale not finite", i);
+  }
+  return DMUON_OK;
+}
+
+// ------------------------------------------------------------------- plan --
+struct Plan {
+  std::vector<MatDev> mats;
+  std::vector<StageEntry> stage[3];  // gram, square, apply
+  int64_t stage_total[3] = {0, 0, 0};
+  int64_t ew_total = 0, tr_total = 0;
+  // workspace layout (byte offsets)
+  int64_t off_mats = 0, off_stage[3] = {0, 0, 0}, off_partials = 0, off_inv = 0, off_ns = 0;
+  int64_t table_bytes = 0;  // [0, table_bytes) is uploaded
+  int64_t total_bytes = 0;
+};
+
+// Builds the plan; with ws == nullptr only sizes are computed.
+void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg, char *ws,
+                Plan &p) {
+  const bool fp32 = cfg.flags & DMUON_FLAG_NS_FP32;
+  const int64_t es = fp32 ? 4 : 2;
+  const int K = cfg.ns_steps;
+  p.mats.resize(n);
+  int64_t ew = 0, tr = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    const dmuon_matrix &s = in[i];
+    MatDev &d = p.mats[i];
+    std::memset(&d, 0, sizeof d);
+    d.param = s.param;
+    d.grad = s.grad;
+    d.mom = s.momentum;
+    d.orth = s.orth_out;
+    d.rows = s.rows;
+    d.cols = s.cols;
+    d.transposed = s.rows > s.cols;
+    d.m = std::min(s.rows, s.cols);
+    d.n = std::max(s.rows, s.cols);
+    d.mp = round_up(d.m, kPad);
+    d.np = round_up(d.n, kPad);
+    d.tm = static_cast<int32_t>(d.mp / kGemmTile);
+    d.tn = static_cast<int32_t>(d.np / kGemmTile);
+    d.param_dt = s.param_dtype;
+    d.grad_dt = s.grad_dtype;
+    d.scale = s.scale;
+    d.ew_first = ew;
+    d.ew_count = static_cast<int32_t>((s.rows * s.cols + kEwChunk - 1) / kEwChunk);
+    ew += d.ew_count;
+    d.tr_first = tr;
+    tr += (d.mp / kTrTile) * (d.np / kTrTile);
+  }
+  p.ew_total = ew;
+  p.tr_total = K > 0 ? tr : 0;
+
+  // grouped launch order per stage: longest tiles first (K-depth of a tile
+  // is n_p for Gram, m_p for Square and Apply), ties in input order
+  for (int st = 0; st < 3; ++st) {
+    std::vector<int32_t> order(n);
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+      const int64_t kx = st == 0 ? p.mats[x].np : p.mats[x].mp;
+      const int64_t ky = st == 0 ? p.mats[y].np : p.mats[y].mp;
+      return kx > ky;
+    });
+    p.stage[st].clear();
+    int64_t first = 0;
+    for (int32_t i : order) {
+      const MatDev &d = p.mats[i];
+      const int64_t cnt = st < 2 ? int64_t(d.tm) * (d.tm + 1) / 2 : int64_t(d.tm) * d.tn;
+      p.stage[st].push_back(StageEntry{first, i, static_cast<int32_t>(cnt)});
+      first += cnt;
+    }
+    p.stage_total[st] = K > 0 ? first : 0;
+  }
+
+  // workspace layout
+  int64_t off = 0;
+  p.off_mats = off;
+  off = round_up(off + int64_t(sizeof(MatDev)) * n, 256);
+  for (int st = 0; st < 3; ++st) {
+    p.off_stage[st] = off;
+    off = round_up(off + int64_t(sizeof(StageEntry)) * n, 256);
+  }
+  p.table_bytes = off;
+  p.off_partials = off;
+  off = round_up(off + 8 * ew, 256);
+  p.off_inv = off;
+  off = round_up(off + 256 * int64_t(n), 256);  // one 256-byte slot per matrix
+  p.off_ns = off;
+  for (int32_t i = 0; i < n; ++i) {
+    MatDev &d = p.mats[i];
+    d.partials = ws ? reinterpret_cast<double *>(ws + p.off_partials) + d.ew_first : nullptr;
+    d.inv_norm = ws ? reinterpret_cast<float *>(ws + p.off_inv + 256 * int64_t(i)) : nullptr;
+    if (K == 0) continue;
+    const int64_t xb = d.mp * d.np * es, ab = d.mp * d.mp * es;
+    const int nbuf = K >= 2 ? 2 : 1;
+    for (int b = 0; b < nbuf; ++b) {
+      d.x[b] = ws ? ws + off : nullptr;
+      off = round_up(off + xb, 256);
+      d.xt[b] = ws ? ws + off : nullptr;
+      off = round_up(off + xb, 256);
+    }
+    d.a = ws ? ws + off : nullptr;
+    off = round_up(off + ab, 256);
+    d.b = ws ? ws + off : nullptr;
+    off = round_up(off + ab, 256);
+  }
+  p.total_bytes = off;
+}
+
+// ------------------------------------------------- pinned staging uploads --
+struct Slot {
+  void *host = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool pending = false;
+};
+struct Ring {
+  Slot slots[4];
+  int next = 0;
+};
+std::mutex g_ring_mu;
+std::map<int, Ring> g_rings;
+
+// Copies `bytes` of host data to device memory `dst` on `st`, through a
+// pinned staging slot that is reused only after its previous copy finished.
+int upload(void *dst, const std::vector<char> &src, hipStream_t st) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_ring_mu);
+  Ring &ring = g_rings[dev];
+  Slot &s = ring.slots[ring.next];
+  ring.next = (ring.next + 1) % 4;
+  if (s.pending) {
+    e = hipEventSynchronize(s.ev);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    s.pending = false;
+  }
+  if (!s.ev) {
+    e = hipEventCreateWithFlags(&s.ev, hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+  }
+  if (s.cap < src.size()) {
+    if (s.host) (void)hipHostFree(s.host);
+    s.host = nullptr;
+    s.cap = 0;
+    const size_t cap = std::max<size_t>(65536, src.size() * 2);
+    e = hipHostMalloc(&s.host, cap, hipHostMallocDefault);
+    if (e != hipSuccess) return hip_fail(e, "hipHostMalloc");
+    s.cap = cap;
+  }
+  std::memcpy(s.host, src.data(), src.size());
+  e = hipMemcpyAsync(dst, s.host, src.size(), hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+  e = hipEventRecord(s.ev, st);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  s.pending = true;
+  return DMUON_OK;
+}
+
+int check_launch(hipError_t e, const char *what) {
+  return e == hipSuccess ? DMUON_OK : hip_fail(e, what);
+}
+
+}  // namespace
+}  // namespace dmuon
+
+using namespace dmuon;
+
+extern "C" {
+
+int dmuon_abi_version(void) { return DMUON_ABI_VERSION; }
+
+const char *dmuon_error_string(int status) {
+  switch (status) {
+    case DMUON_OK: return "ok";
+    case DMUON_ERR_INVALID_ARG: return "invalid argument";
+    case DMUON_ERR_UNSUPPORTED_DTYPE: return "unsupported dtype";
+    case DMUON_ERR_ALIAS: return "overlapping buffers";
+    case DMUON_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case DMUON_ERR_MISALIGNED: return "misaligned pointer";
+    case DMUON_ERR_HIP: return "HIP error";
+    default: return "unknown status";
+  }
+}
+
+const char *dmuon_last_error(void) { return g_last_error.c_str(); }
+
+int dmuon_partition_lpt(const int64_t *numel, int32_t n, int32_t n_owners, int32_t *owner_out,
+                        int64_t *load_out) {
+  g_last_error.clear();
+  if (n < 0) return fail(DMUON_ERR_INVALID_ARG, "n < 0");
+  if (n_owners < 1) return fail(DMUON_ERR_INVALID_ARG, "n_owners < 1");
+  if (n > 0 && (!numel || !owner_out)) return fail(DMUON_ERR_INVALID_ARG, "NULL array");
+  for (int32_t i = 0; i < n; ++i)
+    if (numel[i] < 0) return fail(DMUON_ERR_INVALID_ARG, "numel[%d] < 0", i);
+  std::vector<int32_t> order(n);
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int32_t x, int32_t y) { return numel[x] > numel[y]; });
+  // owners keyed by (load, id): the smallest key takes the next matrix
+  std::vector<std::pair<int64_t, int32_t>> heap;
+  heap.reserve(n_owners);
+  for (int32_t r = 0; r < n_owners; ++r) heap.emplace_back(0, r);
+  auto cmp = [](const std::pair<int64_t, int32_t> &x, const std::pair<int64_t, int32_t> &y) {
+    return x > y;  // min-heap
+  };
+  std::make_heap(heap.begin(), heap.end(), cmp);
+  std::vector<int64_t> load(n_owners, 0);
+  for (int32_t i : order) {
+    std::pop_heap(heap.begin(), heap.end(), cmp);
+    auto [l, r] = heap.back();
+    owner_out[i] = r;
+    load[r] = l + numel[i];
+    heap.back() = {load[r], r};
+    std::push_heap(heap.begin(), heap.end(), cmp);
+  }
+  if (load_out) std::copy(load.begin(), load.end(), load_out);
+  return DMUON_OK;
+}
+
+int dmuon_pack_offsets(const int64_t *numel, int32_t n, int64_t align, int64_t *offset_out,
+                       int64_t *total_out) {
+  g_last_error.clear();
+  if (n < 0 || align < 1) return fail(DMUON_ERR_INVALID_ARG, "n < 0 or align < 1");
+  if (!total_out || (n > 0 && (!numel || !offset_out)))
+    return fail(DMUON_ERR_INVALID_ARG, "NULL array");
+  int64_t end = 0;
+  for (int32_t i = 0; i < n; ++i) {
+    if (numel[i] < 0) return fail(DMUON_ERR_INVALID_ARG, "numel[%d] < 0", i);
+    const int64_t start = round_up(end, align);
+    offset_out[i] = start;
+    end = start + numel[i];
+  }
+  *total_out = round_up(end, align);
+  return DMUON_OK;
+}
+
+int dmuon_workspace_bytes(const dmuon_matrix *mats, int32_t n, const dmuon_step_config *cfg,
+                          size_t *out_bytes) {
+  g_last_error.clear();
+  if (!out_bytes) return fail(DMUON_ERR_INVALID_ARG, "out_bytes is NULL");
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  rc = validate_shapes(mats, n);
+  if (rc) return rc;
+  Plan p;
+  build_plan(mats, n, *cfg, nullptr, p);
+  *out_bytes = static_cast<size_t>(p.total_bytes);
+  return DMUON_OK;
+}
+
+static int muon_step_impl(const dmuon_matrix *mats, int32_t n, const dmuon_step_config *cfg,
+                          void *workspace, size_t workspace_bytes, void *stream,
+                          void *const *events, int32_t n_events) {
+  g_last_error.clear();
+  if (n_events < 0 || (n_events > 0 && !events))
+    return fail(DMUON_ERR_INVALID_ARG, "bad event list");
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  rc = validate_shapes(mats, n);
+  if (rc) return rc;
+  if (n == 0) return DMUON_OK;
+
+  std::vector<Interval> iv;
+  iv.reserve(4 * n + 1);
+  for (int32_t i = 0; i < n; ++i) {
+    const dmuon_matrix &d = mats[i];
+    if (!d.param || !d.grad || !d.momentum)
+      return fail(DMUON_ERR_INVALID_ARG, "matrix %d: NULL param, grad or momentum", i);
+    if (!aligned16(d.param) || !aligned16(d.grad) || !aligned16(d.momentum) ||
+        (d.orth_out && !aligned16(d.orth_out)))
+      return fail(DMUON_ERR_MISALIGNED, "matrix %d: pointers must be 16-byte aligned", i);
+    const uintptr_t numel = static_cast<uintptr_t>(d.rows * d.cols);
+    auto add = [&](const void *ptr, int64_t es, bool w, const char *what) {
+      const uintptr_t lo = reinterpret_cast<uintptr_t>(ptr);
+      iv.push_back(Interval{lo, lo + numel * es, w, what, i});
+    };
+    add(d.param, elem_size(d.param_dtype), true, "param");
+    add(d.grad, elem_size(d.grad_dtype), false, "grad");
+    add(d.momentum, 4, true, "momentum");
+    if (d.orth_out) add(d.orth_out, elem_size(d.param_dtype), true, "orth_out");
+  }
+
+  rc = check_aliasing(iv);  // caller buffers among themselves
+  if (rc) return rc;
+  Plan p;
+  build_plan(mats, n, *cfg, nullptr, p);
+  if (workspace_bytes < static_cast<size_t>(p.total_bytes))
+    return fail(DMUON_ERR_WORKSPACE_TOO_SMALL, "workspace needs %lld bytes, got %zu",
+                (long long)p.total_bytes, workspace_bytes);
+  if (!workspace) return fail(DMUON_ERR_INVALID_ARG, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+    return fail(DMUON_ERR_MISALIGNED, "workspace must be 256-byte aligned");
+  {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(workspace);
+    iv.push_back(Interval{lo, lo + static_cast<uintptr_t>(p.total_bytes), true, "workspace", -1});
+  }
+  rc = check_aliasing(iv);  // and against the workspace
+  if (rc) return rc;
+
+  // ---- validated: plan with real addresses, upload tables, launch ----
+  char *ws = static_cast<char *>(workspace);
+  build_plan(mats, n, *cfg, ws, p);
+  std::vector<char> tables(static_cast<size_t>(p.table_bytes), 0);
+  std::memcpy(tables.data() + p.off_mats, p.mats.data(), sizeof(MatDev) * n);
+  for (int st = 0; st < 3; ++st)
+    std::memcpy(tables.data() + p.off_stage[st], p.stage[st].data(), sizeof(StageEntry) * n);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  rc = upload(ws, tables, s);
+  if (rc) return rc;
+
+  const MatDev *dm = reinterpret_cast<const MatDev *>(ws + p.off_mats);
+  const StageEntry *dst[3];
+  for (int st = 0; st < 3; ++st) dst[st] = reinterpret_cast<const StageEntry *>(ws + p.off_stage[st]);
+  StepScalars sc{cfg->a, cfg->b, cfg->c, cfg->lr, cfg->momentum, cfg->eps,
+                 (cfg->flags & DMUON_FLAG_NESTEROV) ? 1 : 0, 0};
+  const bool fp32 = cfg->flags & DMUON_FLAG_NS_FP32;
+
+  // events[0] before the first launch, events[j] after launch j
+  int32_t ev = 0;
+  auto mark = [&]() -> int {
+    if (ev < n_events) {
+      hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[ev]), s);
+      if (e != hipSuccess) return hip_fail(e, "hipEventRecord (trace)");
+    }
+    ++ev;
+    return DMUON_OK;
+  };
+  auto launched = [&](hipError_t e, const char *what) -> int {
+    const int r = check_launch(e, what);
+    return r ? r : mark();
+  };
+
+  if ((rc = mark())) return rc;
+  if ((rc = launched(launch_momentum_sumsq(dm, n, p.ew_total, sc, s), "momentum_sumsq launch")))
+    return rc;
+  if ((rc = launched(launch_finalize_norm(dm, n, cfg->eps, s), "finalize_norm launch"))) return rc;
+  if (cfg->ns_steps == 0)
+    return launched(launch_update_direct(dm, n, p.ew_total, sc, s), "update_direct launch");
+
+  if ((rc = launched(launch_normalise_orient(dm, n, p.tr_total, sc, fp32, s), "normalise launch")))
+    return rc;
+  for (int k = 0; k < cfg->ns_steps; ++k) {
+    const int32_t cur = k & 1;
+    const bool last = k + 1 == cfg->ns_steps;
+    if ((rc = launched(launch_ns_stage(kModeGram, fp32, dm, dst[0], n, p.stage_total[0], cur, sc, s),
+                       "gram launch")))
+      return rc;
+    if ((rc = launched(launch_ns_stage(kModeSquare, fp32, dm, dst[1], n, p.stage_total[1], cur, sc, s),
+                       "square launch")))
+      return rc;
+    if ((rc = launched(launch_ns_stage(last ? kModeFinal : kModeApply, fp32, dm, dst[2], n,
+                                       p.stage_total[2], cur, sc, s),
+                       "apply launch")))
+      return rc;
+  }
+  return DMUON_OK;
+}
+
+int dmuon_muon_step(const dmuon_matrix *mats, int32_t n, const dmuon_step_config *cfg,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+  return muon_step_impl(mats, n, cfg, workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+int dmuon_muon_step_traced(const dmuon_matrix *mats, int32_t n, const dmuon_step_config *cfg,
+                           void *workspace, size_t workspace_bytes, void *stream,
+                           void *const *events, int32_t n_events) {
+  return muon_step_impl(mats, n, cfg, workspace, workspace_bytes, stream, events, n_events);
+}
+
+// ------------------------------------------------------------ pack/unpack --
+static int pack_common(const dmuon_matrix *mats, int32_t n, int32_t field, void *packed_rw,
+                       const void *packed, int32_t packed_dtype, int64_t packed_numel,
+                       void *stream, bool to_packed) {
+  g_last_error.clear();
+  if (n < 0) return fail(DMUON_ERR_INVALID_ARG, "n < 0");
+  if (n == 0) return DMUON_OK;
+  if (!mats || !packed) return fail(DMUON_ERR_INVALID_ARG, "NULL mats or packed");
+  if (field != DMUON_FIELD_PARAM && field != DMUON_FIELD_GRAD)
+    return fail(DMUON_ERR_INVALID_ARG, "field %d", field);
+  if (!dtype_ok(packed_dtype)) return fail(DMUON_ERR_UNSUPPORTED_DTYPE, "packed dtype %d", packed_dtype);
+  if (packed_numel < 0) return fail(DMUON_ERR_INVALID_ARG, "packed_numel < 0");
+  const int64_t es = elem_size(packed_dtype);
+  std::vector<Interval> iv;
+  for (int32_t i = 0; i < n; ++i) {
+    const dmuon_matrix &d = mats[i];
+    if (d.rows < 1 || d.cols < 1 || d.rows >= kMaxDim || d.cols >= kMaxDim ||
+        d.rows * d.cols > kMaxNumel)
+      return fail(DMUON_ERR_INVALID_ARG, "matrix %d: bad shape", i);
+    const int32_t fdt = field == DMUON_FIELD_PARAM ? d.param_dtype : d.grad_dtype;
+    if (fdt != packed_dtype)
+      return fail(DMUON_ERR_UNSUPPORTED_DTYPE, "matrix %d: field dtype %d != packed dtype %d", i,
+                  fdt, packed_dtype);
+    const void *fp = field == DMUON_FIELD_PARAM ? d.param : d.grad;
+    if (!fp) return fail(DMUON_ERR_INVALID_ARG, "matrix %d: NULL field pointer", i);
+    const int64_t numel = d.rows * d.cols;
+    if (d.packed_offset < 0 || d.packed_offset > packed_numel - numel)
+      return fail(DMUON_ERR_INVALID_ARG, "matrix %d: [%lld, +%lld) outside packed buffer of %lld", i,
+                  (long long)d.packed_offset, (long long)numel, (long long)packed_numel);
+    const char *pp = static_cast<const char *>(packed) + d.packed_offset * es;
+    if (!aligned16(fp) || !aligned16(pp))
+      return fail(DMUON_ERR_MISALIGNED, "matrix %d: field or packed slot not 16-byte aligned", i);
+    const uintptr_t flo = reinterpret_cast<uintptr_t>(fp), plo = reinterpret_cast<uintptr_t>(pp);
+    const uintptr_t bytes = static_cast<uintptr_t>(numel * es);
+    iv.push_back(Interval{flo, flo + bytes, !to_packed, "field", i});
+    iv.push_back(Interval{plo, plo + bytes, to_packed, "packed slot", i});
+  }
+  int rc = check_aliasing(iv);
+  if (rc) return rc;
+  (void)packed_rw;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  PackBatch b;
+  std::memset(&b, 0, sizeof b);
+  for (int32_t i = 0; i < n; ++i) {
+    const dmuon_matrix &d = mats[i];
+    const void *fp = field == DMUON_FIELD_PARAM ? d.param : d.grad;
+    char *pp = const_cast<char *>(static_cast<const char *>(packed)) + d.packed_offset * es;
+    const int64_t bytes = d.rows * d.cols * es;
+    const int k = b.n;
+    b.src[k] = to_packed ? fp : pp;
+    b.dst[k] = to_packed ? static_cast<void *>(pp) : const_cast<void *>(fp);
+    b.bytes[k] = bytes;
+    b.first_block[k + 1] = b.first_block[k] + (bytes + kPackBlockBytes - 1) / kPackBlockBytes;
+    b.n = k + 1;
+    if (b.n == kPackBatch || i + 1 == n) {
+      if (b.first_block[b.n] > 0x7fffffff) return fail(DMUON_ERR_INVALID_ARG, "pack batch too large");
+      rc = check_launch(launch_pack_batch(b, s), "pack launch");
+      if (rc) return rc;
+      std::memset(&b, 0, sizeof b);
+    }
+  }
+  return DMUON_OK;
+}
+
+int dmuon_pack(const dmuon_matrix *mats, int32_t n, int32_t field, void *packed,
+               int32_t packed_dtype, int64_t packed_numel, void *stream) {
+  return pack_common(mats, n, field, packed, packed, packed_dtype, packed_numel, stream, true);
+}
+
+int dmuon_unpack(const dmuon_matrix *mats, int32_t n, int32_t field, const void *packed,
+                 int32_t packed_dtype, int64_t packed_numel, void *stream) {
+  return pack_common(mats, n, field, nullptr, packed, packed_dtype, packed_numel, stream, false);
+}
+
+}  // extern "C"

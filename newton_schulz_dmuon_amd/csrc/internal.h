@@ -1,0 +1,108 @@
+// Internal declarations shared by the host planner (host_api.cpp) and the
+// gfx950 kernels (elementwise.hip, gemm.hip).  Not part of the C ABI.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+namespace dmuon {
+
+// Newton-Schulz operands live in the workspace padded to multiples of this
+// many rows and columns, zero in the padding.  The padding stays zero through
+// every stage (X X^T, b A + c A A and a X + B X all map zero rows/columns to
+// zero), so the GEMM kernels never mask.
+constexpr int64_t kPad = 256;
+// Elements per work-group of the flat elementwise kernels.
+constexpr int64_t kEwChunk = 8192;
+// Side of the square tiles of the normalise/transpose kernel.
+constexpr int64_t kTrTile = 64;
+// Square output tile of the Newton-Schulz GEMM kernels.
+constexpr int64_t kGemmTile = 256;
+
+enum Dtype : int32_t { kBF16 = 0, kF32 = 1 };
+
+// Per-matrix descriptor, uploaded to the workspace on every step call.
+struct MatDev {
+  // caller memory
+  void *param;
+  const void *grad;
+  float *mom;
+  void *orth;
+  // workspace memory (element type bf16, or fp32 in the fp32 mode)
+  void *x[2];       // m_p x n_p, row-major, ping-pong
+  void *xt[2];      // n_p x m_p, row-major: the transpose of x[i]
+  void *a;          // m_p x m_p: A = X X^T
+  void *b;          // m_p x m_p: B = b A + c A A
+  double *partials; // per elementwise chunk: sum of U^2 over the chunk
+  float *inv_norm;  // one float: 1 / (||U||_F + eps)
+  int64_t rows, cols;   // caller shape r x c
+  int64_t m, n;         // wide orientation m = min(r, c), n = max(r, c)
+  int64_t mp, np;       // m, n rounded up to kPad
+  int64_t ew_first;     // first flat chunk index of this matrix
+  int64_t tr_first;     // first normalise-tile index of this matrix
+  int32_t ew_count;     // number of flat chunks
+  int32_t param_dt, grad_dt;
+  int32_t transposed;   // rows > cols
+  float scale;
+  int32_t tm, tn;       // mp / kGemmTile, np / kGemmTile
+  int32_t pad_;
+};
+
+// A matrix's slice of one GEMM stage's launch: work-groups
+// [first, first + count) of the launch compute its tiles.
+struct StageEntry {
+  int64_t first;
+  int32_t mat;
+  int32_t count;
+};
+
+struct StepScalars {
+  float a, b, c;
+  float lr, mu, eps;
+  int32_t nesterov;
+  int32_t pad_;
+};
+
+enum GemmMode : int32_t {
+  kModeGram = 0,    // C = X X^T (upper tiles, mirrored)        -> A
+  kModeSquare = 1,  // C = b A + c A A^T (upper tiles, mirrored) -> B
+  kModeApply = 2,   // C = a X + B X                             -> X', X'^T
+  kModeFinal = 3    // last apply: P -= lr*scale*C, orth <- C
+};
+
+// ---- launchers (elementwise.hip) ----
+hipError_t launch_momentum_sumsq(const MatDev *mats, int32_t nmat,
+                                 int64_t total_chunks, StepScalars s,
+                                 hipStream_t st);
+hipError_t launch_finalize_norm(const MatDev *mats, int32_t nmat, float eps,
+                                hipStream_t st);
+hipError_t launch_normalise_orient(const MatDev *mats, int32_t nmat,
+                                   int64_t total_tiles, StepScalars s,
+                                   bool fp32, hipStream_t st);
+hipError_t launch_update_direct(const MatDev *mats, int32_t nmat,
+                                int64_t total_chunks, StepScalars s,
+                                hipStream_t st);
+
+// Pack / unpack: batches of up to kPackBatch byte-copies per launch, passed
+// by value in the kernel arguments.
+constexpr int kPackBatch = 48;
+struct PackBatch {
+  int32_t n;
+  int32_t pad_;
+  int64_t first_block[kPackBatch + 1];  // prefix sum of blocks per copy
+  const void *src[kPackBatch];
+  void *dst[kPackBatch];
+  int64_t bytes[kPackBatch];
+};
+constexpr int64_t kPackBlockBytes = 64 * 1024;
+hipError_t launch_pack_batch(const PackBatch &b, hipStream_t st);
+
+// ---- launchers (gemm.hip) ----
+hipError_t launch_ns_stage(GemmMode mode, bool fp32, const MatDev *mats,
+                           const StageEntry *stage, int32_t nstage,
+                           int64_t total_tiles, int32_t cur, StepScalars s,
+                           hipStream_t st);
+
+}  // namespace dmuon

@@ -1,0 +1,175 @@
+"""GPU parity of the owner-side Muon step: the HIP library (through the C ABI
+binding) against the fp64 oracle on the same seeded inputs.
+
+Bars: momentum buffer <= 1e-6 relative Frobenius; Newton-Schulz output
+<= 2e-2 (bf16 chain) or <= 1e-4 (fp32 checking mode); parameters within one
+bf16 ulp plus the update's share of the O error, and mostly bit-equal to the
+rounded oracle value.
+"""
+
+import numpy as np
+import pytest
+
+from _gpu_util import Case, check_step, rel_fro, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def nsd():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import newton_schulz_dmuon_amd as m
+    m.load()
+    return m
+
+
+SHAPES = [
+    (128, 256),     # one fp32-sized tile, wide
+    (300, 700),     # 2 x 3 tiles, ragged both ways
+    (700, 300),     # tall: transposed path
+    (513, 513),     # square, one row/col past a tile boundary
+    (17, 33),
+    (1, 1),
+    (1, 300),
+    (300, 1),
+    (256, 256),     # exactly one tile
+    (257, 1000),
+    (1000, 257),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_single_matrix_bf16(nsd, shape):
+    say(f"bf16 step {shape}")
+    case = Case([shape], "bf16", "bf16", seed=1, m_std=1e-3)
+    opts = nsd.StepOptions()
+    err = check_step(case, opts, case.run_gpu(opts), case.run_oracle(opts))
+    say(f"  O rel err {err:.3e}")
+
+
+@pytest.mark.parametrize("shape", [(128, 256), (300, 700), (700, 300), (513, 513), (17, 33),
+                                   (1, 300)])
+def test_single_matrix_fp32_mode(nsd, shape):
+    say(f"fp32-mode step {shape}")
+    case = Case([shape], "f32", "f32", seed=2, g_std=1.0, m_std=0.5)
+    opts = nsd.StepOptions(ns_fp32=True)
+    err = check_step(case, opts, case.run_gpu(opts), case.run_oracle(opts))
+    say(f"  O rel err {err:.3e}")
+
+
+def test_tiny_fp32_workload(nsd):
+    """One fp32 128x256 matrix, grad N(0,1), param N(0,0.02), zero momentum,
+    mu 0.95, lr 0.02, 5 quintic steps; bf16 chain and fp32 mode."""
+    from synth import matrix_inputs, workload
+    w = workload(1)
+    P, G, M = matrix_inputs(w, 0)
+    for fp32 in (False, True):
+        case = Case([(128, 256)], "f32", "f32")
+        case.P, case.G, case.M = [P], [G], [M]
+        opts = nsd.StepOptions(ns_fp32=fp32)
+        err = check_step(case, opts, case.run_gpu(opts), case.run_oracle(opts))
+        say(f"tiny workload fp32={fp32}: O rel err {err:.3e}")
+
+
+@pytest.mark.parametrize("k", [0, 1, 2, 3, 8])
+def test_ns_steps(nsd, k):
+    case = Case([(300, 700), (700, 300)], "bf16", "bf16", seed=3, m_std=1e-3)
+    opts = nsd.StepOptions(ns_steps=k)
+    check_step(case, opts, case.run_gpu(opts), case.run_oracle(opts))
+
+
+@pytest.mark.parametrize("fp32", [False, True])
+def test_nesterov(nsd, fp32):
+    dt = "f32" if fp32 else "bf16"
+    case = Case([(300, 700), (513, 260)], dt, dt, seed=4, m_std=1e-3)
+    opts = nsd.StepOptions(nesterov=True, ns_fp32=fp32)
+    check_step(case, opts, case.run_gpu(opts), case.run_oracle(opts))
+
+
+def test_mixed_dtypes_and_coefficients(nsd):
+    case = Case([(200, 330)], "f32", "bf16", seed=5, m_std=1e-3)
+    opts = nsd.StepOptions(a=1.5, b=-0.5, c=0.0, ns_steps=7, lr=0.1, momentum=0.9)
+    check_step(case, opts, case.run_gpu(opts), case.run_oracle(opts))
+    case = Case([(330, 200)], "bf16", "f32", seed=6, g_std=1.0)
+    opts = nsd.StepOptions(a=2.0, b=-1.3, c=0.4, ns_steps=4)
+    check_step(case, opts, case.run_gpu(opts), case.run_oracle(opts))
+
+
+def test_heterogeneous_group(nsd):
+    """Many shapes in one grouped launch per stage."""
+    shapes = [(300, 700), (700, 300), (17, 33), (513, 513), (1, 1), (256, 1024), (1024, 256),
+              (64, 64), (129, 900)]
+    case = Case(shapes, "bf16", "bf16", seed=7, m_std=1e-3)
+    opts = nsd.StepOptions()
+    check_step(case, opts, case.run_gpu(opts), case.run_oracle(opts))
+
+
+def test_zero_gradient_and_momentum(nsd):
+    case = Case([(300, 700)], "bf16", "bf16", seed=8)
+    case.G = [np.zeros_like(case.G[0])]
+    opts = nsd.StepOptions()
+    P, M, O = case.run_gpu(opts)
+    assert np.all(O[0] == 0) and np.all(M[0] == 0)
+    assert np.array_equal(P[0], case.P[0].astype(np.float64))
+
+
+def test_qwen25_1p5b_layer(nsd):
+    """One Qwen2.5-1.5B layer's projections: q/o 1536^2, k/v 256x1536,
+    gate/up 8960x1536, down 1536x8960, bf16."""
+    from synth import matrix_inputs, workload
+    w = workload(2)
+    case = Case([(r, c) for _, r, c in w.shapes], "bf16", "bf16")
+    case.P, case.G, case.M = [], [], []
+    for i in range(len(w.shapes)):
+        P, G, M = matrix_inputs(w, i)
+        case.P.append(P); case.G.append(G); case.M.append(M)
+    opts = nsd.StepOptions()
+    say("qwen layer: gpu")
+    gpu = case.run_gpu(opts)
+    say("qwen layer: oracle")
+    err = check_step(case, opts, gpu, case.run_oracle(opts))
+    say(f"  worst O rel err {err:.3e}")
+
+
+def test_deterministic(nsd):
+    case = Case([(300, 700), (700, 300), (513, 513)], "bf16", "bf16", seed=9, m_std=1e-3)
+    opts = nsd.StepOptions()
+    a = case.run_gpu(opts)
+    b = case.run_gpu(opts)
+    for x, y in zip(a, b):
+        for u, v in zip(x, y):
+            assert np.array_equal(u, v)
+
+
+def test_workspace_reuse_across_shapes(nsd):
+    """A workspace sized for a large call, reused by a smaller one."""
+    ws = nsd.Workspace()
+    for shapes in ([(700, 900)], [(300, 200), (17, 33)]):
+        case = Case(shapes, "bf16", "bf16", seed=10, m_std=1e-3)
+        opts = nsd.StepOptions()
+        check_step(case, opts, case.run_gpu(opts, workspace=ws), case.run_oracle(opts))
+
+
+def test_grads_read_from_packed_buffer(nsd):
+    """Descriptors whose grad pointers point into one packed gradient buffer."""
+    from oracle import partition as refp
+    shapes = [(300, 700), (17, 33), (700, 300)]
+    case = Case(shapes, "bf16", "bf16", seed=11)
+    offs, total = refp.pack_offsets([r * c for r, c in shapes], 128)
+    packed = torch.zeros(total, dtype=torch.bfloat16, device="cuda")
+    G = []
+    for g, o in zip(case.G, offs):
+        view = packed[o:o + g.size].view(g.shape)
+        view.copy_(to_dev(g, "bf16"))
+        G.append(view)
+    P = [to_dev(p, "bf16") for p in case.P]
+    M = [to_dev(m, "f32") for m in case.M]
+    O = [torch.empty_like(p) for p in P]
+    opts = nsd.StepOptions()
+    nsd.muon_step(P, G, M, case.scales, opts, orth_out=O)
+    torch.cuda.synchronize()
+    check_step(case, opts, ([to_host(p) for p in P], [to_host(m) for m in M],
+                            [to_host(o) for o in O]), case.run_oracle(opts))
