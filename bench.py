@@ -111,6 +111,9 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="4", help="workload id or name (synth.workloads)")
+    ap.add_argument("--shape", action="append", default=None,
+                    help="RxC: run a custom bf16 set of these shapes instead (repeatable)")
+    ap.add_argument("--repeat", type=int, default=1, help="copies of each --shape")
     ap.add_argument("--ns-steps", type=int, default=None)
     ap.add_argument("--fp32-ns", action="store_true", help="fp32 checking mode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -129,6 +132,14 @@ def main(argv=None) -> int:
 
     key = int(args.workload) if args.workload.isdigit() else args.workload
     w = workload(key)
+    if args.shape:
+        from synth import Workload
+        shp = []
+        for s in args.shape:
+            r, c = (int(x) for x in s.lower().split("x"))
+            shp += [(f"custom.{r}x{c}.{i}", r, c) for i in range(args.repeat)]
+        w = Workload(0, "custom:" + ",".join(args.shape) + f"x{args.repeat}", shp,
+                     "bf16", "bf16", 0.02, 1e-3)
     K = args.ns_steps if args.ns_steps is not None else w.ns_steps
     nsd.load()
     dev = torch.device("cuda:0")

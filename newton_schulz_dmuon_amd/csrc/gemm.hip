@@ -22,11 +22,17 @@
 //
 // Tiling: 256x256 output tile per work-group of 8 waves (2 x 4), each wave
 // 128x64 = 8x4 MFMA 16x16 blocks.  K advances 128 bytes per step (64 bf16 or
-// 32 fp32).  Tiles are staged global -> registers -> LDS, double buffered
-// (2 x 64 KB); the next K step's global loads are in flight while the
-// current one runs on the matrix cores.  LDS rows are 128 bytes; the 16-byte
-// chunk index is XOR-swizzled with the row so the fragment reads of 16
-// consecutive rows spread over the banks.
+// 32 fp32).  Operand tiles go straight from global memory into LDS with
+// global_load_lds_dwordx4 (no register staging): each wave instruction fills
+// one contiguous KB of LDS, and every lane picks the global 16-byte chunk that
+// belongs at its LDS slot.  Two LDS stages (2 x 64 KB) form a ring: after the
+// barrier that opens step k, the loads of step k+1 go into the stage step k-1
+// used, and run while step k is on the matrix cores.
+//
+// LDS rows are 128 bytes; the 16-byte chunk index is XOR-swizzled with
+// (row / 2) mod 8.  A fragment read of 16 consecutive rows then touches 16
+// distinct 16-byte bank groups of the 256-byte LDS line (two rows per line),
+// which the bank-conflict counter confirms at zero.
 //
 // Operands are zero-padded to multiples of 256 in the workspace, so no
 // load or store is masked except the caller-visible writes of Final.
@@ -46,25 +52,63 @@ constexpr int kWaveM = kTile / kWavesM;             // 128
 constexpr int kWaveN = kTile / kWavesN;             // 64
 constexpr int kFragM = kWaveM / 16;                 // 8
 constexpr int kFragN = kWaveN / 16;                 // 4
-constexpr int kLoadRounds = kOperandBytes / (kThreads * 16);  // 4
+constexpr int kStageBytes = 2 * kOperandBytes;     // L and R tiles of one K step
+constexpr int kDmaPerWave = kOperandBytes / 1024 / 8;  // 4 KB-sized DMA instructions
 
-__device__ __forceinline__ int swz(int chunk, int row) { return chunk ^ (row & 7); }
+typedef __attribute__((address_space(3))) char lds_char;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+__device__ __forceinline__ int swz(int chunk, int row) { return chunk ^ ((row >> 1) & 7); }
+
+// Waits until this wave's LDS-bound global loads and LDS reads are complete,
+// then synchronises the work-group.  The memory clobber keeps the compiler
+// from moving LDS accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 template <typename T> struct Mfma;
 template <> struct Mfma<uint16_t> {
   // one 16-byte chunk per lane = 8 bf16 along k = one 16x16x32 MFMA
-  static __device__ __forceinline__ void run(f32x4 &acc, const uint4 &a, const uint4 &b) {
+  static __device__ __forceinline__ void run(f32x4 &acc, const u32x4 &a, const u32x4 &b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                   __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
   }
 };
 template <> struct Mfma<float> {
   // one 16-byte chunk per lane = 4 fp32 along k = four 16x16x4 MFMAs
-  static __device__ __forceinline__ void run(f32x4 &acc, const uint4 &a, const uint4 &b) {
+  static __device__ __forceinline__ void run(f32x4 &acc, const u32x4 &a, const u32x4 &b) {
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.z), __uint_as_float(b.z), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
+  }
+};
+
+// Four consecutive workspace elements as one vector access (8 bytes for bf16,
+// 16 for fp32); the address is a multiple of four elements.
+template <typename T> struct Vec4;
+template <> struct Vec4<uint16_t> {
+  static __device__ __forceinline__ f32x4 ld(const uint16_t *p) {
+    const uint2 v = *reinterpret_cast<const uint2 *>(p);
+    return f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                 __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
+  }
+  static __device__ __forceinline__ void st(uint16_t *p, const f32x4 &v) {
+    uint2 u;
+    u.x = static_cast<uint32_t>(f32_to_bf16_bits(v[0])) | (static_cast<uint32_t>(f32_to_bf16_bits(v[1])) << 16);
+    u.y = static_cast<uint32_t>(f32_to_bf16_bits(v[2])) | (static_cast<uint32_t>(f32_to_bf16_bits(v[3])) << 16);
+    *reinterpret_cast<uint2 *>(p) = u;
+  }
+};
+template <> struct Vec4<float> {
+  static __device__ __forceinline__ f32x4 ld(const float *p) {
+    const float4 v = *reinterpret_cast<const float4 *>(p);
+    return f32x4{v.x, v.y, v.z, v.w};
+  }
+  static __device__ __forceinline__ void st(float *p, const f32x4 &v) {
+    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
   }
 };
 
@@ -81,9 +125,8 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
                                                            const StageEntry *__restrict__ stage,
                                                            int32_t nstage, int32_t cur,
                                                            StepScalars s) {
-  __shared__ __attribute__((aligned(16))) char smem[4 * kOperandBytes];  // 128 KB
-  char *lds_l = smem;                      // [2][256][128 B]
-  char *lds_r = smem + 2 * kOperandBytes;  // [2][256][128 B]
+  __shared__ __attribute__((aligned(1024))) char smem[4 * kOperandBytes];  // 128 KB
+  lds_char *const lds = (lds_char *)smem;  // C cast: generic -> LDS address space  // [2 stages][L, R][256][128 B]
 
   const int64_t w = blockIdx.x;
   const int32_t si = find_range(nstage, w, [&](int32_t i) { return stage[i].first; });
@@ -119,29 +162,33 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   const char *gr = reinterpret_cast<const char *>(R) + static_cast<int64_t>(tj) * kTile * ld_bytes;
 
   const int tid = threadIdx.x;
-  const int lrow = tid >> 3, lch = tid & 7;  // global -> LDS copy position
-  uint4 rl[kLoadRounds], rr[kLoadRounds];
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  auto load_regs = [&](int kt) {
+  // This wave's share of a stage: kDmaPerWave instructions per operand, each
+  // filling LDS rows [8b, 8b + 8) of the operand tile, b = j*8 + wave.  Lane
+  // l writes LDS byte 16*l of that KB: row 8b + l/8, physical chunk l%8,
+  // which holds logical chunk swz(l%8, row) of the row.
+  int64_t goff[kDmaPerWave];
 #pragma unroll
-    for (int q = 0; q < kLoadRounds; ++q) {
-      const int64_t off = static_cast<int64_t>(q * 64 + lrow) * ld_bytes +
-                          static_cast<int64_t>(kt) * kRowBytes + lch * 16;
-      rl[q] = *reinterpret_cast<const uint4 *>(gl + off);
-      rr[q] = *reinterpret_cast<const uint4 *>(gr + off);
+  for (int j = 0; j < kDmaPerWave; ++j) {
+    const int row = (j * 8 + wave) * 8 + (lane >> 3);
+    goff[j] = static_cast<int64_t>(row) * ld_bytes + swz(lane & 7, row) * 16;
+  }
+  auto issue = [&](int kt) {
+    lds_char *st = lds + (kt & 1) * kStageBytes;
+    const int64_t kofs = static_cast<int64_t>(kt) * kRowBytes;
+#pragma unroll
+    for (int j = 0; j < kDmaPerWave; ++j) {
+      const int lofs = (j * 8 + wave) * 1024;
+      __builtin_amdgcn_global_load_lds((const void *)(gl + goff[j] + kofs),
+                                       (__attribute__((address_space(3))) void *)(st + lofs), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void *)(gr + goff[j] + kofs),
+                                       (__attribute__((address_space(3))) void *)(st + kOperandBytes + lofs),
+                                       16, 0, 0);
     }
   };
-  auto store_lds = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < kLoadRounds; ++q) {
-      const int row = q * 64 + lrow;
-      const int off = buf * kOperandBytes + row * kRowBytes + swz(lch, row) * 16;
-      *reinterpret_cast<uint4 *>(lds_l + off) = rl[q];
-      *reinterpret_cast<uint4 *>(lds_r + off) = rr[q];
-    }
-  };
 
-  const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int r16 = lane & 15, g4 = lane >> 4;
 
@@ -151,39 +198,37 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
 #pragma unroll
     for (int j = 0; j < kFragN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_regs(0);
-  store_lds(0);
-  __syncthreads();
-
+  issue(0);
   for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nkt) load_regs(kt + 1);
+    stage_barrier();               // step kt is in LDS; step kt-1's stage is free
+    if (kt + 1 < nkt) issue(kt + 1);
+    const lds_char *sl = lds + (kt & 1) * kStageBytes;
+    const lds_char *sr = sl + kOperandBytes;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int chunk = sub * 4 + g4;
-      uint4 fl[kFragM], fr[kFragN];
+      u32x4 fl[kFragM], fr[kFragN];
 #pragma unroll
       for (int i = 0; i < kFragM; ++i) {
         const int row = wm * kWaveM + i * 16 + r16;
-        fl[i] = *reinterpret_cast<const uint4 *>(lds_l + buf * kOperandBytes + row * kRowBytes +
-                                                 swz(chunk, row) * 16);
+        fl[i] = *(const lds_u32x4 *)(sl + row * kRowBytes + swz(chunk, row) * 16);
       }
 #pragma unroll
       for (int j = 0; j < kFragN; ++j) {
         const int row = wn * kWaveN + j * 16 + r16;
-        fr[j] = *reinterpret_cast<const uint4 *>(lds_r + buf * kOperandBytes + row * kRowBytes +
-                                                 swz(chunk, row) * 16);
+        fr[j] = *(const lds_u32x4 *)(sr + row * kRowBytes + swz(chunk, row) * 16);
       }
 #pragma unroll
       for (int i = 0; i < kFragM; ++i)
 #pragma unroll
         for (int j = 0; j < kFragN; ++j) Mfma<T>::run(acc[i][j], fl[i], fr[j]);
     }
-    if (kt + 1 < nkt) store_lds(buf ^ 1);
-    __syncthreads();
   }
 
   // ---- epilogue: lane holds C[row0 + 4*g4 + v][col0 + r16], v = 0..3 ----
+  // The four values of a lane are four consecutive rows of one column, i.e.
+  // four consecutive elements of a row of the transposed matrix: transposed
+  // reads and writes move them as one 8-byte (bf16) or 16-byte (fp32) vector.
   const int64_t row_base = static_cast<int64_t>(ti) * kTile + wm * kWaveM + 4 * g4;
   const int64_t col_base = static_cast<int64_t>(tj) * kTile + wn * kWaveN + r16;
 
@@ -195,18 +240,20 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
     for (int i = 0; i < kFragM; ++i)
 #pragma unroll
       for (int j = 0; j < kFragN; ++j) {
-        const int64_t col = col_base + j * 16;
+        const int64_t col = col_base + j * 16, row = row_base + i * 16;
+        f32x4 val = acc[i][j];
+        if (MODE == kModeSquare) {
+          // A[row + v][col] = A[col][row + v]: A is exactly symmetric
+          const f32x4 av = Vec4<T>::ld(prev + col * mp + row);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int64_t row = row_base + i * 16 + v;
-          float val = acc[i][j][v];
-          if (MODE == kModeSquare) val = fmaf(s.b, WsType<T>::ld(prev, row * mp + col), s.c * val);
-          WsType<T>::st(out, row * mp + col, val);
-          if (ti != tj) WsType<T>::st(out, col * mp + row, val);
+          for (int v = 0; v < 4; ++v) val[v] = fmaf(s.b, av[v], s.c * val[v]);
         }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) WsType<T>::st(out, (row + v) * mp + col, val[v]);
+        if (ti != tj) Vec4<T>::st(out + col * mp + row, val);
       }
   } else if (MODE == kModeApply) {
-    const T *X = static_cast<const T *>(d.x[cur]);
+    const T *XT = static_cast<const T *>(d.xt[cur]);
     T *Xn = static_cast<T *>(d.x[cur ^ 1]);
     T *XTn = static_cast<T *>(d.xt[cur ^ 1]);
     const int64_t np = d.np, mp = d.mp;
@@ -214,34 +261,34 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
     for (int i = 0; i < kFragM; ++i)
 #pragma unroll
       for (int j = 0; j < kFragN; ++j) {
-        const int64_t col = col_base + j * 16;
+        const int64_t col = col_base + j * 16, row = row_base + i * 16;
+        const f32x4 xv = Vec4<T>::ld(XT + col * mp + row);  // X[row + v][col]
+        f32x4 val;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int64_t row = row_base + i * 16 + v;
-          const float val = fmaf(s.a, WsType<T>::ld(X, row * np + col), acc[i][j][v]);
-          WsType<T>::st(Xn, row * np + col, val);
-          WsType<T>::st(XTn, col * mp + row, val);
-        }
+        for (int v = 0; v < 4; ++v) val[v] = fmaf(s.a, xv[v], acc[i][j][v]);
+        Vec4<T>::st(XTn + col * mp + row, val);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) WsType<T>::st(Xn, (row + v) * np + col, val[v]);
       }
   } else {  // kModeFinal
-    const T *X = static_cast<const T *>(d.x[cur]);
-    const int64_t np = d.np;
+    const T *XT = static_cast<const T *>(d.xt[cur]);
+    const int64_t mp = d.mp;
     const float step = s.lr * d.scale;
 #pragma unroll
     for (int i = 0; i < kFragM; ++i)
 #pragma unroll
       for (int j = 0; j < kFragN; ++j) {
-        const int64_t col = col_base + j * 16;
+        const int64_t col = col_base + j * 16, row = row_base + i * 16;
+        if (row >= d.m || col >= d.n) continue;
+        const f32x4 xv = Vec4<T>::ld(XT + col * mp + row);
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int64_t row = row_base + i * 16 + v;
-          if (row < d.m && col < d.n) {
-            const float o = fmaf(s.a, WsType<T>::ld(X, row * np + col), acc[i][j][v]);
-            const int64_t pidx = d.transposed ? col * d.cols + row : row * d.cols + col;
-            if (d.orth) store_elem(d.orth, d.param_dt, pidx, o);
-            store_elem(d.param, d.param_dt, pidx,
-                       fmaf(-step, o, load_elem(d.param, d.param_dt, pidx)));
-          }
+          if (row + v >= d.m) break;
+          const float o = fmaf(s.a, xv[v], acc[i][j][v]);
+          const int64_t pidx = d.transposed ? col * d.cols + row + v : (row + v) * d.cols + col;
+          if (d.orth) store_elem(d.orth, d.param_dt, pidx, o);
+          store_elem(d.param, d.param_dt, pidx,
+                     fmaf(-step, o, load_elem(d.param, d.param_dt, pidx)));
         }
       }
   }
