@@ -112,6 +112,38 @@ template <> struct Vec4<float> {
   }
 };
 
+// Row-major 256 x 256 bf16 tile in LDS (512-byte rows, 32 chunks of 16 B).
+// The chunk index is XOR-swizzled with bits 2-3 of the row (moved to chunk
+// bits 1-2): the 64 lanes of one put touch 4 rows x 2 chunks, all in
+// distinct bank groups, and a 16-lane read of one row stays a permutation.
+__device__ __forceinline__ int tile_swz(int row, int chunk) {
+  return chunk ^ (((row >> 2) & 3) << 1);
+}
+
+// Puts rows r0 .. r0+3 of column c (one lane's four values) as bf16.
+__device__ __forceinline__ void stage_tile_put(lds_char *lds, int r0, int c, const f32x4 &v) {
+  typedef __attribute__((address_space(3))) uint16_t lds_u16;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int row = r0 + k;
+    const int off = row * 512 + tile_swz(row, c >> 3) * 16 + (c & 7) * 2;
+    *(lds_u16 *)(lds + off) = f32_to_bf16_bits(v[k]);
+  }
+}
+
+// Writes the staged tile to dst (row-major, leading dimension ld elements)
+// with 16-byte stores: thread t moves chunks t, t + 512, ... (row = f / 32).
+__device__ __forceinline__ void stage_tile_flush(lds_char *lds, uint16_t *dst, int64_t ld, int tid) {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int f = q * 512 + tid;
+    const int row = f >> 5, chunk = f & 31;
+    const u32x4 v = *(const lds_u32x4 *)(lds + row * 512 + tile_swz(row, chunk) * 16);
+    *reinterpret_cast<u32x4 *>(dst + row * ld + chunk * 8) = v;
+  }
+}
+
 // Upper-triangle tile t (row-major enumeration) of a tm x tm tile grid.
 __device__ __forceinline__ void upper_tile(int32_t t, int32_t tm, int32_t &ti, int32_t &tj) {
   int32_t r = 0;
@@ -126,7 +158,8 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
                                                            int32_t nstage, int32_t cur,
                                                            StepScalars s) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * kOperandBytes];  // 128 KB
-  lds_char *const lds = (lds_char *)smem;  // C cast: generic -> LDS address space  // [2 stages][L, R][256][128 B]
+  // C cast: generic -> LDS address space.  [2 stages][L, R][256 rows][128 B]
+  lds_char *const lds = (lds_char *)smem;
 
   const int64_t w = blockIdx.x;
   const int32_t si = find_range(nstage, w, [&](int32_t i) { return stage[i].first; });
@@ -158,8 +191,14 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   }
   const int64_t ld_bytes = ld * static_cast<int64_t>(sizeof(T));
   const int nkt = static_cast<int>(ld_bytes / kRowBytes);
-  const char *gl = reinterpret_cast<const char *>(L) + static_cast<int64_t>(ti) * kTile * ld_bytes;
-  const char *gr = reinterpret_cast<const char *>(R) + static_cast<int64_t>(tj) * kTile * ld_bytes;
+  // The last Apply of a wide matrix (P is m x n, not transposed) computes
+  // the transposed tile, (B X)^T = X^T B: each lane's four consecutive
+  // values then run along a row of P, so the update is a vector access.
+  const bool swap = (MODE == kModeFinal) && !d.transposed;
+  const char *gl = reinterpret_cast<const char *>(swap ? R : L) +
+                   static_cast<int64_t>(swap ? tj : ti) * kTile * ld_bytes;
+  const char *gr = reinterpret_cast<const char *>(swap ? L : R) +
+                   static_cast<int64_t>(swap ? ti : tj) * kTile * ld_bytes;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -198,39 +237,69 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
 #pragma unroll
     for (int j = 0; j < kFragN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  issue(0);
-  for (int kt = 0; kt < nkt; ++kt) {
-    stage_barrier();               // step kt is in LDS; step kt-1's stage is free
-    if (kt + 1 < nkt) issue(kt + 1);
-    const lds_char *sl = lds + (kt & 1) * kStageBytes;
-    const lds_char *sr = sl + kOperandBytes;
+  // Fragments of one K step: sub-step 0 covers k chunks 0-3, sub-step 1
+  // chunks 4-7 of the 128-byte rows.
+  struct Frag {
+    u32x4 l[kFragM], r[kFragN];
+  };
+  auto read_frag = [&](const lds_char *st, int sub, Frag &f) {
+    const int chunk = sub * 4 + g4;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int chunk = sub * 4 + g4;
-      u32x4 fl[kFragM], fr[kFragN];
-#pragma unroll
-      for (int i = 0; i < kFragM; ++i) {
-        const int row = wm * kWaveM + i * 16 + r16;
-        fl[i] = *(const lds_u32x4 *)(sl + row * kRowBytes + swz(chunk, row) * 16);
-      }
-#pragma unroll
-      for (int j = 0; j < kFragN; ++j) {
-        const int row = wn * kWaveN + j * 16 + r16;
-        fr[j] = *(const lds_u32x4 *)(sr + row * kRowBytes + swz(chunk, row) * 16);
-      }
-#pragma unroll
-      for (int i = 0; i < kFragM; ++i)
-#pragma unroll
-        for (int j = 0; j < kFragN; ++j) Mfma<T>::run(acc[i][j], fl[i], fr[j]);
+    for (int i = 0; i < kFragM; ++i) {
+      const int row = wm * kWaveM + i * 16 + r16;
+      f.l[i] = *(const lds_u32x4 *)(st + row * kRowBytes + swz(chunk, row) * 16);
     }
+#pragma unroll
+    for (int j = 0; j < kFragN; ++j) {
+      const int row = wn * kWaveN + j * 16 + r16;
+      f.r[j] = *(const lds_u32x4 *)(st + kOperandBytes + row * kRowBytes + swz(chunk, row) * 16);
+    }
+  };
+  auto mfma_frag = [&](const Frag &f) {
+#pragma unroll
+    for (int i = 0; i < kFragM; ++i)
+#pragma unroll
+      for (int j = 0; j < kFragN; ++j) Mfma<T>::run(acc[i][j], f.l[i], f.r[j]);
+  };
+
+  // Software pipeline across the barrier: the products of step k-1's
+  // sub-step 1 (already in registers) run right after the barrier of step
+  // k, while step k's sub-step 0 fragments come out of LDS.  The loads of
+  // step k+1 are issued unconditionally (the last step re-loads its own K
+  // range into the free stage), so each iteration is one basic block the
+  // compiler can interleave.  nkt >= 4 because operands are padded to 256.
+  Frag fa, fb;
+  issue(0);
+  stage_barrier();
+  issue(1);
+  read_frag(lds, 0, fa);
+  read_frag(lds, 1, fb);
+  mfma_frag(fa);
+  for (int kt = 1; kt < nkt; ++kt) {
+    stage_barrier();  // step kt is in LDS; step kt-1's stage is free
+    const lds_char *st = lds + (kt & 1) * kStageBytes;
+    issue(min(kt + 1, nkt - 1));
+    read_frag(st, 0, fa);
+    mfma_frag(fb);    // sub-step 1 of step kt-1
+    read_frag(st, 1, fb);
+    mfma_frag(fa);
   }
+  mfma_frag(fb);
+  // no LDS-bound load may still be in flight when the LDS is reused or the
+  // work-group ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: lane holds C[row0 + 4*g4 + v][col0 + r16], v = 0..3 ----
   // The four values of a lane are four consecutive rows of one column, i.e.
   // four consecutive elements of a row of the transposed matrix: transposed
   // reads and writes move them as one 8-byte (bf16) or 16-byte (fp32) vector.
-  const int64_t row_base = static_cast<int64_t>(ti) * kTile + wm * kWaveM + 4 * g4;
-  const int64_t col_base = static_cast<int64_t>(tj) * kTile + wn * kWaveN + r16;
+  // Row-major bf16 outputs are staged through LDS (the 128 KB of the two
+  // stages hold one 256 x 256 bf16 tile) and leave as 16-byte row segments.
+  // rows of the computed product come from the L panel, columns from R
+  const int64_t row_base = static_cast<int64_t>(swap ? tj : ti) * kTile + wm * kWaveM + 4 * g4;
+  const int64_t col_base = static_cast<int64_t>(swap ? ti : tj) * kTile + wn * kWaveN + r16;
+  constexpr bool kStage = sizeof(T) == 2;
+  if (kStage && MODE != kModeFinal) stage_barrier();  // mainloop LDS reads done
 
   if (MODE == kModeGram || MODE == kModeSquare) {
     T *out = static_cast<T *>(MODE == kModeGram ? d.a : d.b);
@@ -248,10 +317,16 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
 #pragma unroll
           for (int v = 0; v < 4; ++v) val[v] = fmaf(s.b, av[v], s.c * val[v]);
         }
+        if constexpr (kStage)
+          stage_tile_put(lds, wm * kWaveM + i * 16 + 4 * g4, wn * kWaveN + j * 16 + r16, val);
+        else
 #pragma unroll
-        for (int v = 0; v < 4; ++v) WsType<T>::st(out, (row + v) * mp + col, val[v]);
+          for (int v = 0; v < 4; ++v) WsType<T>::st(out, (row + v) * mp + col, val[v]);
         if (ti != tj) Vec4<T>::st(out + col * mp + row, val);
       }
+    if constexpr (kStage)
+      stage_tile_flush(lds, reinterpret_cast<uint16_t *>(out) + static_cast<int64_t>(ti) * kTile * mp +
+                                static_cast<int64_t>(tj) * kTile, mp, tid);
   } else if (MODE == kModeApply) {
     const T *XT = static_cast<const T *>(d.xt[cur]);
     T *Xn = static_cast<T *>(d.x[cur ^ 1]);
@@ -267,28 +342,62 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
 #pragma unroll
         for (int v = 0; v < 4; ++v) val[v] = fmaf(s.a, xv[v], acc[i][j][v]);
         Vec4<T>::st(XTn + col * mp + row, val);
+        if constexpr (kStage)
+          stage_tile_put(lds, wm * kWaveM + i * 16 + 4 * g4, wn * kWaveN + j * 16 + r16, val);
+        else
 #pragma unroll
-        for (int v = 0; v < 4; ++v) WsType<T>::st(Xn, (row + v) * np + col, val[v]);
+          for (int v = 0; v < 4; ++v) WsType<T>::st(Xn, (row + v) * np + col, val[v]);
       }
+    if constexpr (kStage)
+      stage_tile_flush(lds, reinterpret_cast<uint16_t *>(Xn) + static_cast<int64_t>(ti) * kTile * np +
+                                static_cast<int64_t>(tj) * kTile, np, tid);
   } else {  // kModeFinal
-    const T *XT = static_cast<const T *>(d.xt[cur]);
-    const int64_t mp = d.mp;
     const float step = s.lr * d.scale;
+    // (p, q): lane's four values are C[p + v][q] of the computed product.
+    // Not swapped: p over m, q over n, P index (q, p + v) of the r x c = n x m
+    // matrix.  Swapped: the product is C^T, p over n, q over m, P index
+    // (q, p + v) of the m x n matrix.  Either way P[q][p .. p+3].
+    const int64_t p_lim = swap ? d.n : d.m, q_lim = swap ? d.m : d.n;
+    const T *Xsrc = static_cast<const T *>(swap ? d.x[cur] : d.xt[cur]);
+    const int64_t xld = swap ? d.np : d.mp;
+    const bool vec_ok = (d.cols & 3) == 0;  // rows of P start 4-element aligned
 #pragma unroll
     for (int i = 0; i < kFragM; ++i)
 #pragma unroll
       for (int j = 0; j < kFragN; ++j) {
-        const int64_t col = col_base + j * 16, row = row_base + i * 16;
-        if (row >= d.m || col >= d.n) continue;
-        const f32x4 xv = Vec4<T>::ld(XT + col * mp + row);
+        const int64_t q = col_base + j * 16, p = row_base + i * 16;
+        if (p >= p_lim || q >= q_lim) continue;
+        const f32x4 xv = Vec4<T>::ld(Xsrc + q * xld + p);  // X at the same positions
+        f32x4 o;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          if (row + v >= d.m) break;
-          const float o = fmaf(s.a, xv[v], acc[i][j][v]);
-          const int64_t pidx = d.transposed ? col * d.cols + row + v : (row + v) * d.cols + col;
-          if (d.orth) store_elem(d.orth, d.param_dt, pidx, o);
-          store_elem(d.param, d.param_dt, pidx,
-                     fmaf(-step, o, load_elem(d.param, d.param_dt, pidx)));
+        for (int v = 0; v < 4; ++v) o[v] = fmaf(s.a, xv[v], acc[i][j][v]);
+        const int64_t pidx = q * d.cols + p;
+        if (vec_ok && p + 4 <= p_lim) {
+          if (d.param_dt == kBF16) {
+            uint16_t *P = static_cast<uint16_t *>(d.param) + pidx;
+            const f32x4 pv = Vec4<uint16_t>::ld(P);
+            f32x4 nv;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) nv[v] = fmaf(-step, o[v], pv[v]);
+            Vec4<uint16_t>::st(P, nv);
+            if (d.orth) Vec4<uint16_t>::st(static_cast<uint16_t *>(d.orth) + pidx, o);
+          } else {
+            float *P = static_cast<float *>(d.param) + pidx;
+            const f32x4 pv = Vec4<float>::ld(P);
+            f32x4 nv;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) nv[v] = fmaf(-step, o[v], pv[v]);
+            Vec4<float>::st(P, nv);
+            if (d.orth) Vec4<float>::st(static_cast<float *>(d.orth) + pidx, o);
+          }
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            if (p + v >= p_lim) break;
+            if (d.orth) store_elem(d.orth, d.param_dt, pidx + v, o[v]);
+            store_elem(d.param, d.param_dt, pidx + v,
+                       fmaf(-step, o[v], load_elem(d.param, d.param_dt, pidx + v)));
+          }
         }
       }
   }
