@@ -1,0 +1,44 @@
+"""Error model of the bf16 Newton-Schulz chain (test utility).
+
+Runs the iteration with the rounding points of the GPU's bf16 mode: X, A and
+B stored as bf16 (round to nearest even) after each product, products
+accumulated in fp32 (here: computed in fp64, then rounded to fp32), the last
+X kept in fp32.  Comparing it with the fp64 oracle measures how much error
+bf16 storage alone introduces, which is what a bf16 tolerance has to allow.
+It is neither the oracle nor the HIP path and shares no code with either.
+"""
+
+import numpy as np
+
+
+def rne_bf16(x):
+    import torch
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).float().numpy() \
+        .astype(np.float64)
+
+
+def to_f32(x):
+    return np.asarray(x, np.float32).astype(np.float64)
+
+
+def ns_bf16_storage(X0, a, b, c, steps):
+    X = rne_bf16(X0)
+    for k in range(steps):
+        A = rne_bf16(to_f32(X @ X.T))
+        B = rne_bf16(to_f32(b * A + c * to_f32(A @ A)))
+        Xn = to_f32(a * X + to_f32(B @ X))
+        X = Xn if k == steps - 1 else rne_bf16(Xn)
+    return X
+
+
+def tol_o_bf16(steps: int) -> float:
+    """Relative-Frobenius bar for the bf16 chain's output O.  2e-2 up to the
+    default 5 iterations; above that the default quintic keeps amplifying
+    rounding errors (|p'(s)| > 1 on part of its band), and bf16 storage alone
+    reaches about 2.8e-2 at 8 iterations on Qwen2.5-7B k/v shapes (pinned in
+    test_bf16_error_model.py), so the bar is 1.5x that."""
+    if steps <= 5:
+        return 2e-2
+    if steps <= 8:
+        return 4.2e-2
+    raise ValueError("no bf16 bar derived beyond 8 iterations")

@@ -1,0 +1,118 @@
+"""Parity at full workload sizes, in the launch configuration bench.py times.
+
+The whole matrix set runs in one ``muon_step`` call, with the gradients read
+from one packed buffer.  A sample of matrices (one of every shape, from the
+first and the last layer) gets seeded inputs from ``synth`` and is checked
+against the fp64 oracle; the other matrices get device-generated values and
+only shape the launch.
+"""
+
+import numpy as np
+import pytest
+
+from _gpu_util import Case, check_step, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def nsd():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import newton_schulz_dmuon_amd as m
+    m.load()
+    return m
+
+
+def run_set(nsd, w, shapes, sample, opts):
+    """One step over ``shapes`` (list of (global index, name, r, c)); returns
+    the GPU outputs of the sampled positions and the oracle's."""
+    from synth import matrix_inputs, update_scale
+    numels = [r * c for _, _, r, c in shapes]
+    offs, total = nsd.pack_offsets(numels, 128)
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    gpacked = torch.empty(total, dtype=torch.bfloat16, device=dev)
+    P, G, M, O = [], [], [], []
+    case = Case([], "bf16", "bf16")
+    for pos, ((gi, name, r, c), off) in enumerate(zip(shapes, offs)):
+        g = gpacked[off:off + r * c].view(r, c)
+        if pos in sample:
+            p_h, g_h, m_h = matrix_inputs(w, gi)
+            case.shapes.append((r, c)); case.P.append(p_h); case.G.append(g_h)
+            case.M.append(m_h); case.scales.append(update_scale(r, c))
+            g.copy_(to_dev(g_h, "bf16"))
+            P.append(to_dev(p_h, "bf16"))
+            O.append(torch.empty_like(P[-1]))
+        else:
+            g.copy_(torch.randn(r, c, generator=gen, device=dev) * w.grad_std)
+            P.append((torch.randn(r, c, generator=gen, device=dev) * w.param_std).to(torch.bfloat16))
+            O.append(None)
+        G.append(g)
+        M.append(torch.zeros(r, c, dtype=torch.float32, device=dev))
+    scales = [update_scale(r, c) for _, _, r, c in shapes]
+    # orth_out only for the sampled matrices: the binding takes None entries
+    # as "no output" (NULL pointer)
+    nsd.muon_step(P, G, M, scales, opts, orth_out=O)
+    torch.cuda.synchronize()
+    gpu = ([to_host(P[i]) for i in sorted(sample)], [to_host(M[i]) for i in sorted(sample)],
+           [to_host(O[i]) for i in sorted(sample)])
+    say(f"  gpu step done ({len(shapes)} matrices); oracle on {len(sample)}")
+    return case, gpu
+
+
+def sample_positions(shapes):
+    """First occurrence of each distinct shape in the first layer and the
+    last one (every shape appears in both)."""
+    seen, pos = set(), []
+    last_layer = max(int(n.split(".")[1]) for _, n, _, _ in shapes)
+    for layer in (0, last_layer):
+        for i, (_, n, r, c) in enumerate(shapes):
+            if int(n.split(".")[1]) == layer and (layer, r, c) not in seen:
+                seen.add((layer, r, c))
+                pos.append(i)
+    return pos
+
+
+def test_llama31_8b_owner0_share(nsd):
+    """The benchmark workload: owner 0's 28 matrices of Llama-3.1-8B."""
+    from synth import workload
+    w = workload(4)
+    numels = [r * c for _, r, c in w.shapes]
+    owners, _ = nsd.partition_lpt(numels, w.n_owners)
+    shapes = [(i, n, r, c) for i, ((n, r, c), o) in enumerate(zip(w.shapes, owners)) if o == 0]
+    assert len(shapes) == 28
+    seen, sample = set(), set()
+    for pos, (_, _, r, c) in enumerate(shapes):
+        if (r, c) not in seen:
+            seen.add((r, c)); sample.add(pos)
+    assert len(sample) == 4   # q, k, gate/up (tall), down (wide)
+    say("llama-3.1-8b owner 0: 28 matrices")
+    opts = nsd.StepOptions()
+    case, gpu = run_set(nsd, w, shapes, sample, opts)
+    err = check_step(case, opts, gpu, case.run_oracle(opts))
+    say(f"  worst O rel err {err:.3e}")
+
+
+@pytest.mark.parametrize("wid,k_values", [(3, (5,)), (5, (3, 5, 8))])
+def test_full_model_sets(nsd, wid, k_values):
+    """All 28 layers of Llama-3.2-3B and Qwen2.5-7B (196 matrices) in one step;
+    sampled matrices of the first and last layer checked.  The sweep over
+    ns_steps checks the small shapes at every K and every shape at K = 5."""
+    from synth import workload
+    w = workload(wid)
+    shapes = [(i, n, r, c) for i, (n, r, c) in enumerate(w.shapes)]
+    pos = sample_positions(shapes)
+    for k in k_values:
+        # large shapes only at K = 5 (oracle time)
+        sample = {p for p in pos if k == 5 or shapes[p][2] * shapes[p][3] <= 4096 * 4096}
+        if k == 5 and wid == 5:
+            sample = {p for p in pos if int(shapes[p][1].split(".")[1]) == 0}
+        say(f"{w.name}: {len(shapes)} matrices, ns_steps {k}, {len(sample)} checked")
+        opts = nsd.StepOptions(ns_steps=k)
+        case, gpu = run_set(nsd, w, shapes, sample, opts)
+        err = check_step(case, opts, gpu, case.run_oracle(opts))
+        say(f"  worst O rel err {err:.3e}")
