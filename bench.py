@@ -173,7 +173,7 @@ def main(argv=None) -> int:
     arr, n = nsd.api.matrices(P, G, M, scales)
     cfg = opts.to_c()
     stream = torch.cuda.current_stream(dev)
-    n_launch = 3 + 3 * K if K > 0 else 3
+    n_launch = 2 + 3 * K if K > 0 else 3
 
     def step(ev=None):
         if ev is None:
@@ -202,8 +202,7 @@ def main(argv=None) -> int:
     log(f"timed {args.steps} steps: {ms:.3f} ms/step")
 
     # per-launch durations from the traced events
-    names = ["momentum_sumsq", "norm", "normalise_orient"] if K > 0 else \
-        ["momentum_sumsq", "norm", "update_direct"]
+    names = ["momentum_orient", "norm"] if K > 0 else ["momentum_sumsq", "norm", "update_direct"]
     for k in range(K):
         names += ["gram", "square", "final" if k == K - 1 else "apply"]
     per = {nm: [] for nm in set(names)}
@@ -236,8 +235,10 @@ def main(argv=None) -> int:
         stages["final"] = {"ms": avg["final"],
                            "tflops": flops["apply"] / K / (avg["final"] * 1e-3) / 1e12}
     elem = sum(numels)
-    gbytes = {"momentum_sumsq": elem * (4 + 4 + (2 if w.grad_dtype == "bf16" else 4)),
-              "normalise_orient": elem * (4 + 2 * (4 if args.fp32_ns else 2))}
+    gsz = 2 if w.grad_dtype == "bf16" else 4
+    gbytes = {"momentum_sumsq": elem * (4 + 4 + gsz),
+              # G read, M read + write, U written twice (X and X^T)
+              "momentum_orient": elem * (gsz + 4 + 4 + 2 * (4 if args.fp32_ns else 2))}
     for nm, b in gbytes.items():
         if nm in avg:
             stages[nm] = {"ms": avg[nm], "gbs": b / (avg[nm] * 1e-3) / 1e9}

@@ -178,9 +178,10 @@ int dmuon_muon_step(const dmuon_matrix *mats, int32_t n,
 /* dmuon_muon_step that also records caller-created HIP events (hipEvent_t,
  * passed as void*) on `stream`, for per-kernel timing: events[0] before the
  * first launch and events[j] right after the j-th launch.  Launch order:
- * momentum + sum of squares, norm, then either the direct update
- * (ns_steps = 0) or normalise/orient followed by Gram, Square, Apply for each
- * iteration (the last Apply carries the parameter update).  Only the first
+ * with ns_steps = 0: momentum + sum of squares, norm, direct update; with
+ * ns_steps >= 1: momentum + sum of squares + wide orientation, norm, then
+ * Gram, Square, Apply for each iteration (the last Apply carries the
+ * parameter update).  Only the first
  * n_events are recorded; n_events = 0 makes this dmuon_muon_step.
  * Errors: those of dmuon_muon_step; INVALID_ARG for n_events < 0 or a NULL
  * list with n_events > 0; HIP if an event cannot be recorded. */

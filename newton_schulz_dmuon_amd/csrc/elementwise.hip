@@ -1,6 +1,7 @@
 // Memory-bound stages of the owner's Muon step on gfx950: momentum + sum of
-// squares, the norm, normalise + cast + wide orientation, the direct update
-// (ns_steps = 0) and the packed-buffer copies.
+// squares fused with the cast to the wide orientation (X and X^T), the norm,
+// the direct update (ns_steps = 0, with a flat momentum pass) and the
+// packed-buffer copies.
 //
 // Every kernel here moves each byte once; they are bound by HBM bandwidth.
 // Loads and stores are 16-byte vectors where the layout allows, consecutive
@@ -43,6 +44,26 @@ __device__ __forceinline__ f32x4 load_grad4(const void *g, int32_t dt, int64_t i
   }
   return r;
 }
+
+// Eight consecutive workspace elements as 16-byte stores (address: a
+// multiple of eight elements).
+template <typename T> struct Vec8;
+template <> struct Vec8<uint16_t> {
+  static __device__ __forceinline__ void st(uint16_t *p, const float (&v)[8]) {
+    uint4 u;
+    u.x = f32_to_bf16_bits(v[0]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[1])) << 16);
+    u.y = f32_to_bf16_bits(v[2]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[3])) << 16);
+    u.z = f32_to_bf16_bits(v[4]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[5])) << 16);
+    u.w = f32_to_bf16_bits(v[6]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[7])) << 16);
+    *reinterpret_cast<uint4 *>(p) = u;
+  }
+};
+template <> struct Vec8<float> {
+  static __device__ __forceinline__ void st(float *p, const float (&v)[8]) {
+    reinterpret_cast<float4 *>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+    reinterpret_cast<float4 *>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+  }
+};
 
 // M <- mu*M + G over one chunk; partial sum of U^2, U = M or G + mu*M.
 __global__ __launch_bounds__(kEwThreads) void momentum_sumsq_kernel(
@@ -92,19 +113,25 @@ __global__ __launch_bounds__(256) void finalize_norm_kernel(const MatDev *__rest
   __shared__ double red[4];
   const MatDev &d = mats[blockIdx.x];
   double acc = 0.0;
-  for (int32_t i = threadIdx.x; i < d.ew_count; i += 256) acc += d.partials[i];
+  for (int32_t i = threadIdx.x; i < d.part_count; i += 256) acc += d.partials[i];
   const double tot = block_sum_f64(acc, red);
   if (threadIdx.x == 0) *d.inv_norm = static_cast<float>(1.0 / (sqrt(tot) + (double)eps));
 }
 
-// X0 = U * inv_norm in wide orientation, written as X (m_p x n_p) and X^T
-// (n_p x m_p), zero outside the m x n corner.  One 64 x 64 tile of X per
-// work-group, staged through LDS so both writes are row-contiguous.
+// Fused momentum + sum of squares + wide orientation, one 64 x 64 tile of the
+// padded X (m_p x n_p) per work-group:
+//   M <- mu*M + G on the caller block that maps onto the tile,
+//   U = M (or G + mu*M), its sum of squares into partials[tile],
+//   U written unnormalised as X (row-major) and X^T, zero in the padding.
+// The 1/(||U||_F + eps) scale is applied by the first iteration's Gram and
+// Apply epilogues, so M is read once.  The block is staged through LDS so
+// that both X and X^T leave as 16-byte row segments.
 template <typename T>
-__global__ __launch_bounds__(256) void normalise_orient_kernel(
+__global__ __launch_bounds__(256) void momentum_orient_kernel(
     const MatDev *__restrict__ mats, int32_t nmat, StepScalars s) {
   constexpr int TT = static_cast<int>(kTrTile);
   __shared__ float tile[TT][TT + 1];
+  __shared__ double red[4];
   const int64_t w = blockIdx.x;
   const int32_t mi = find_range(nmat, w, [&](int32_t i) { return mats[i].tr_first; });
   const MatDev &d = mats[mi];
@@ -112,33 +139,61 @@ __global__ __launch_bounds__(256) void normalise_orient_kernel(
   const int64_t tiles_n = d.np / TT;
   const int64_t i0 = (t / tiles_n) * TT, j0 = (t % tiles_n) * TT;  // X coords
   const int64_t ur0 = d.transposed ? j0 : i0, uc0 = d.transposed ? i0 : j0;
-  const float inv = *d.inv_norm;
   const float mu = s.mu;
-  // load U block (rows ur0.., cols uc0..) of the r x c caller matrix
-  for (int e = threadIdx.x; e < TT * TT; e += 256) {
-    const int p = e / TT, q = e % TT;
+  const int tid = threadIdx.x;
+  const bool vec = (d.cols & 3) == 0;  // rows of M start 16-byte aligned
+  double acc = 0.0;
+  // read: 4 consecutive columns of one row per thread and step
+  for (int e = tid; e < TT * TT / 4; e += 256) {
+    const int p = e >> 4, q = (e & 15) * 4;
     const int64_t ur = ur0 + p, uc = uc0 + q;
-    float v = 0.f;
+    float u[4] = {0.f, 0.f, 0.f, 0.f};
     if (ur < d.rows && uc < d.cols) {
       const int64_t idx = ur * d.cols + uc;
-      float u = d.mom[idx];
-      if (s.nesterov) u = fmaf(mu, u, load_elem(d.grad, d.grad_dt, idx));
-      v = u * inv;
+      if (vec && uc + 4 <= d.cols) {
+        float4 mv = *reinterpret_cast<const float4 *>(d.mom + idx);
+        const f32x4 g = load_grad4(d.grad, d.grad_dt, idx);
+        mv.x = fmaf(mu, mv.x, g[0]);
+        mv.y = fmaf(mu, mv.y, g[1]);
+        mv.z = fmaf(mu, mv.z, g[2]);
+        mv.w = fmaf(mu, mv.w, g[3]);
+        *reinterpret_cast<float4 *>(d.mom + idx) = mv;
+        u[0] = mv.x; u[1] = mv.y; u[2] = mv.z; u[3] = mv.w;
+        if (s.nesterov)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) u[k] = fmaf(mu, u[k], g[k]);
+      } else {
+        for (int k = 0; k < 4 && uc + k < d.cols; ++k) {
+          const float g = load_elem(d.grad, d.grad_dt, idx + k);
+          const float m = fmaf(mu, d.mom[idx + k], g);
+          d.mom[idx + k] = m;
+          u[k] = s.nesterov ? fmaf(mu, m, g) : m;
+        }
+      }
     }
-    tile[p][q] = v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      tile[p][q + k] = u[k];
+      acc += (double)u[k] * u[k];
+    }
   }
   __syncthreads();
+  // write: 8 consecutive elements of an X row, then of an X^T row
   T *X = static_cast<T *>(d.x[0]);
   T *XT = static_cast<T *>(d.xt[0]);
-  for (int e = threadIdx.x; e < TT * TT; e += 256) {
-    const int a = e / TT, b = e % TT;
-    // X[i0 + a][j0 + b]
-    const float vx = d.transposed ? tile[b][a] : tile[a][b];
-    WsType<T>::st(X, (i0 + a) * d.np + j0 + b, vx);
-    // X^T[j0 + a][i0 + b] = X[i0 + b][j0 + a]
-    const float vt = d.transposed ? tile[a][b] : tile[b][a];
-    WsType<T>::st(XT, (j0 + a) * d.mp + i0 + b, vt);
+  for (int c = tid; c < TT * TT / 8; c += 256) {
+    const int a = c >> 3, b = (c & 7) * 8;
+    float vx[8], vt[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      vx[k] = d.transposed ? tile[b + k][a] : tile[a][b + k];  // X[i0 + a][j0 + b + k]
+      vt[k] = d.transposed ? tile[a][b + k] : tile[b + k][a];  // X^T[j0 + a][i0 + b + k]
+    }
+    Vec8<T>::st(X + (i0 + a) * d.np + j0 + b, vx);
+    Vec8<T>::st(XT + (j0 + a) * d.mp + i0 + b, vt);
   }
+  const double tot = block_sum_f64(acc, red);
+  if (tid == 0) d.partials[t] = tot;
 }
 
 // ns_steps = 0: O = U * inv_norm (already r x c), P -= lr*scale*O.
@@ -194,14 +249,14 @@ hipError_t launch_finalize_norm(const MatDev *mats, int32_t nmat, float eps, hip
   return hipGetLastError();
 }
 
-hipError_t launch_normalise_orient(const MatDev *mats, int32_t nmat, int64_t total_tiles,
-                                   StepScalars s, bool fp32, hipStream_t st) {
+hipError_t launch_momentum_orient(const MatDev *mats, int32_t nmat, int64_t total_tiles,
+                                  StepScalars s, bool fp32, hipStream_t st) {
   if (fp32)
-    hipLaunchKernelGGL(normalise_orient_kernel<float>, dim3((uint32_t)total_tiles), dim3(256),
-                       0, st, mats, nmat, s);
+    hipLaunchKernelGGL(momentum_orient_kernel<float>, dim3((uint32_t)total_tiles), dim3(256), 0,
+                       st, mats, nmat, s);
   else
-    hipLaunchKernelGGL(normalise_orient_kernel<uint16_t>, dim3((uint32_t)total_tiles),
-                       dim3(256), 0, st, mats, nmat, s);
+    hipLaunchKernelGGL(momentum_orient_kernel<uint16_t>, dim3((uint32_t)total_tiles), dim3(256),
+                       0, st, mats, nmat, s);
   return hipGetLastError();
 }
 

@@ -156,7 +156,7 @@ template <typename T, int MODE>
 __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restrict__ mats,
                                                            const StageEntry *__restrict__ stage,
                                                            int32_t nstage, int32_t cur,
-                                                           StepScalars s) {
+                                                           int32_t first, StepScalars s) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * kOperandBytes];  // 128 KB
   // C cast: generic -> LDS address space.  [2 stages][L, R][256 rows][128 B]
   lds_char *const lds = (lds_char *)smem;
@@ -301,6 +301,10 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   constexpr bool kStage = sizeof(T) == 2;
   if (kStage && MODE != kModeFinal) stage_barrier();  // mainloop LDS reads done
 
+  // The first iteration's X is U unnormalised (X0 = U * inv_norm): A0 picks
+  // up inv_norm^2 and the first X' (or O) inv_norm.
+  const float inv = first ? *d.inv_norm : 1.f;
+  const float gram_scale = inv * inv;
   if (MODE == kModeGram || MODE == kModeSquare) {
     T *out = static_cast<T *>(MODE == kModeGram ? d.a : d.b);
     const T *prev = static_cast<const T *>(d.a);
@@ -311,6 +315,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
       for (int j = 0; j < kFragN; ++j) {
         const int64_t col = col_base + j * 16, row = row_base + i * 16;
         f32x4 val = acc[i][j];
+        if (MODE == kModeGram) val *= gram_scale;
         if (MODE == kModeSquare) {
           // A[row + v][col] = A[col][row + v]: A is exactly symmetric
           const f32x4 av = Vec4<T>::ld(prev + col * mp + row);
@@ -340,7 +345,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
         const f32x4 xv = Vec4<T>::ld(XT + col * mp + row);  // X[row + v][col]
         f32x4 val;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) val[v] = fmaf(s.a, xv[v], acc[i][j][v]);
+        for (int v = 0; v < 4; ++v) val[v] = fmaf(s.a, xv[v], acc[i][j][v]) * inv;
         Vec4<T>::st(XTn + col * mp + row, val);
         if constexpr (kStage)
           stage_tile_put(lds, wm * kWaveM + i * 16 + 4 * g4, wn * kWaveN + j * 16 + r16, val);
@@ -370,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
         const f32x4 xv = Vec4<T>::ld(Xsrc + q * xld + p);  // X at the same positions
         f32x4 o;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) o[v] = fmaf(s.a, xv[v], acc[i][j][v]);
+        for (int v = 0; v < 4; ++v) o[v] = fmaf(s.a, xv[v], acc[i][j][v]) * inv;
         const int64_t pidx = q * d.cols + p;
         if (vec_ok && p + 4 <= p_lim) {
           if (d.param_dt == kBF16) {
@@ -405,20 +410,20 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
 
 template <typename T>
 hipError_t launch_t(GemmMode mode, const MatDev *mats, const StageEntry *stage, int32_t nstage,
-                    int64_t total, int32_t cur, StepScalars s, hipStream_t st) {
+                    int64_t total, int32_t cur, int32_t first, StepScalars s, hipStream_t st) {
   const dim3 grid(static_cast<uint32_t>(total)), block(kThreads);
   switch (mode) {
     case kModeGram:
-      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeGram>), grid, block, 0, st, mats, stage, nstage, cur, s);
+      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeGram>), grid, block, 0, st, mats, stage, nstage, cur, first, s);
       break;
     case kModeSquare:
-      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeSquare>), grid, block, 0, st, mats, stage, nstage, cur, s);
+      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeSquare>), grid, block, 0, st, mats, stage, nstage, cur, first, s);
       break;
     case kModeApply:
-      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeApply>), grid, block, 0, st, mats, stage, nstage, cur, s);
+      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeApply>), grid, block, 0, st, mats, stage, nstage, cur, first, s);
       break;
     default:
-      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeFinal>), grid, block, 0, st, mats, stage, nstage, cur, s);
+      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeFinal>), grid, block, 0, st, mats, stage, nstage, cur, first, s);
       break;
   }
   return hipGetLastError();
@@ -427,11 +432,12 @@ hipError_t launch_t(GemmMode mode, const MatDev *mats, const StageEntry *stage, 
 }  // namespace
 
 hipError_t launch_ns_stage(GemmMode mode, bool fp32, const MatDev *mats, const StageEntry *stage,
-                           int32_t nstage, int64_t total_tiles, int32_t cur, StepScalars s,
-                           hipStream_t st) {
+                           int32_t nstage, int64_t total_tiles, int32_t cur, bool first,
+                           StepScalars s, hipStream_t st) {
   if (total_tiles == 0) return hipSuccess;
-  return fp32 ? launch_t<float>(mode, mats, stage, nstage, total_tiles, cur, s, st)
-              : launch_t<uint16_t>(mode, mats, stage, nstage, total_tiles, cur, s, st);
+  const int32_t f = first ? 1 : 0;
+  return fp32 ? launch_t<float>(mode, mats, stage, nstage, total_tiles, cur, f, s, st)
+              : launch_t<uint16_t>(mode, mats, stage, nstage, total_tiles, cur, f, s, st);
 }
 
 }  // namespace dmuon

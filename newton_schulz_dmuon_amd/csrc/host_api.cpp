@@ -189,13 +189,18 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
   }
   p.table_bytes = off;
   p.off_partials = off;
-  off = round_up(off + 8 * ew, 256);
+  off = round_up(off + 8 * (K > 0 ? tr : ew), 256);
   p.off_inv = off;
   off = round_up(off + 256 * int64_t(n), 256);  // one 256-byte slot per matrix
   p.off_ns = off;
   for (int32_t i = 0; i < n; ++i) {
     MatDev &d = p.mats[i];
-    d.partials = ws ? reinterpret_cast<double *>(ws + p.off_partials) + d.ew_first : nullptr;
+    // sum-of-squares partials: one per orientation tile, or per flat chunk
+    // when there is no Newton-Schulz iteration
+    d.partials = ws ? reinterpret_cast<double *>(ws + p.off_partials) +
+                          (K > 0 ? d.tr_first : d.ew_first)
+                    : nullptr;
+    d.part_count = K > 0 ? static_cast<int32_t>((d.mp / kTrTile) * (d.np / kTrTile)) : d.ew_count;
     d.inv_norm = ws ? reinterpret_cast<float *>(ws + p.off_inv + 256 * int64_t(i)) : nullptr;
     if (K == 0) continue;
     const int64_t xb = d.mp * d.np * es, ab = d.mp * d.mp * es;
@@ -441,25 +446,29 @@ static int muon_step_impl(const dmuon_matrix *mats, int32_t n, const dmuon_step_
   };
 
   if ((rc = mark())) return rc;
-  if ((rc = launched(launch_momentum_sumsq(dm, n, p.ew_total, sc, s), "momentum_sumsq launch")))
+  if (cfg->ns_steps == 0) {
+    if ((rc = launched(launch_momentum_sumsq(dm, n, p.ew_total, sc, s), "momentum_sumsq launch")))
+      return rc;
+    if ((rc = launched(launch_finalize_norm(dm, n, cfg->eps, s), "finalize_norm launch"))) return rc;
+    return launched(launch_update_direct(dm, n, p.ew_total, sc, s), "update_direct launch");
+  }
+  if ((rc = launched(launch_momentum_orient(dm, n, p.tr_total, sc, fp32, s),
+                     "momentum_orient launch")))
     return rc;
   if ((rc = launched(launch_finalize_norm(dm, n, cfg->eps, s), "finalize_norm launch"))) return rc;
-  if (cfg->ns_steps == 0)
-    return launched(launch_update_direct(dm, n, p.ew_total, sc, s), "update_direct launch");
-
-  if ((rc = launched(launch_normalise_orient(dm, n, p.tr_total, sc, fp32, s), "normalise launch")))
-    return rc;
   for (int k = 0; k < cfg->ns_steps; ++k) {
     const int32_t cur = k & 1;
-    const bool last = k + 1 == cfg->ns_steps;
-    if ((rc = launched(launch_ns_stage(kModeGram, fp32, dm, dst[0], n, p.stage_total[0], cur, sc, s),
+    const bool last = k + 1 == cfg->ns_steps, first = k == 0;
+    if ((rc = launched(launch_ns_stage(kModeGram, fp32, dm, dst[0], n, p.stage_total[0], cur, first,
+                                       sc, s),
                        "gram launch")))
       return rc;
-    if ((rc = launched(launch_ns_stage(kModeSquare, fp32, dm, dst[1], n, p.stage_total[1], cur, sc, s),
+    if ((rc = launched(launch_ns_stage(kModeSquare, fp32, dm, dst[1], n, p.stage_total[1], cur,
+                                       first, sc, s),
                        "square launch")))
       return rc;
     if ((rc = launched(launch_ns_stage(last ? kModeFinal : kModeApply, fp32, dm, dst[2], n,
-                                       p.stage_total[2], cur, sc, s),
+                                       p.stage_total[2], cur, first, sc, s),
                        "apply launch")))
       return rc;
   }

@@ -35,7 +35,8 @@ struct MatDev {
   void *xt[2];      // n_p x m_p, row-major: the transpose of x[i]
   void *a;          // m_p x m_p: A = X X^T
   void *b;          // m_p x m_p: B = b A + c A A
-  double *partials; // per elementwise chunk: sum of U^2 over the chunk
+  double *partials; // sum of U^2 per flat chunk (ns_steps = 0) or per
+                    // 64 x 64 orientation tile (ns_steps >= 1)
   float *inv_norm;  // one float: 1 / (||U||_F + eps)
   int64_t rows, cols;   // caller shape r x c
   int64_t m, n;         // wide orientation m = min(r, c), n = max(r, c)
@@ -43,11 +44,11 @@ struct MatDev {
   int64_t ew_first;     // first flat chunk index of this matrix
   int64_t tr_first;     // first normalise-tile index of this matrix
   int32_t ew_count;     // number of flat chunks
+  int32_t part_count;   // number of partial sums of U^2
   int32_t param_dt, grad_dt;
   int32_t transposed;   // rows > cols
   float scale;
   int32_t tm, tn;       // mp / kGemmTile, np / kGemmTile
-  int32_t pad_;
 };
 
 // A matrix's slice of one GEMM stage's launch: work-groups
@@ -78,9 +79,9 @@ hipError_t launch_momentum_sumsq(const MatDev *mats, int32_t nmat,
                                  hipStream_t st);
 hipError_t launch_finalize_norm(const MatDev *mats, int32_t nmat, float eps,
                                 hipStream_t st);
-hipError_t launch_normalise_orient(const MatDev *mats, int32_t nmat,
-                                   int64_t total_tiles, StepScalars s,
-                                   bool fp32, hipStream_t st);
+hipError_t launch_momentum_orient(const MatDev *mats, int32_t nmat,
+                                  int64_t total_tiles, StepScalars s, bool fp32,
+                                  hipStream_t st);
 hipError_t launch_update_direct(const MatDev *mats, int32_t nmat,
                                 int64_t total_chunks, StepScalars s,
                                 hipStream_t st);
@@ -100,9 +101,11 @@ constexpr int64_t kPackBlockBytes = 64 * 1024;
 hipError_t launch_pack_batch(const PackBatch &b, hipStream_t st);
 
 // ---- launchers (gemm.hip) ----
+// first: the first iteration, whose X holds U unnormalised: Gram scales by
+// inv_norm^2 and Apply / Final by inv_norm.
 hipError_t launch_ns_stage(GemmMode mode, bool fp32, const MatDev *mats,
                            const StageEntry *stage, int32_t nstage,
-                           int64_t total_tiles, int32_t cur, StepScalars s,
-                           hipStream_t st);
+                           int64_t total_tiles, int32_t cur, bool first,
+                           StepScalars s, hipStream_t st);
 
 }  // namespace dmuon
