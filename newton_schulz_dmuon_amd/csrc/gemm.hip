@@ -88,27 +88,38 @@ template <> struct Mfma<float> {
 
 // Four consecutive workspace elements as one vector access (8 bytes for bf16,
 // 16 for fp32); the address is a multiple of four elements.
+// Accesses go through global (address space 1) pointers, so they count on
+// vmcnt only and never wait on LDS traffic.  raw() / cvt() split a load so
+// that a batch of loads can be issued before the first use.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) u32x2 g_u32x2;
+typedef __attribute__((address_space(1))) u32x4 g_u32x4;
 template <typename T> struct Vec4;
 template <> struct Vec4<uint16_t> {
-  static __device__ __forceinline__ f32x4 ld(const uint16_t *p) {
-    const uint2 v = *reinterpret_cast<const uint2 *>(p);
+  typedef u32x2 Raw;
+  static __device__ __forceinline__ Raw raw(const uint16_t *p) { return *(const g_u32x2 *)p; }
+  static __device__ __forceinline__ f32x4 cvt(const Raw &v) {
     return f32x4{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
                  __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u)};
   }
+  static __device__ __forceinline__ f32x4 ld(const uint16_t *p) { return cvt(raw(p)); }
   static __device__ __forceinline__ void st(uint16_t *p, const f32x4 &v) {
-    uint2 u;
+    u32x2 u;
     u.x = static_cast<uint32_t>(f32_to_bf16_bits(v[0])) | (static_cast<uint32_t>(f32_to_bf16_bits(v[1])) << 16);
     u.y = static_cast<uint32_t>(f32_to_bf16_bits(v[2])) | (static_cast<uint32_t>(f32_to_bf16_bits(v[3])) << 16);
-    *reinterpret_cast<uint2 *>(p) = u;
+    *(g_u32x2 *)p = u;
   }
 };
 template <> struct Vec4<float> {
-  static __device__ __forceinline__ f32x4 ld(const float *p) {
-    const float4 v = *reinterpret_cast<const float4 *>(p);
-    return f32x4{v.x, v.y, v.z, v.w};
+  typedef u32x4 Raw;
+  static __device__ __forceinline__ Raw raw(const float *p) { return *(const g_u32x4 *)p; }
+  static __device__ __forceinline__ f32x4 cvt(const Raw &v) {
+    return f32x4{__uint_as_float(v.x), __uint_as_float(v.y), __uint_as_float(v.z), __uint_as_float(v.w)};
   }
+  static __device__ __forceinline__ f32x4 ld(const float *p) { return cvt(raw(p)); }
   static __device__ __forceinline__ void st(float *p, const f32x4 &v) {
-    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *(g_u32x4 *)p = u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                          __float_as_uint(v[3])};
   }
 };
 
@@ -299,6 +310,9 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   const int64_t row_base = static_cast<int64_t>(swap ? tj : ti) * kTile + wm * kWaveM + 4 * g4;
   const int64_t col_base = static_cast<int64_t>(swap ? ti : tj) * kTile + wn * kWaveN + r16;
   constexpr bool kStage = sizeof(T) == 2;
+  // fragment rows whose epilogue inputs are read in one batch: all of them
+  // for bf16 (2 VGPRs per vector), two at a time for fp32 (4 per vector)
+  constexpr int kReadRows = sizeof(T) == 2 ? kFragM : 2;
   if (kStage && MODE != kModeFinal) stage_barrier();  // mainloop LDS reads done
 
   // The first iteration's X is U unnormalised (X0 = U * inv_norm): A0 picks
@@ -309,16 +323,28 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
     T *out = static_cast<T *>(MODE == kModeGram ? d.a : d.b);
     const T *prev = static_cast<const T *>(d.a);
     const int64_t mp = d.mp;
+    // all of a lane's reads first: the compiler cannot prove that the
+    // stores below miss them, so interleaving would serialise each one
 #pragma unroll
-    for (int i = 0; i < kFragM; ++i)
+    for (int i0 = 0; i0 < kFragM; i0 += kReadRows) {
+    typename Vec4<T>::Raw araw[kReadRows][kFragN];
+    if (MODE == kModeSquare)
+#pragma unroll
+      for (int ii = 0; ii < kReadRows; ++ii)
+#pragma unroll
+        for (int j = 0; j < kFragN; ++j)
+          // A[row + v][col] = A[col][row + v]: A is exactly symmetric
+          araw[ii][j] = Vec4<T>::raw(prev + (col_base + j * 16) * mp + row_base + (i0 + ii) * 16);
+#pragma unroll
+    for (int ii = 0; ii < kReadRows; ++ii)
 #pragma unroll
       for (int j = 0; j < kFragN; ++j) {
+        const int i = i0 + ii;
         const int64_t col = col_base + j * 16, row = row_base + i * 16;
         f32x4 val = acc[i][j];
         if (MODE == kModeGram) val *= gram_scale;
         if (MODE == kModeSquare) {
-          // A[row + v][col] = A[col][row + v]: A is exactly symmetric
-          const f32x4 av = Vec4<T>::ld(prev + col * mp + row);
+          const f32x4 av = Vec4<T>::cvt(araw[ii][j]);
 #pragma unroll
           for (int v = 0; v < 4; ++v) val[v] = fmaf(s.b, av[v], s.c * val[v]);
         }
@@ -329,6 +355,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
           for (int v = 0; v < 4; ++v) WsType<T>::st(out, (row + v) * mp + col, val[v]);
         if (ti != tj) Vec4<T>::st(out + col * mp + row, val);
       }
+    }
     if constexpr (kStage)
       stage_tile_flush(lds, reinterpret_cast<uint16_t *>(out) + static_cast<int64_t>(ti) * kTile * mp +
                                 static_cast<int64_t>(tj) * kTile, mp, tid);
@@ -338,11 +365,20 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
     T *XTn = static_cast<T *>(d.xt[cur ^ 1]);
     const int64_t np = d.np, mp = d.mp;
 #pragma unroll
-    for (int i = 0; i < kFragM; ++i)
+    for (int i0 = 0; i0 < kFragM; i0 += kReadRows) {
+    typename Vec4<T>::Raw xraw[kReadRows][kFragN];  // X[row + v][col], reads first
+#pragma unroll
+    for (int ii = 0; ii < kReadRows; ++ii)
+#pragma unroll
+      for (int j = 0; j < kFragN; ++j)
+        xraw[ii][j] = Vec4<T>::raw(XT + (col_base + j * 16) * mp + row_base + (i0 + ii) * 16);
+#pragma unroll
+    for (int ii = 0; ii < kReadRows; ++ii)
 #pragma unroll
       for (int j = 0; j < kFragN; ++j) {
+        const int i = i0 + ii;
         const int64_t col = col_base + j * 16, row = row_base + i * 16;
-        const f32x4 xv = Vec4<T>::ld(XT + col * mp + row);  // X[row + v][col]
+        const f32x4 xv = Vec4<T>::cvt(xraw[ii][j]);
         f32x4 val;
 #pragma unroll
         for (int v = 0; v < 4; ++v) val[v] = fmaf(s.a, xv[v], acc[i][j][v]) * inv;
@@ -353,6 +389,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
 #pragma unroll
           for (int v = 0; v < 4; ++v) WsType<T>::st(Xn, (row + v) * np + col, val[v]);
       }
+    }
     if constexpr (kStage)
       stage_tile_flush(lds, reinterpret_cast<uint16_t *>(Xn) + static_cast<int64_t>(ti) * kTile * np +
                                 static_cast<int64_t>(tj) * kTile, np, tid);
@@ -366,45 +403,65 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
     const T *Xsrc = static_cast<const T *>(swap ? d.x[cur] : d.xt[cur]);
     const int64_t xld = swap ? d.np : d.mp;
     const bool vec_ok = (d.cols & 3) == 0;  // rows of P start 4-element aligned
+    const bool pbf = d.param_dt == kBF16;
+    constexpr int kRows = sizeof(T) == 2 ? 2 : 1;  // fragment rows per read batch
 #pragma unroll
-    for (int i = 0; i < kFragM; ++i)
+    for (int i0 = 0; i0 < kFragM; i0 += kRows) {
+      // reads of the batch first (X and, on the vector path, P)
+      typename Vec4<T>::Raw xraw[kRows][kFragN];
+      u32x4 praw[kRows][kFragN];
 #pragma unroll
-      for (int j = 0; j < kFragN; ++j) {
-        const int64_t q = col_base + j * 16, p = row_base + i * 16;
-        if (p >= p_lim || q >= q_lim) continue;
-        const f32x4 xv = Vec4<T>::ld(Xsrc + q * xld + p);  // X at the same positions
-        f32x4 o;
+      for (int ii = 0; ii < kRows; ++ii)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) o[v] = fmaf(s.a, xv[v], acc[i][j][v]) * inv;
-        const int64_t pidx = q * d.cols + p;
-        if (vec_ok && p + 4 <= p_lim) {
-          if (d.param_dt == kBF16) {
-            uint16_t *P = static_cast<uint16_t *>(d.param) + pidx;
-            const f32x4 pv = Vec4<uint16_t>::ld(P);
-            f32x4 nv;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) nv[v] = fmaf(-step, o[v], pv[v]);
-            Vec4<uint16_t>::st(P, nv);
-            if (d.orth) Vec4<uint16_t>::st(static_cast<uint16_t *>(d.orth) + pidx, o);
-          } else {
-            float *P = static_cast<float *>(d.param) + pidx;
-            const f32x4 pv = Vec4<float>::ld(P);
-            f32x4 nv;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) nv[v] = fmaf(-step, o[v], pv[v]);
-            Vec4<float>::st(P, nv);
-            if (d.orth) Vec4<float>::st(static_cast<float *>(d.orth) + pidx, o);
-          }
-        } else {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            if (p + v >= p_lim) break;
-            if (d.orth) store_elem(d.orth, d.param_dt, pidx + v, o[v]);
-            store_elem(d.param, d.param_dt, pidx + v,
-                       fmaf(-step, o[v], load_elem(d.param, d.param_dt, pidx + v)));
+        for (int j = 0; j < kFragN; ++j) {
+          const int64_t q = col_base + j * 16, p = row_base + (i0 + ii) * 16;
+          xraw[ii][j] = Vec4<T>::raw(Xsrc + q * xld + p);  // in the padded buffer
+          if (vec_ok && p + 4 <= p_lim && q < q_lim) {
+            const int64_t pidx = q * d.cols + p;
+            if (pbf) {
+              const u32x2 v = *(const g_u32x2 *)(static_cast<const uint16_t *>(d.param) + pidx);
+              praw[ii][j] = u32x4{v.x, v.y, 0u, 0u};
+            } else {
+              praw[ii][j] = *(const g_u32x4 *)(static_cast<const float *>(d.param) + pidx);
+            }
           }
         }
-      }
+#pragma unroll
+      for (int ii = 0; ii < kRows; ++ii)
+#pragma unroll
+        for (int j = 0; j < kFragN; ++j) {
+          const int i = i0 + ii;
+          const int64_t q = col_base + j * 16, p = row_base + i * 16;
+          if (p >= p_lim || q >= q_lim) continue;
+          const f32x4 xv = Vec4<T>::cvt(xraw[ii][j]);
+          f32x4 o;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) o[v] = fmaf(s.a, xv[v], acc[i][j][v]) * inv;
+          const int64_t pidx = q * d.cols + p;
+          if (vec_ok && p + 4 <= p_lim) {
+            const u32x4 pr = praw[ii][j];
+            const f32x4 pv = pbf ? Vec4<uint16_t>::cvt(u32x2{pr.x, pr.y}) : Vec4<float>::cvt(pr);
+            f32x4 nv;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) nv[v] = fmaf(-step, o[v], pv[v]);
+            if (pbf) {
+              Vec4<uint16_t>::st(static_cast<uint16_t *>(d.param) + pidx, nv);
+              if (d.orth) Vec4<uint16_t>::st(static_cast<uint16_t *>(d.orth) + pidx, o);
+            } else {
+              Vec4<float>::st(static_cast<float *>(d.param) + pidx, nv);
+              if (d.orth) Vec4<float>::st(static_cast<float *>(d.orth) + pidx, o);
+            }
+          } else {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              if (p + v >= p_lim) break;
+              if (d.orth) store_elem(d.orth, d.param_dt, pidx + v, o[v]);
+              store_elem(d.param, d.param_dt, pidx + v,
+                         fmaf(-step, o[v], load_elem(d.param, d.param_dt, pidx + v)));
+            }
+          }
+        }
+    }
   }
 }
 
