@@ -57,6 +57,24 @@ class TraceEvents:
         return self.ev[j].elapsed_time(self.ev[j + 1])
 
 
+def measured_traffic(workload_name: str, fp32: bool):
+    """HBM bytes per Apply launch from the committed rocprofv3 counter
+    summary (FETCH_SIZE and WRITE_SIZE scaled by a copy kernel of known
+    size), or None when the summary is for another workload or the GEMM
+    source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "apply_traffic_llama31_8b_owner0.json")
+    src = os.path.join(ROOT, "newton_schulz_dmuon_amd", "csrc", "gemm.hip")
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    if fp32 or rec.get("workload") != workload_name or rec.get("gemm_source_sha256") != sha:
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
 def owner_share(w, nsd):
     shapes = w.shapes
     if w.n_owners > 1:
@@ -253,7 +271,8 @@ def main(argv=None) -> int:
         ach = apply_flops / (stages["apply"]["ms"] * 1e-3) / 1e12
         roofline = {"bound": "mfma", "kernel": "ns_gemm_kernel<Apply> (X <- aX + BX)",
                     "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
-                    "frac": round(ach / peak, 4), "traffic": None,
+                    "frac": round(ach / peak, 4),
+                    "traffic": measured_traffic(w.name, args.fp32_ns),
                     "algorithmic_flops_per_launch": apply_flops}
 
     out = {
