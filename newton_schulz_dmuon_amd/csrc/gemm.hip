@@ -155,37 +155,22 @@ __device__ __forceinline__ void stage_tile_flush(lds_char *lds, uint16_t *dst, i
   }
 }
 
-// Upper-triangle tile t (row-major enumeration) of a tm x tm tile grid.
-__device__ __forceinline__ void upper_tile(int32_t t, int32_t tm, int32_t &ti, int32_t &tj) {
-  int32_t r = 0;
-  while (t >= tm - r) { t -= tm - r; ++r; }
-  ti = r;
-  tj = r + t;
-}
-
 template <typename T, int MODE>
 __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restrict__ mats,
-                                                           const StageEntry *__restrict__ stage,
-                                                           int32_t nstage, int32_t cur,
+                                                           const TileEntry *__restrict__ tiles,
+                                                           StageXcd xcd, int32_t cur,
                                                            int32_t first, StepScalars s) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * kOperandBytes];  // 128 KB
   // C cast: generic -> LDS address space.  [2 stages][L, R][256 rows][128 B]
   lds_char *const lds = (lds_char *)smem;
 
-  const int64_t w = blockIdx.x;
-  const int32_t si = find_range(nstage, w, [&](int32_t i) { return stage[i].first; });
-  const MatDev &d = mats[stage[si].mat];
-  const int32_t t = static_cast<int32_t>(w - stage[si].first);
-
-  int32_t ti, tj;
-  constexpr bool kSym = (MODE == kModeGram || MODE == kModeSquare);
-  if (kSym) {
-    upper_tile(t, d.tm, ti, tj);
-  } else {
-    // column of tiles first: consecutive work-groups share the X^T panel
-    ti = t % d.tm;
-    tj = t / d.tm;
-  }
+  // this work-group's tile: entry w / 8 of XCD (w % 8)'s list
+  const int32_t w = static_cast<int32_t>(blockIdx.x);
+  const int32_t xi = w % kXcds, k = w / kXcds;
+  if (k >= xcd.count[xi]) return;  // whole group leaves before any barrier
+  const TileEntry e = tiles[xcd.first[xi] + k];
+  const MatDev &d = mats[e.mat];
+  const int32_t ti = e.ti, tj = e.tj;
 
   const T *L, *R;
   int64_t ld;  // elements; both operands have the same leading dimension
@@ -466,21 +451,24 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
 }
 
 template <typename T>
-hipError_t launch_t(GemmMode mode, const MatDev *mats, const StageEntry *stage, int32_t nstage,
-                    int64_t total, int32_t cur, int32_t first, StepScalars s, hipStream_t st) {
-  const dim3 grid(static_cast<uint32_t>(total)), block(kThreads);
+hipError_t launch_t(GemmMode mode, const MatDev *mats, const TileEntry *tiles, const StageXcd &xcd,
+                    int32_t cur, int32_t first, StepScalars s, hipStream_t st) {
+  int32_t longest = 0;
+  for (int x = 0; x < kXcds; ++x) longest = xcd.count[x] > longest ? xcd.count[x] : longest;
+  if (longest == 0) return hipSuccess;
+  const dim3 grid(static_cast<uint32_t>(longest) * kXcds), block(kThreads);
   switch (mode) {
     case kModeGram:
-      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeGram>), grid, block, 0, st, mats, stage, nstage, cur, first, s);
+      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeGram>), grid, block, 0, st, mats, tiles, xcd, cur, first, s);
       break;
     case kModeSquare:
-      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeSquare>), grid, block, 0, st, mats, stage, nstage, cur, first, s);
+      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeSquare>), grid, block, 0, st, mats, tiles, xcd, cur, first, s);
       break;
     case kModeApply:
-      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeApply>), grid, block, 0, st, mats, stage, nstage, cur, first, s);
+      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeApply>), grid, block, 0, st, mats, tiles, xcd, cur, first, s);
       break;
     default:
-      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeFinal>), grid, block, 0, st, mats, stage, nstage, cur, first, s);
+      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeFinal>), grid, block, 0, st, mats, tiles, xcd, cur, first, s);
       break;
   }
   return hipGetLastError();
@@ -488,13 +476,12 @@ hipError_t launch_t(GemmMode mode, const MatDev *mats, const StageEntry *stage, 
 
 }  // namespace
 
-hipError_t launch_ns_stage(GemmMode mode, bool fp32, const MatDev *mats, const StageEntry *stage,
-                           int32_t nstage, int64_t total_tiles, int32_t cur, bool first,
-                           StepScalars s, hipStream_t st) {
-  if (total_tiles == 0) return hipSuccess;
+hipError_t launch_ns_stage(GemmMode mode, bool fp32, const MatDev *mats, const TileEntry *tiles,
+                           const StageXcd &xcd, int32_t cur, bool first, StepScalars s,
+                           hipStream_t st) {
   const int32_t f = first ? 1 : 0;
-  return fp32 ? launch_t<float>(mode, mats, stage, nstage, total_tiles, cur, f, s, st)
-              : launch_t<uint16_t>(mode, mats, stage, nstage, total_tiles, cur, f, s, st);
+  return fp32 ? launch_t<float>(mode, mats, tiles, xcd, cur, f, s, st)
+              : launch_t<uint16_t>(mode, mats, tiles, xcd, cur, f, s, st);
 }
 
 }  // namespace dmuon

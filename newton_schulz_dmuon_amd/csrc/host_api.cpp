@@ -112,14 +112,67 @@ int validate_shapes(const dmuon_matrix *mats, int32_t n) {
 // ------------------------------------------------------------------- plan --
 struct Plan {
   std::vector<MatDev> mats;
-  std::vector<StageEntry> stage[3];  // gram, square, apply
-  int64_t stage_total[3] = {0, 0, 0};
+  std::vector<TileEntry> tiles[3];  // gram, square, apply: XCD lists back to back
+  StageXcd xcd[3];
   int64_t ew_total = 0, tr_total = 0;
   // workspace layout (byte offsets)
   int64_t off_mats = 0, off_stage[3] = {0, 0, 0}, off_partials = 0, off_inv = 0, off_ns = 0;
   int64_t table_bytes = 0;  // [0, table_bytes) is uploaded
   int64_t total_bytes = 0;
 };
+
+// Tile lists of one grouped GEMM stage (0 Gram, 1 Square, 2 Apply), one per
+// XCD.  Tiles are grouped into blocks that share operand panels: 4 x 4 tile
+// blocks of the upper triangle for the symmetric products (they read panels
+// ti and tj of one matrix), 4 x 8 blocks for Apply (B panel ti, X^T panel
+// tj).  Blocks go, costliest first (tiles x K depth, ties in matrix order),
+// to the XCD with the least work so far; each XCD's list keeps that order, so
+// its 32 CUs work through long-K tiles first and the tiles running together
+// on one XCD read few distinct panels through its L2.
+void build_stage_tiles(const std::vector<MatDev> &mats, int st, std::vector<TileEntry> &out,
+                       StageXcd &xcd) {
+  struct Block {
+    int64_t cost;
+    int32_t mat, ti0, tj0;
+  };
+  const bool sym = st < 2;
+  const int bm = 4, bn = sym ? 4 : 8;
+  std::vector<Block> blocks;
+  for (int32_t i = 0; i < static_cast<int32_t>(mats.size()); ++i) {
+    const MatDev &d = mats[i];
+    const int64_t depth = st == 0 ? d.np : d.mp;
+    const int32_t rows = d.tm, cols = sym ? d.tm : d.tn;
+    for (int32_t bi = 0; bi < rows; bi += bm)
+      for (int32_t bj = sym ? bi : 0; bj < cols; bj += bn) {
+        int64_t nt = 0;
+        for (int32_t ti = bi; ti < std::min(bi + bm, rows); ++ti)
+          for (int32_t tj = bj; tj < std::min(bj + bn, cols); ++tj) nt += (!sym || tj >= ti);
+        if (nt) blocks.push_back(Block{nt * depth, i, bi, bj});
+      }
+  }
+  std::stable_sort(blocks.begin(), blocks.end(),
+                   [](const Block &x, const Block &y) { return x.cost > y.cost; });
+  std::vector<TileEntry> lists[kXcds];
+  int64_t load[kXcds] = {0};
+  for (const Block &b : blocks) {
+    int x = 0;
+    for (int y = 1; y < kXcds; ++y)
+      if (load[y] < load[x]) x = y;
+    load[x] += b.cost;
+    const MatDev &d = mats[b.mat];
+    const int32_t rows = d.tm, cols = sym ? d.tm : d.tn;
+    for (int32_t ti = b.ti0; ti < std::min(b.ti0 + bm, rows); ++ti)
+      for (int32_t tj = b.tj0; tj < std::min(b.tj0 + bn, cols); ++tj)
+        if (!sym || tj >= ti)
+          lists[x].push_back(TileEntry{b.mat, static_cast<uint16_t>(ti), static_cast<uint16_t>(tj)});
+  }
+  out.clear();
+  for (int x = 0; x < kXcds; ++x) {
+    xcd.first[x] = static_cast<int32_t>(out.size());
+    xcd.count[x] = static_cast<int32_t>(lists[x].size());
+    out.insert(out.end(), lists[x].begin(), lists[x].end());
+  }
+}
 
 // Builds the plan; with ws == nullptr only sizes are computed.
 void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg, char *ws,
@@ -158,25 +211,13 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
   p.ew_total = ew;
   p.tr_total = K > 0 ? tr : 0;
 
-  // grouped launch order per stage: longest tiles first (K-depth of a tile
-  // is n_p for Gram, m_p for Square and Apply), ties in input order
   for (int st = 0; st < 3; ++st) {
-    std::vector<int32_t> order(n);
-    std::iota(order.begin(), order.end(), 0);
-    std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
-      const int64_t kx = st == 0 ? p.mats[x].np : p.mats[x].mp;
-      const int64_t ky = st == 0 ? p.mats[y].np : p.mats[y].mp;
-      return kx > ky;
-    });
-    p.stage[st].clear();
-    int64_t first = 0;
-    for (int32_t i : order) {
-      const MatDev &d = p.mats[i];
-      const int64_t cnt = st < 2 ? int64_t(d.tm) * (d.tm + 1) / 2 : int64_t(d.tm) * d.tn;
-      p.stage[st].push_back(StageEntry{first, i, static_cast<int32_t>(cnt)});
-      first += cnt;
+    if (K > 0) {
+      build_stage_tiles(p.mats, st, p.tiles[st], p.xcd[st]);
+    } else {
+      p.tiles[st].clear();
+      std::memset(&p.xcd[st], 0, sizeof(StageXcd));
     }
-    p.stage_total[st] = K > 0 ? first : 0;
   }
 
   // workspace layout
@@ -185,7 +226,7 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
   off = round_up(off + int64_t(sizeof(MatDev)) * n, 256);
   for (int st = 0; st < 3; ++st) {
     p.off_stage[st] = off;
-    off = round_up(off + int64_t(sizeof(StageEntry)) * n, 256);
+    off = round_up(off + int64_t(sizeof(TileEntry)) * static_cast<int64_t>(p.tiles[st].size()), 256);
   }
   p.table_bytes = off;
   p.off_partials = off;
@@ -417,15 +458,17 @@ static int muon_step_impl(const dmuon_matrix *mats, int32_t n, const dmuon_step_
   std::vector<char> tables(static_cast<size_t>(p.table_bytes), 0);
   std::memcpy(tables.data() + p.off_mats, p.mats.data(), sizeof(MatDev) * n);
   for (int st = 0; st < 3; ++st)
-    std::memcpy(tables.data() + p.off_stage[st], p.stage[st].data(), sizeof(StageEntry) * n);
+    if (!p.tiles[st].empty())
+      std::memcpy(tables.data() + p.off_stage[st], p.tiles[st].data(),
+                  sizeof(TileEntry) * p.tiles[st].size());
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   rc = upload(ws, tables, s);
   if (rc) return rc;
 
   const MatDev *dm = reinterpret_cast<const MatDev *>(ws + p.off_mats);
-  const StageEntry *dst[3];
-  for (int st = 0; st < 3; ++st) dst[st] = reinterpret_cast<const StageEntry *>(ws + p.off_stage[st]);
+  const TileEntry *dst[3];
+  for (int st = 0; st < 3; ++st) dst[st] = reinterpret_cast<const TileEntry *>(ws + p.off_stage[st]);
   StepScalars sc{cfg->a, cfg->b, cfg->c, cfg->lr, cfg->momentum, cfg->eps,
                  (cfg->flags & DMUON_FLAG_NESTEROV) ? 1 : 0, 0};
   const bool fp32 = cfg->flags & DMUON_FLAG_NS_FP32;
@@ -459,16 +502,14 @@ static int muon_step_impl(const dmuon_matrix *mats, int32_t n, const dmuon_step_
   for (int k = 0; k < cfg->ns_steps; ++k) {
     const int32_t cur = k & 1;
     const bool last = k + 1 == cfg->ns_steps, first = k == 0;
-    if ((rc = launched(launch_ns_stage(kModeGram, fp32, dm, dst[0], n, p.stage_total[0], cur, first,
-                                       sc, s),
+    if ((rc = launched(launch_ns_stage(kModeGram, fp32, dm, dst[0], p.xcd[0], cur, first, sc, s),
                        "gram launch")))
       return rc;
-    if ((rc = launched(launch_ns_stage(kModeSquare, fp32, dm, dst[1], n, p.stage_total[1], cur,
-                                       first, sc, s),
+    if ((rc = launched(launch_ns_stage(kModeSquare, fp32, dm, dst[1], p.xcd[1], cur, first, sc, s),
                        "square launch")))
       return rc;
-    if ((rc = launched(launch_ns_stage(last ? kModeFinal : kModeApply, fp32, dm, dst[2], n,
-                                       p.stage_total[2], cur, first, sc, s),
+    if ((rc = launched(launch_ns_stage(last ? kModeFinal : kModeApply, fp32, dm, dst[2], p.xcd[2],
+                                       cur, first, sc, s),
                        "apply launch")))
       return rc;
   }

@@ -51,12 +51,19 @@ struct MatDev {
   int32_t tm, tn;       // mp / kGemmTile, np / kGemmTile
 };
 
-// A matrix's slice of one GEMM stage's launch: work-groups
-// [first, first + count) of the launch compute its tiles.
-struct StageEntry {
-  int64_t first;
+// One 256 x 256 output tile of a grouped GEMM stage.
+struct TileEntry {
   int32_t mat;
-  int32_t count;
+  uint16_t ti, tj;
+};
+
+// Work-groups are handed to the 8 XCDs (each with its own L2) in turn: group
+// w runs on XCD w % 8.  A stage therefore keeps one tile list per XCD, and
+// group w computes entry first[w % 8] + w / 8 if w / 8 < count[w % 8].
+constexpr int kXcds = 8;
+struct StageXcd {
+  int32_t first[kXcds];
+  int32_t count[kXcds];
 };
 
 struct StepScalars {
@@ -104,8 +111,7 @@ hipError_t launch_pack_batch(const PackBatch &b, hipStream_t st);
 // first: the first iteration, whose X holds U unnormalised: Gram scales by
 // inv_norm^2 and Apply / Final by inv_norm.
 hipError_t launch_ns_stage(GemmMode mode, bool fp32, const MatDev *mats,
-                           const StageEntry *stage, int32_t nstage,
-                           int64_t total_tiles, int32_t cur, bool first,
-                           StepScalars s, hipStream_t st);
+                           const TileEntry *tiles, const StageXcd &xcd,
+                           int32_t cur, bool first, StepScalars s, hipStream_t st);
 
 }  // namespace dmuon
