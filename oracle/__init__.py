@@ -15,10 +15,11 @@ Modules
                       Newton-Schulz iteration, scaled update, whole step.
 ``oracle.pack``       per-owner contiguous buffer: pack / unpack (bit copies).
 ``oracle.partition``  balanced (LPT greedy) owner assignment and pack offsets.
+``oracle.adamw``      AdamW step for the parameters Muon does not own.
 
 Every function is pinned by a ``-m "not gpu"`` test against something other
 than itself (closed forms, library routines, invariants, brute force).  No
 function is "parity unpinned".
 """
 
-from . import muon, pack, partition  # noqa: F401
+from . import adamw, muon, pack, partition  # noqa: F401
