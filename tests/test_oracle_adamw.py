@@ -21,9 +21,12 @@ def test_matches_torch_adamw_fp64(wd):
         opt.step()
         P, M, V = adamw_step(P, g, M, V, AdamWConfig(3e-3, 0.8, 0.99, 1e-6, wd, t))
         st = opt.state[p]
+        # torch forms the first moment with lerp, m + (1 - beta1)(g - m), which
+        # rounds differently where the two terms nearly cancel: absolute
+        # tolerance relative to the tensor's scale
         assert np.allclose(P, p.detach().numpy(), rtol=1e-13, atol=1e-16)
-        assert np.allclose(M, st["exp_avg"].numpy(), rtol=1e-13, atol=1e-20)
-        assert np.allclose(V, st["exp_avg_sq"].numpy(), rtol=1e-13, atol=1e-24)
+        assert np.allclose(M, st["exp_avg"].numpy(), rtol=1e-12, atol=1e-15 * np.abs(M).max())
+        assert np.allclose(V, st["exp_avg_sq"].numpy(), rtol=1e-12, atol=1e-15 * np.abs(V).max())
 
 
 def test_constant_gradient_closed_form():
