@@ -175,6 +175,40 @@ int dmuon_muon_step(const dmuon_matrix *mats, int32_t n,
                     const dmuon_step_config *cfg, void *workspace,
                     size_t workspace_bytes, void *stream);
 
+/* One tensor of the AdamW step: any shape, numel contiguous elements. */
+typedef struct {
+  void *param;          /* numel elements, param_dtype, updated in place      */
+  int32_t param_dtype;  /* DMUON_BF16 or DMUON_F32                           */
+  int32_t grad_dtype;   /* DMUON_BF16 or DMUON_F32                           */
+  const void *grad;     /* numel elements, read only                         */
+  float *exp_avg;       /* numel fp32 first moment, updated in place         */
+  float *exp_avg_sq;    /* numel fp32 second moment, updated in place        */
+  int64_t numel;        /* >= 1                                              */
+} dmuon_tensor;
+
+/* AdamW hyper-parameters.  The landing page's optimizer call takes an
+ * adamw_lr (1e-3 in its example, "LLM Pretraining"); betas, eps and weight
+ * decay are not on the pages. */
+typedef struct {
+  float lr;             /* finite                                            */
+  float beta1, beta2;   /* in [0, 1)                                         */
+  float eps;            /* finite, > 0                                       */
+  float weight_decay;   /* finite (decoupled: P <- P - lr*wd*P)              */
+  int32_t step;         /* 1-based step count t, for the bias corrections    */
+} dmuon_adamw_config;
+
+/* AdamW on the parameters the Muon step does not own (landing page, "VLA and
+ * VLM": parameters the predicate does not select stay under the ordinary
+ * sharded setup; "LLM Pretraining": adamw_lr).  Per element, in fp32:
+ *   P <- P - lr*wd*P;  M <- b1*M + (1-b1)*G;  V <- b2*V + (1-b2)*G^2
+ *   P <- P - lr * (M / (1 - b1^t)) / (sqrt(V / (1 - b2^t)) + eps)
+ * n = 0 is a no-op.  Pointers 16-byte aligned.
+ * Errors: INVALID_ARG (NULL pointer, numel < 1, step < 1, beta outside
+ * [0, 1), eps <= 0, non-finite value), UNSUPPORTED_DTYPE, MISALIGNED, ALIAS
+ * (a written buffer overlaps another buffer of the call), HIP. */
+int dmuon_adamw_step(const dmuon_tensor *tensors, int32_t n,
+                     const dmuon_adamw_config *cfg, void *stream);
+
 /* dmuon_muon_step that also records caller-created HIP events (hipEvent_t,
  * passed as void*) on `stream`, for per-kernel timing: events[0] before the
  * first launch and events[j] right after the j-th launch.  Launch order:

@@ -30,7 +30,8 @@ FLAG_NESTEROV = 1 << 1
 
 EXPORTED = ("dmuon_abi_version", "dmuon_error_string", "dmuon_last_error",
             "dmuon_partition_lpt", "dmuon_pack_offsets", "dmuon_workspace_bytes",
-            "dmuon_pack", "dmuon_unpack", "dmuon_muon_step", "dmuon_muon_step_traced")
+            "dmuon_pack", "dmuon_unpack", "dmuon_muon_step", "dmuon_muon_step_traced",
+            "dmuon_adamw_step")
 
 
 class Matrix(ctypes.Structure):
@@ -57,6 +58,27 @@ class StepConfig(ctypes.Structure):
         ("ns_steps", ctypes.c_int32),
         ("lr", ctypes.c_float), ("momentum", ctypes.c_float), ("eps", ctypes.c_float),
         ("flags", ctypes.c_uint32),
+    ]
+
+
+class Tensor(ctypes.Structure):
+    """``dmuon_tensor``"""
+    _fields_ = [
+        ("param", ctypes.c_void_p),
+        ("param_dtype", ctypes.c_int32),
+        ("grad_dtype", ctypes.c_int32),
+        ("grad", ctypes.c_void_p),
+        ("exp_avg", ctypes.c_void_p),
+        ("exp_avg_sq", ctypes.c_void_p),
+        ("numel", ctypes.c_int64),
+    ]
+
+
+class AdamWConfig(ctypes.Structure):
+    """``dmuon_adamw_config``"""
+    _fields_ = [
+        ("lr", ctypes.c_float), ("beta1", ctypes.c_float), ("beta2", ctypes.c_float),
+        ("eps", ctypes.c_float), ("weight_decay", ctypes.c_float), ("step", ctypes.c_int32),
     ]
 
 
@@ -98,8 +120,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dmuon_muon_step.argtypes = [P(Matrix), c_i32, P(StepConfig), vp, ctypes.c_size_t, vp]
     lib.dmuon_muon_step_traced.argtypes = [P(Matrix), c_i32, P(StepConfig), vp,
                                            ctypes.c_size_t, vp, P(vp), c_i32]
+    lib.dmuon_adamw_step.argtypes = [P(Tensor), c_i32, P(AdamWConfig), vp]
     for name in ("dmuon_partition_lpt", "dmuon_pack_offsets", "dmuon_workspace_bytes",
-                 "dmuon_pack", "dmuon_unpack", "dmuon_muon_step", "dmuon_muon_step_traced"):
+                 "dmuon_pack", "dmuon_unpack", "dmuon_muon_step", "dmuon_muon_step_traced",
+            "dmuon_adamw_step"):
         getattr(lib, name).restype = ctypes.c_int
     if lib.dmuon_abi_version() != ABI_VERSION:
         raise ImportError(f"libdmuon ABI {lib.dmuon_abi_version()} != {ABI_VERSION}")

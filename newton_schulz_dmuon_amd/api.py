@@ -12,7 +12,7 @@ from dataclasses import dataclass
 from typing import Optional, Sequence
 
 from . import _lib
-from ._lib import DmuonError, Matrix, StepConfig, check, load
+from ._lib import AdamWConfig, DmuonError, Matrix, StepConfig, Tensor, check, load
 
 # Public Muon quintic (Jordan et al., 2024); the DMuon pages print none.
 QUINTIC = (3.4445, -4.7750, 2.0315)
@@ -158,3 +158,35 @@ def pack_offsets(numels: Sequence[int], align: int = 128):
     total = ctypes.c_int64(0)
     check(load().dmuon_pack_offsets(arr, n, int(align), offs, ctypes.byref(total)))
     return list(offs[:n]), total.value
+
+
+@dataclass
+class AdamWOptions:
+    """``dmuon_adamw_config``; ``lr`` default is the landing page's
+    ``adamw_lr`` (1e-3), the rest are not on the pages (PyTorch's AdamW
+    defaults)."""
+
+    lr: float = 1e-3
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 0.01
+
+    def to_c(self, step: int) -> AdamWConfig:
+        return AdamWConfig(self.lr, self.beta1, self.beta2, self.eps, self.weight_decay, int(step))
+
+
+def adamw_step(params: Sequence, grads: Sequence, exp_avgs: Sequence, exp_avg_sqs: Sequence,
+               step: int, opts: AdamWOptions = AdamWOptions(), stream=None) -> None:
+    """AdamW on the non-Muon parameters, in place (tensors of any shape)."""
+    n = len(params)
+    if n == 0:
+        return
+    arr = (Tensor * n)()
+    for i in range(n):
+        p, g = params[i], grads[i]
+        arr[i] = Tensor(_ptr(p), _dtype_code(p), _dtype_code(g), _ptr(g), _ptr(exp_avgs[i]),
+                        _ptr(exp_avg_sqs[i]), p.numel())
+    cfg = opts.to_c(step)
+    check(load().dmuon_adamw_step(arr, n, ctypes.byref(cfg),
+                                  _stream_handle(params[0].device, stream)))

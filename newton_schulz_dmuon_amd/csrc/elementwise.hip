@@ -29,7 +29,7 @@ __device__ __forceinline__ double block_sum_f64(double v, double *lds) {
   return s;  // valid in thread 0
 }
 
-// Four consecutive grad values at flat index i (i multiple of 4).
+// Four consecutive bf16 or fp32 values at flat index i (i multiple of 4).
 __device__ __forceinline__ f32x4 load_grad4(const void *g, int32_t dt, int64_t i) {
   f32x4 r;
   if (dt == kBF16) {
@@ -217,6 +217,59 @@ __global__ __launch_bounds__(kEwThreads) void update_direct_kernel(
   }
 }
 
+// AdamW over a batch of tensors: 32 elements per thread, 4-wide vectors
+// where the tensor's length allows.
+__device__ __forceinline__ void adamw_elem(float &p, float g, float &m, float &v,
+                                           const AdamScalars &s) {
+  p *= s.decay;
+  m = fmaf(s.beta1, m, (1.f - s.beta1) * g);
+  v = fmaf(s.beta2, v, (1.f - s.beta2) * g * g);
+  const float denom = fmaf(sqrtf(v), s.inv_sqrt_bc2, s.eps);
+  p = fmaf(-s.step_size, m / denom, p);
+}
+
+__global__ __launch_bounds__(kEwThreads) void adamw_kernel(AdamBatch b, AdamScalars s) {
+  const int64_t w = blockIdx.x;
+  const int32_t ti = find_range(b.n, w, [&](int32_t i) { return b.first_block[i]; });
+  const int64_t numel = b.numel[ti];
+  const int64_t base = (w - b.first_block[ti]) * kEwChunk;
+  float *M = b.m[ti], *V = b.v[ti];
+  void *P = b.param[ti];
+  const void *G = b.grad[ti];
+  const int32_t pdt = b.param_dt[ti], gdt = b.grad_dt[ti];
+#pragma unroll
+  for (int k = 0; k < kEwPerThread / 4; ++k) {
+    const int64_t i = base + (static_cast<int64_t>(k) * kEwThreads + threadIdx.x) * 4;
+    if (i + 4 <= numel) {
+      float4 mv = *reinterpret_cast<const float4 *>(M + i);
+      float4 vv = *reinterpret_cast<const float4 *>(V + i);
+      const f32x4 g = load_grad4(G, gdt, i);
+      const f32x4 pv = load_grad4(P, pdt, i);
+      float p[4] = {pv[0], pv[1], pv[2], pv[3]};
+      adamw_elem(p[0], g[0], mv.x, vv.x, s);
+      adamw_elem(p[1], g[1], mv.y, vv.y, s);
+      adamw_elem(p[2], g[2], mv.z, vv.z, s);
+      adamw_elem(p[3], g[3], mv.w, vv.w, s);
+      *reinterpret_cast<float4 *>(M + i) = mv;
+      *reinterpret_cast<float4 *>(V + i) = vv;
+      if (pdt == kBF16) {
+        uint2 u;
+        u.x = f32_to_bf16_bits(p[0]) | (static_cast<uint32_t>(f32_to_bf16_bits(p[1])) << 16);
+        u.y = f32_to_bf16_bits(p[2]) | (static_cast<uint32_t>(f32_to_bf16_bits(p[3])) << 16);
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(P) + i) = u;
+      } else {
+        *reinterpret_cast<float4 *>(static_cast<float *>(P) + i) = make_float4(p[0], p[1], p[2], p[3]);
+      }
+    } else {
+      for (int64_t j = i; j < numel && j < i + 4; ++j) {
+        float p = load_elem(P, pdt, j);
+        adamw_elem(p, load_elem(G, gdt, j), M[j], V[j], s);
+        store_elem(P, pdt, j, p);
+      }
+    }
+  }
+}
+
 constexpr int kPackThreads = 256;
 
 // Byte copies of a batch of matrices; 16-byte vectors for the body, bytes
@@ -264,6 +317,12 @@ hipError_t launch_update_direct(const MatDev *mats, int32_t nmat, int64_t total_
                                 StepScalars s, hipStream_t st) {
   hipLaunchKernelGGL(update_direct_kernel, dim3((uint32_t)total_chunks), dim3(kEwThreads), 0,
                      st, mats, nmat, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_adamw_batch(const AdamBatch &b, AdamScalars s, hipStream_t st) {
+  if (b.n == 0) return hipSuccess;
+  hipLaunchKernelGGL(adamw_kernel, dim3((uint32_t)b.first_block[b.n]), dim3(kEwThreads), 0, st, b, s);
   return hipGetLastError();
 }
 

@@ -527,6 +527,79 @@ int dmuon_muon_step_traced(const dmuon_matrix *mats, int32_t n, const dmuon_step
   return muon_step_impl(mats, n, cfg, workspace, workspace_bytes, stream, events, n_events);
 }
 
+// ------------------------------------------------------------------ AdamW --
+int dmuon_adamw_step(const dmuon_tensor *tensors, int32_t n, const dmuon_adamw_config *cfg,
+                     void *stream) {
+  g_last_error.clear();
+  if (!cfg) return fail(DMUON_ERR_INVALID_ARG, "cfg is NULL");
+  const float vals[] = {cfg->lr, cfg->beta1, cfg->beta2, cfg->eps, cfg->weight_decay};
+  for (float v : vals)
+    if (!std::isfinite(v)) return fail(DMUON_ERR_INVALID_ARG, "non-finite AdamW value");
+  if (cfg->beta1 < 0.f || cfg->beta1 >= 1.f || cfg->beta2 < 0.f || cfg->beta2 >= 1.f)
+    return fail(DMUON_ERR_INVALID_ARG, "betas must lie in [0, 1)");
+  if (cfg->eps <= 0.f) return fail(DMUON_ERR_INVALID_ARG, "eps must be > 0");
+  if (cfg->step < 1) return fail(DMUON_ERR_INVALID_ARG, "step must be >= 1");
+  if (n < 0) return fail(DMUON_ERR_INVALID_ARG, "n < 0");
+  if (n == 0) return DMUON_OK;
+  if (!tensors) return fail(DMUON_ERR_INVALID_ARG, "tensors is NULL");
+  std::vector<Interval> iv;
+  for (int32_t i = 0; i < n; ++i) {
+    const dmuon_tensor &t = tensors[i];
+    if (t.numel < 1 || t.numel > kMaxNumel)
+      return fail(DMUON_ERR_INVALID_ARG, "tensor %d: numel %lld", i, (long long)t.numel);
+    if (!dtype_ok(t.param_dtype) || !dtype_ok(t.grad_dtype))
+      return fail(DMUON_ERR_UNSUPPORTED_DTYPE, "tensor %d: dtype codes %d/%d", i, t.param_dtype,
+                  t.grad_dtype);
+    if (!t.param || !t.grad || !t.exp_avg || !t.exp_avg_sq)
+      return fail(DMUON_ERR_INVALID_ARG, "tensor %d: NULL pointer", i);
+    if (!aligned16(t.param) || !aligned16(t.grad) || !aligned16(t.exp_avg) ||
+        !aligned16(t.exp_avg_sq))
+      return fail(DMUON_ERR_MISALIGNED, "tensor %d: pointers must be 16-byte aligned", i);
+    const uintptr_t ne = static_cast<uintptr_t>(t.numel);
+    auto add = [&](const void *ptr, int64_t es, bool w, const char *what) {
+      const uintptr_t lo = reinterpret_cast<uintptr_t>(ptr);
+      iv.push_back(Interval{lo, lo + ne * es, w, what, i});
+    };
+    add(t.param, elem_size(t.param_dtype), true, "param");
+    add(t.grad, elem_size(t.grad_dtype), false, "grad");
+    add(t.exp_avg, 4, true, "exp_avg");
+    add(t.exp_avg_sq, 4, true, "exp_avg_sq");
+  }
+  int rc = check_aliasing(iv);
+  if (rc) return rc;
+  const double lr = cfg->lr, b1 = cfg->beta1, b2 = cfg->beta2;
+  AdamScalars sc;
+  sc.decay = static_cast<float>(1.0 - lr * cfg->weight_decay);
+  sc.beta1 = cfg->beta1;
+  sc.beta2 = cfg->beta2;
+  sc.step_size = static_cast<float>(lr / (1.0 - std::pow(b1, cfg->step)));
+  sc.inv_sqrt_bc2 = static_cast<float>(1.0 / std::sqrt(1.0 - std::pow(b2, cfg->step)));
+  sc.eps = cfg->eps;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  AdamBatch b;
+  std::memset(&b, 0, sizeof b);
+  for (int32_t i = 0; i < n; ++i) {
+    const dmuon_tensor &t = tensors[i];
+    const int k = b.n;
+    b.param[k] = t.param;
+    b.grad[k] = t.grad;
+    b.m[k] = t.exp_avg;
+    b.v[k] = t.exp_avg_sq;
+    b.numel[k] = t.numel;
+    b.param_dt[k] = t.param_dtype;
+    b.grad_dt[k] = t.grad_dtype;
+    b.first_block[k + 1] = b.first_block[k] + (t.numel + kEwChunk - 1) / kEwChunk;
+    b.n = k + 1;
+    if (b.n == kAdamBatch || i + 1 == n) {
+      if (b.first_block[b.n] > 0x7fffffff) return fail(DMUON_ERR_INVALID_ARG, "AdamW batch too large");
+      rc = check_launch(launch_adamw_batch(b, sc, s), "adamw launch");
+      if (rc) return rc;
+      std::memset(&b, 0, sizeof b);
+    }
+  }
+  return DMUON_OK;
+}
+
 // ------------------------------------------------------------ pack/unpack --
 static int pack_common(const dmuon_matrix *mats, int32_t n, int32_t field, void *packed_rw,
                        const void *packed, int32_t packed_dtype, int64_t packed_numel,

@@ -107,6 +107,29 @@ struct PackBatch {
 constexpr int64_t kPackBlockBytes = 64 * 1024;
 hipError_t launch_pack_batch(const PackBatch &b, hipStream_t st);
 
+// AdamW: batches of up to kAdamBatch tensors per launch, by value.
+constexpr int kAdamBatch = 32;
+struct AdamBatch {
+  int32_t n;
+  int32_t pad_;
+  int64_t first_block[kAdamBatch + 1];  // prefix sum of kEwChunk blocks
+  void *param[kAdamBatch];
+  const void *grad[kAdamBatch];
+  float *m[kAdamBatch];
+  float *v[kAdamBatch];
+  int64_t numel[kAdamBatch];
+  int32_t param_dt[kAdamBatch];
+  int32_t grad_dt[kAdamBatch];
+};
+struct AdamScalars {
+  float decay;          // 1 - lr * wd
+  float beta1, beta2;
+  float step_size;      // lr / (1 - beta1^t)
+  float inv_sqrt_bc2;   // 1 / sqrt(1 - beta2^t)
+  float eps;
+};
+hipError_t launch_adamw_batch(const AdamBatch &b, AdamScalars s, hipStream_t st);
+
 // ---- launchers (gemm.hip) ----
 // first: the first iteration, whose X holds U unnormalised: Gram scales by
 // inv_norm^2 and Apply / Final by inv_norm.

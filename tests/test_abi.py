@@ -219,3 +219,44 @@ def test_pack_errors(lib):
     arr = (_lib.Matrix * 1)(m)                            # packed over the source param
     assert lib.dmuon_pack(arr, 1, 0, m.param, _lib.BF16, 64, None) == _lib.ERR_ALIAS
     assert lib.dmuon_pack(arr, 0, 0, packed, _lib.BF16, 0, None) == _lib.OK
+
+
+# ------------------------------------------------ AdamW validation, no GPU ---
+
+def tensor(i=0, numel=100, pdt=_lib.BF16, gdt=_lib.BF16):
+    stride = 1 << 24
+    b = FAKE + (i + 16) * 4 * stride
+    return _lib.Tensor(b, pdt, gdt, b + stride, b + 2 * stride, b + 3 * stride, numel)
+
+
+def adam(lib, ts, **kw):
+    c = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=1)
+    c.update(kw)
+    cfg = _lib.AdamWConfig(c["lr"], c["beta1"], c["beta2"], c["eps"], c["weight_decay"], c["step"])
+    arr = (_lib.Tensor * max(len(ts), 1))(*ts)
+    return lib.dmuon_adamw_step(arr, len(ts), ctypes.byref(cfg), None)
+
+
+def test_adamw_struct_layout():
+    assert ctypes.sizeof(_lib.Tensor) == 48
+    assert ctypes.sizeof(_lib.AdamWConfig) == 24
+
+
+def test_adamw_errors(lib):
+    assert adam(lib, []) == _lib.OK
+    for bad in (dict(step=0), dict(beta1=1.0), dict(beta2=-0.1), dict(eps=0.0),
+                dict(lr=float("nan")), dict(weight_decay=float("inf"))):
+        assert adam(lib, [tensor()], **bad) == _lib.ERR_INVALID_ARG, bad
+    t = tensor(); t.numel = 0
+    assert adam(lib, [t]) == _lib.ERR_INVALID_ARG
+    t = tensor(); t.param_dtype = 3
+    assert adam(lib, [t]) == _lib.ERR_UNSUPPORTED_DTYPE
+    t = tensor(); t.exp_avg = None
+    assert adam(lib, [t]) == _lib.ERR_INVALID_ARG
+    t = tensor(); t.exp_avg_sq = t.exp_avg_sq + 4
+    assert adam(lib, [t]) == _lib.ERR_MISALIGNED
+    t = tensor(); t.exp_avg_sq = t.exp_avg
+    assert adam(lib, [t]) == _lib.ERR_ALIAS
+    a, b = tensor(0), tensor(1)
+    b.param = a.grad
+    assert adam(lib, [a, b]) == _lib.ERR_ALIAS
