@@ -75,6 +75,36 @@ def measured_traffic(workload_name: str, fp32: bool):
     return rec["traffic_bytes_per_launch"]
 
 
+def adamw_measure(nsd, torch, dev, stream, steps: int):
+    """AdamW on one rank's 1/8 shard of Llama-3.1-8B's non-Muon parameters
+    (embeddings, lm_head, norms), bf16 params and grads, fp32 moments."""
+    from synth import LLAMA31_8B, LLAMA31_8B_VOCAB, non_muon_sizes
+    sizes = [(n, (c + 7) // 8) for n, c in
+             non_muon_sizes(LLAMA31_8B["d_model"], LLAMA31_8B["n_layers"], LLAMA31_8B_VOCAB)]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(99)
+    P = [(torch.randn(c, generator=gen, device=dev) * 0.02).to(torch.bfloat16) for _, c in sizes]
+    G = [(torch.randn(c, generator=gen, device=dev) * 1e-3).to(torch.bfloat16) for _, c in sizes]
+    M = [torch.zeros(c, dtype=torch.float32, device=dev) for _, c in sizes]
+    V = [torch.zeros(c, dtype=torch.float32, device=dev) for _, c in sizes]
+    opts = nsd.AdamWOptions()
+    for t in range(1, 3):
+        nsd.adamw_step(P, G, M, V, t, opts, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for t in range(3, 3 + steps):
+        nsd.adamw_step(P, G, M, V, t, opts, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    elems = sum(c for _, c in sizes)
+    nbytes = elems * (2 + 2 + 4 + 4 + 2 + 4 + 4)   # P, G, M, V read; P, M, V written
+    return {"tensors": [n for n, _ in sizes], "elements": elems, "ms": round(ms, 4),
+            "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes_per_elem": 22,
+            "peak_gbs": PEAK_HBM_GBS}
+
+
 def owner_share(w, nsd):
     shapes = w.shapes
     if w.n_owners > 1:
@@ -292,6 +322,8 @@ def main(argv=None) -> int:
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if w.wid == 4 and not args.shape:
+        out["adamw"] = adamw_measure(nsd, torch, dev, stream, args.steps)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, shapes, K, args.cpu_budget)
     print(json.dumps(out), flush=True)

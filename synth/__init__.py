@@ -54,6 +54,20 @@ LLAMA31_8B = dict(d_model=4096, kv_dim=1024, d_ff=14336, n_layers=32)
 QWEN25_7B = dict(d_model=3584, kv_dim=512, d_ff=18944, n_layers=28)
 
 
+def non_muon_sizes(d_model: int, n_layers: int, vocab: int, tied: bool = False):
+    """Element counts of a decoder's parameters the Muon predicate leaves out:
+    token embedding, output head (unless tied), and the RMSNorm weights (two
+    per layer plus the final one)."""
+    sizes = [("embed_tokens", vocab * d_model)]
+    if not tied:
+        sizes.append(("lm_head", vocab * d_model))
+    sizes.append(("norms", (2 * n_layers + 1) * d_model))
+    return sizes
+
+
+LLAMA31_8B_VOCAB = 128256   # public Llama-3.1-8B configuration
+
+
 @dataclass
 class Workload:
     """A named set of matrices with its value distributions."""
