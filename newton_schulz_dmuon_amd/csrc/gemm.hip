@@ -388,65 +388,60 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
     const T *Xsrc = static_cast<const T *>(swap ? d.x[cur] : d.xt[cur]);
     const int64_t xld = swap ? d.np : d.mp;
     const bool vec_ok = (d.cols & 3) == 0;  // rows of P start 4-element aligned
-    const bool pbf = d.param_dt == kBF16;
-    constexpr int kRows = sizeof(T) == 2 ? 2 : 1;  // fragment rows per read batch
+    // PT: the parameter's storage type.  Reads of a batch go first (X, and P
+    // on the vector path); four fragment rows per batch when both are bf16.
+    auto update = [&](auto ptag) {
+      using PT = decltype(ptag);
+      constexpr int kRows = sizeof(T) == 2 ? (sizeof(PT) == 2 ? 4 : 2) : 1;
+      PT *const P = static_cast<PT *>(d.param);
+      PT *const Orth = static_cast<PT *>(d.orth);
 #pragma unroll
-    for (int i0 = 0; i0 < kFragM; i0 += kRows) {
-      // reads of the batch first (X and, on the vector path, P)
-      typename Vec4<T>::Raw xraw[kRows][kFragN];
-      u32x4 praw[kRows][kFragN];
+      for (int i0 = 0; i0 < kFragM; i0 += kRows) {
+        typename Vec4<T>::Raw xraw[kRows][kFragN];
+        typename Vec4<PT>::Raw praw[kRows][kFragN];
 #pragma unroll
-      for (int ii = 0; ii < kRows; ++ii)
+        for (int ii = 0; ii < kRows; ++ii)
 #pragma unroll
-        for (int j = 0; j < kFragN; ++j) {
-          const int64_t q = col_base + j * 16, p = row_base + (i0 + ii) * 16;
-          xraw[ii][j] = Vec4<T>::raw(Xsrc + q * xld + p);  // in the padded buffer
-          if (vec_ok && p + 4 <= p_lim && q < q_lim) {
+          for (int j = 0; j < kFragN; ++j) {
+            const int64_t q = col_base + j * 16, p = row_base + (i0 + ii) * 16;
+            xraw[ii][j] = Vec4<T>::raw(Xsrc + q * xld + p);  // in the padded buffer
+            if (vec_ok && p + 4 <= p_lim && q < q_lim) praw[ii][j] = Vec4<PT>::raw(P + q * d.cols + p);
+          }
+#pragma unroll
+        for (int ii = 0; ii < kRows; ++ii)
+#pragma unroll
+          for (int j = 0; j < kFragN; ++j) {
+            const int i = i0 + ii;
+            const int64_t q = col_base + j * 16, p = row_base + i * 16;
+            if (p >= p_lim || q >= q_lim) continue;
+            const f32x4 xv = Vec4<T>::cvt(xraw[ii][j]);
+            f32x4 o;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) o[v] = fmaf(s.a, xv[v], acc[i][j][v]) * inv;
             const int64_t pidx = q * d.cols + p;
-            if (pbf) {
-              const u32x2 v = *(const g_u32x2 *)(static_cast<const uint16_t *>(d.param) + pidx);
-              praw[ii][j] = u32x4{v.x, v.y, 0u, 0u};
+            if (vec_ok && p + 4 <= p_lim) {
+              const f32x4 pv = Vec4<PT>::cvt(praw[ii][j]);
+              f32x4 nv;
+#pragma unroll
+              for (int v = 0; v < 4; ++v) nv[v] = fmaf(-step, o[v], pv[v]);
+              Vec4<PT>::st(P + pidx, nv);
+              if (Orth) Vec4<PT>::st(Orth + pidx, o);
             } else {
-              praw[ii][j] = *(const g_u32x4 *)(static_cast<const float *>(d.param) + pidx);
+#pragma unroll
+              for (int v = 0; v < 4; ++v) {
+                if (p + v >= p_lim) break;
+                if (Orth) store_elem(d.orth, d.param_dt, pidx + v, o[v]);
+                store_elem(d.param, d.param_dt, pidx + v,
+                           fmaf(-step, o[v], load_elem(d.param, d.param_dt, pidx + v)));
+              }
             }
           }
-        }
-#pragma unroll
-      for (int ii = 0; ii < kRows; ++ii)
-#pragma unroll
-        for (int j = 0; j < kFragN; ++j) {
-          const int i = i0 + ii;
-          const int64_t q = col_base + j * 16, p = row_base + i * 16;
-          if (p >= p_lim || q >= q_lim) continue;
-          const f32x4 xv = Vec4<T>::cvt(xraw[ii][j]);
-          f32x4 o;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) o[v] = fmaf(s.a, xv[v], acc[i][j][v]) * inv;
-          const int64_t pidx = q * d.cols + p;
-          if (vec_ok && p + 4 <= p_lim) {
-            const u32x4 pr = praw[ii][j];
-            const f32x4 pv = pbf ? Vec4<uint16_t>::cvt(u32x2{pr.x, pr.y}) : Vec4<float>::cvt(pr);
-            f32x4 nv;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) nv[v] = fmaf(-step, o[v], pv[v]);
-            if (pbf) {
-              Vec4<uint16_t>::st(static_cast<uint16_t *>(d.param) + pidx, nv);
-              if (d.orth) Vec4<uint16_t>::st(static_cast<uint16_t *>(d.orth) + pidx, o);
-            } else {
-              Vec4<float>::st(static_cast<float *>(d.param) + pidx, nv);
-              if (d.orth) Vec4<float>::st(static_cast<float *>(d.orth) + pidx, o);
-            }
-          } else {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              if (p + v >= p_lim) break;
-              if (d.orth) store_elem(d.orth, d.param_dt, pidx + v, o[v]);
-              store_elem(d.param, d.param_dt, pidx + v,
-                         fmaf(-step, o[v], load_elem(d.param, d.param_dt, pidx + v)));
-            }
-          }
-        }
-    }
+      }
+    };
+    if (d.param_dt == kBF16)
+      update(uint16_t{});
+    else
+      update(float{});
   }
 }
 
