@@ -15,6 +15,7 @@ namespace dmuon {
 namespace {
 
 constexpr int kEwThreads = 256;
+constexpr int kOrientThreads = 1024;  // one 64 x 64 tile, four elements per thread
 constexpr int kEwPerThread = static_cast<int>(kEwChunk / kEwThreads);  // 32
 static_assert(kEwPerThread % 4 == 0, "4-wide vectors");
 
@@ -45,23 +46,20 @@ __device__ __forceinline__ f32x4 load_grad4(const void *g, int32_t dt, int64_t i
   return r;
 }
 
-// Eight consecutive workspace elements as 16-byte stores (address: a
-// multiple of eight elements).
-template <typename T> struct Vec8;
-template <> struct Vec8<uint16_t> {
-  static __device__ __forceinline__ void st(uint16_t *p, const float (&v)[8]) {
-    uint4 u;
+// Four consecutive workspace elements as one 8-byte (bf16) or 16-byte (fp32)
+// store (address: a multiple of four elements).
+template <typename T> struct Vec4St;
+template <> struct Vec4St<uint16_t> {
+  static __device__ __forceinline__ void st(uint16_t *p, const float (&v)[4]) {
+    uint2 u;
     u.x = f32_to_bf16_bits(v[0]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[1])) << 16);
     u.y = f32_to_bf16_bits(v[2]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[3])) << 16);
-    u.z = f32_to_bf16_bits(v[4]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[5])) << 16);
-    u.w = f32_to_bf16_bits(v[6]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[7])) << 16);
-    *reinterpret_cast<uint4 *>(p) = u;
+    *reinterpret_cast<uint2 *>(p) = u;
   }
 };
-template <> struct Vec8<float> {
-  static __device__ __forceinline__ void st(float *p, const float (&v)[8]) {
-    reinterpret_cast<float4 *>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
-    reinterpret_cast<float4 *>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+template <> struct Vec4St<float> {
+  static __device__ __forceinline__ void st(float *p, const float (&v)[4]) {
+    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
   }
 };
 
@@ -127,11 +125,12 @@ __global__ __launch_bounds__(256) void finalize_norm_kernel(const MatDev *__rest
 // Apply epilogues, so M is read once.  The block is staged through LDS so
 // that both X and X^T leave as 16-byte row segments.
 template <typename T>
-__global__ __launch_bounds__(256) void momentum_orient_kernel(
+__global__ __launch_bounds__(kOrientThreads) void momentum_orient_kernel(
     const MatDev *__restrict__ mats, int32_t nmat, StepScalars s) {
   constexpr int TT = static_cast<int>(kTrTile);
+  static_assert(TT * TT == kOrientThreads * 4, "four elements per thread");
   __shared__ float tile[TT][TT + 1];
-  __shared__ double red[4];
+  __shared__ double red[kOrientThreads / 64];
   const int64_t w = blockIdx.x;
   const int32_t mi = find_range(nmat, w, [&](int32_t i) { return mats[i].tr_first; });
   const MatDev &d = mats[mi];
@@ -142,56 +141,52 @@ __global__ __launch_bounds__(256) void momentum_orient_kernel(
   const float mu = s.mu;
   const int tid = threadIdx.x;
   const bool vec = (d.cols & 3) == 0;  // rows of M start 16-byte aligned
-  double acc = 0.0;
-  // read: 4 consecutive columns of one row per thread and step
-  for (int e = tid; e < TT * TT / 4; e += 256) {
-    const int p = e >> 4, q = (e & 15) * 4;
-    const int64_t ur = ur0 + p, uc = uc0 + q;
-    float u[4] = {0.f, 0.f, 0.f, 0.f};
-    if (ur < d.rows && uc < d.cols) {
-      const int64_t idx = ur * d.cols + uc;
-      if (vec && uc + 4 <= d.cols) {
-        float4 mv = *reinterpret_cast<const float4 *>(d.mom + idx);
-        const f32x4 g = load_grad4(d.grad, d.grad_dt, idx);
-        mv.x = fmaf(mu, mv.x, g[0]);
-        mv.y = fmaf(mu, mv.y, g[1]);
-        mv.z = fmaf(mu, mv.z, g[2]);
-        mv.w = fmaf(mu, mv.w, g[3]);
-        *reinterpret_cast<float4 *>(d.mom + idx) = mv;
-        u[0] = mv.x; u[1] = mv.y; u[2] = mv.z; u[3] = mv.w;
-        if (s.nesterov)
+  // read: 4 consecutive columns of one row per thread
+  const int p = tid >> 4, q = (tid & 15) * 4;
+  const int64_t ur = ur0 + p, uc = uc0 + q;
+  float u[4] = {0.f, 0.f, 0.f, 0.f};
+  if (ur < d.rows && uc < d.cols) {
+    const int64_t idx = ur * d.cols + uc;
+    if (vec && uc + 4 <= d.cols) {
+      float4 mv = *reinterpret_cast<const float4 *>(d.mom + idx);
+      const f32x4 g = load_grad4(d.grad, d.grad_dt, idx);
+      mv.x = fmaf(mu, mv.x, g[0]);
+      mv.y = fmaf(mu, mv.y, g[1]);
+      mv.z = fmaf(mu, mv.z, g[2]);
+      mv.w = fmaf(mu, mv.w, g[3]);
+      *reinterpret_cast<float4 *>(d.mom + idx) = mv;
+      u[0] = mv.x; u[1] = mv.y; u[2] = mv.z; u[3] = mv.w;
+      if (s.nesterov)
 #pragma unroll
-          for (int k = 0; k < 4; ++k) u[k] = fmaf(mu, u[k], g[k]);
-      } else {
-        for (int k = 0; k < 4 && uc + k < d.cols; ++k) {
-          const float g = load_elem(d.grad, d.grad_dt, idx + k);
-          const float m = fmaf(mu, d.mom[idx + k], g);
-          d.mom[idx + k] = m;
-          u[k] = s.nesterov ? fmaf(mu, m, g) : m;
-        }
+        for (int k = 0; k < 4; ++k) u[k] = fmaf(mu, u[k], g[k]);
+    } else {
+      for (int k = 0; k < 4 && uc + k < d.cols; ++k) {
+        const float g = load_elem(d.grad, d.grad_dt, idx + k);
+        const float m = fmaf(mu, d.mom[idx + k], g);
+        d.mom[idx + k] = m;
+        u[k] = s.nesterov ? fmaf(mu, m, g) : m;
       }
     }
+  }
+  double acc = 0.0;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      tile[p][q + k] = u[k];
-      acc += (double)u[k] * u[k];
-    }
+  for (int k = 0; k < 4; ++k) {
+    tile[p][q + k] = u[k];
+    acc += (double)u[k] * u[k];
   }
   __syncthreads();
-  // write: 8 consecutive elements of an X row, then of an X^T row
+  // write: 4 consecutive elements of an X row and of an X^T row per thread
   T *X = static_cast<T *>(d.x[0]);
   T *XT = static_cast<T *>(d.xt[0]);
-  for (int c = tid; c < TT * TT / 8; c += 256) {
-    const int a = c >> 3, b = (c & 7) * 8;
-    float vx[8], vt[8];
+  const int a = tid >> 4, b = (tid & 15) * 4;
+  float vx[4], vt[4];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      vx[k] = d.transposed ? tile[b + k][a] : tile[a][b + k];  // X[i0 + a][j0 + b + k]
-      vt[k] = d.transposed ? tile[a][b + k] : tile[b + k][a];  // X^T[j0 + a][i0 + b + k]
-    }
-    Vec8<T>::st(X + (i0 + a) * d.np + j0 + b, vx);
-    Vec8<T>::st(XT + (j0 + a) * d.mp + i0 + b, vt);
+  for (int k = 0; k < 4; ++k) {
+    vx[k] = d.transposed ? tile[b + k][a] : tile[a][b + k];  // X[i0 + a][j0 + b + k]
+    vt[k] = d.transposed ? tile[a][b + k] : tile[b + k][a];  // X^T[j0 + a][i0 + b + k]
   }
+  Vec4St<T>::st(X + (i0 + a) * d.np + j0 + b, vx);
+  Vec4St<T>::st(XT + (j0 + a) * d.mp + i0 + b, vt);
   const double tot = block_sum_f64(acc, red);
   if (tid == 0) d.partials[t] = tot;
 }
@@ -217,8 +212,8 @@ __global__ __launch_bounds__(kEwThreads) void update_direct_kernel(
   }
 }
 
-// AdamW over a batch of tensors: 32 elements per thread, 4-wide vectors
-// where the tensor's length allows.
+// AdamW over a batch of tensors: one 4-wide vector per thread where the
+// tensor's length allows (short work-groups keep more HBM requests in flight).
 __device__ __forceinline__ void adamw_elem(float &p, float g, float &m, float &v,
                                            const AdamScalars &s) {
   p *= s.decay;
@@ -232,13 +227,14 @@ __global__ __launch_bounds__(kEwThreads) void adamw_kernel(AdamBatch b, AdamScal
   const int64_t w = blockIdx.x;
   const int32_t ti = find_range(b.n, w, [&](int32_t i) { return b.first_block[i]; });
   const int64_t numel = b.numel[ti];
-  const int64_t base = (w - b.first_block[ti]) * kEwChunk;
+  const int64_t base = (w - b.first_block[ti]) * kAdamChunk;
   float *M = b.m[ti], *V = b.v[ti];
   void *P = b.param[ti];
   const void *G = b.grad[ti];
   const int32_t pdt = b.param_dt[ti], gdt = b.grad_dt[ti];
+  static_assert(kAdamChunk % (4 * kEwThreads) == 0, "whole vectors per thread");
 #pragma unroll
-  for (int k = 0; k < kEwPerThread / 4; ++k) {
+  for (int k = 0; k < static_cast<int>(kAdamChunk / (4 * kEwThreads)); ++k) {
     const int64_t i = base + (static_cast<int64_t>(k) * kEwThreads + threadIdx.x) * 4;
     if (i + 4 <= numel) {
       float4 mv = *reinterpret_cast<const float4 *>(M + i);
@@ -305,10 +301,10 @@ hipError_t launch_finalize_norm(const MatDev *mats, int32_t nmat, float eps, hip
 hipError_t launch_momentum_orient(const MatDev *mats, int32_t nmat, int64_t total_tiles,
                                   StepScalars s, bool fp32, hipStream_t st) {
   if (fp32)
-    hipLaunchKernelGGL(momentum_orient_kernel<float>, dim3((uint32_t)total_tiles), dim3(256), 0,
+    hipLaunchKernelGGL(momentum_orient_kernel<float>, dim3((uint32_t)total_tiles), dim3(kOrientThreads), 0,
                        st, mats, nmat, s);
   else
-    hipLaunchKernelGGL(momentum_orient_kernel<uint16_t>, dim3((uint32_t)total_tiles), dim3(256),
+    hipLaunchKernelGGL(momentum_orient_kernel<uint16_t>, dim3((uint32_t)total_tiles), dim3(kOrientThreads),
                        0, st, mats, nmat, s);
   return hipGetLastError();
 }

@@ -588,7 +588,7 @@ int dmuon_adamw_step(const dmuon_tensor *tensors, int32_t n, const dmuon_adamw_c
     b.numel[k] = t.numel;
     b.param_dt[k] = t.param_dtype;
     b.grad_dt[k] = t.grad_dtype;
-    b.first_block[k + 1] = b.first_block[k] + (t.numel + kEwChunk - 1) / kEwChunk;
+    b.first_block[k + 1] = b.first_block[k] + (t.numel + kAdamChunk - 1) / kAdamChunk;
     b.n = k + 1;
     if (b.n == kAdamBatch || i + 1 == n) {
       if (b.first_block[b.n] > 0x7fffffff) return fail(DMUON_ERR_INVALID_ARG, "AdamW batch too large");

@@ -104,15 +104,16 @@ struct PackBatch {
   void *dst[kPackBatch];
   int64_t bytes[kPackBatch];
 };
-constexpr int64_t kPackBlockBytes = 64 * 1024;
+constexpr int64_t kPackBlockBytes = 4 * 1024;  // one 16-byte vector per thread
 hipError_t launch_pack_batch(const PackBatch &b, hipStream_t st);
 
 // AdamW: batches of up to kAdamBatch tensors per launch, by value.
 constexpr int kAdamBatch = 32;
+constexpr int64_t kAdamChunk = 1024;  // elements per work-group: four per thread
 struct AdamBatch {
   int32_t n;
   int32_t pad_;
-  int64_t first_block[kAdamBatch + 1];  // prefix sum of kEwChunk blocks
+  int64_t first_block[kAdamBatch + 1];  // prefix sum of kAdamChunk blocks
   void *param[kAdamBatch];
   const void *grad[kAdamBatch];
   float *m[kAdamBatch];
