@@ -68,6 +68,12 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Synchronises the work-group once this wave's LDS reads are complete (its
+// global stores may still be in flight).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 template <typename T> struct Mfma;
 template <> struct Mfma<uint16_t> {
   // one 16-byte chunk per lane = 8 bf16 along k = one 16x16x32 MFMA
@@ -123,12 +129,20 @@ template <> struct Vec4<float> {
   }
 };
 
-// Row-major 256 x 256 bf16 tile in LDS (512-byte rows, 32 chunks of 16 B).
-// The chunk index is XOR-swizzled with bits 2-3 of the row (moved to chunk
-// bits 1-2): the 64 lanes of one put touch 4 rows x 2 chunks, all in
-// distinct bank groups, and a 16-lane read of one row stays a permutation.
+// Row-major 256 x 256 bf16 tile in LDS (512-byte rows, 32 chunks of 16 B),
+// two chunk swizzles, one per way the tile is filled:
+//  kSwzRows: stage_tile_put writes four rows of one column (2-byte stores);
+//    the chunk is XORed with bits 2-3 of the row (moved to chunk bits 1-2),
+//    so the 64 lanes of one put touch 4 rows x 2 chunks in distinct banks.
+//  kSwzCols: stage_tile_put_t writes four consecutive elements of a row
+//    (one 8-byte store); a put touches 16 consecutive rows x 32 bytes, and
+//    the chunk is XORed with (row mod 8) * 2, which keeps the chunk pair of
+//    a row together and spreads 8 rows over 256 bytes of banks.
+// A flush reads whole rows, so either swizzle is a permutation within a row.
+constexpr int kSwzRows = 0, kSwzCols = 1;
+template <int SW>
 __device__ __forceinline__ int tile_swz(int row, int chunk) {
-  return chunk ^ (((row >> 2) & 3) << 1);
+  return SW == kSwzRows ? chunk ^ (((row >> 2) & 3) << 1) : chunk ^ ((row & 7) << 1);
 }
 
 // Puts rows r0 .. r0+3 of column c (one lane's four values) as bf16.
@@ -137,20 +151,33 @@ __device__ __forceinline__ void stage_tile_put(lds_char *lds, int r0, int c, con
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int row = r0 + k;
-    const int off = row * 512 + tile_swz(row, c >> 3) * 16 + (c & 7) * 2;
+    const int off = row * 512 + tile_swz<kSwzRows>(row, c >> 3) * 16 + (c & 7) * 2;
     *(lds_u16 *)(lds + off) = f32_to_bf16_bits(v[k]);
   }
 }
 
+// Puts elements c0 .. c0+3 of row r (c0 a multiple of four) as bf16: the
+// transposed placement of a lane's four values.
+__device__ __forceinline__ void stage_tile_put_t(lds_char *lds, int r, int c0, const f32x4 &v) {
+  typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+  u32x2 u;
+  u.x = static_cast<uint32_t>(f32_to_bf16_bits(v[0])) | (static_cast<uint32_t>(f32_to_bf16_bits(v[1])) << 16);
+  u.y = static_cast<uint32_t>(f32_to_bf16_bits(v[2])) | (static_cast<uint32_t>(f32_to_bf16_bits(v[3])) << 16);
+  *(lds_u32x2 *)(lds + r * 512 + tile_swz<kSwzCols>(r, c0 >> 3) * 16 + (c0 & 7) * 2) = u;
+}
+
 // Writes the staged tile to dst (row-major, leading dimension ld elements)
 // with 16-byte stores: thread t moves chunks t, t + 512, ... (row = f / 32).
+// Starts with a barrier (the puts are visible); a later put into the same
+// LDS needs stage_barrier() first.
+template <int SW>
 __device__ __forceinline__ void stage_tile_flush(lds_char *lds, uint16_t *dst, int64_t ld, int tid) {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int f = q * 512 + tid;
     const int row = f >> 5, chunk = f & 31;
-    const u32x4 v = *(const lds_u32x4 *)(lds + row * 512 + tile_swz(row, chunk) * 16);
+    const u32x4 v = *(const lds_u32x4 *)(lds + row * 512 + tile_swz<SW>(row, chunk) * 16);
     *reinterpret_cast<u32x4 *>(dst + row * ld + chunk * 8) = v;
   }
 }
@@ -333,17 +360,31 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
 #pragma unroll
           for (int v = 0; v < 4; ++v) val[v] = fmaf(s.b, av[v], s.c * val[v]);
         }
-        if constexpr (kStage)
+        if constexpr (kStage) {
           stage_tile_put(lds, wm * kWaveM + i * 16 + 4 * g4, wn * kWaveN + j * 16 + r16, val);
-        else
+          acc[i][j] = val;  // kept for the mirror tile
+        } else {
 #pragma unroll
           for (int v = 0; v < 4; ++v) WsType<T>::st(out, (row + v) * mp + col, val[v]);
-        if (ti != tj) Vec4<T>::st(out + col * mp + row, val);
+          if (ti != tj) Vec4<T>::st(out + col * mp + row, val);
+        }
       }
     }
-    if constexpr (kStage)
-      stage_tile_flush(lds, reinterpret_cast<uint16_t *>(out) + static_cast<int64_t>(ti) * kTile * mp +
-                                static_cast<int64_t>(tj) * kTile, mp, tid);
+    if constexpr (kStage) {
+      uint16_t *const o16 = reinterpret_cast<uint16_t *>(out);
+      stage_tile_flush<kSwzRows>(lds, o16 + static_cast<int64_t>(ti) * kTile * mp + static_cast<int64_t>(tj) * kTile,
+                                 mp, tid);
+      if (ti != tj) {  // the mirror tile (tj, ti), staged the transposed way
+        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < kFragM; ++i)
+#pragma unroll
+          for (int j = 0; j < kFragN; ++j)
+            stage_tile_put_t(lds, wn * kWaveN + j * 16 + r16, wm * kWaveM + i * 16 + 4 * g4, acc[i][j]);
+        stage_tile_flush<kSwzCols>(lds, o16 + static_cast<int64_t>(tj) * kTile * mp + static_cast<int64_t>(ti) * kTile,
+                                   mp, tid);
+      }
+    }
   } else if (MODE == kModeApply) {
     const T *XT = static_cast<const T *>(d.xt[cur]);
     T *Xn = static_cast<T *>(d.x[cur ^ 1]);
@@ -367,17 +408,29 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
         f32x4 val;
 #pragma unroll
         for (int v = 0; v < 4; ++v) val[v] = fmaf(s.a, xv[v], acc[i][j][v]) * inv;
-        Vec4<T>::st(XTn + col * mp + row, val);
-        if constexpr (kStage)
+        if constexpr (kStage) {
           stage_tile_put(lds, wm * kWaveM + i * 16 + 4 * g4, wn * kWaveN + j * 16 + r16, val);
-        else
+          acc[i][j] = val;  // kept for the X'^T tile
+        } else {
+          Vec4<T>::st(XTn + col * mp + row, val);
 #pragma unroll
           for (int v = 0; v < 4; ++v) WsType<T>::st(Xn, (row + v) * np + col, val[v]);
+        }
       }
     }
-    if constexpr (kStage)
-      stage_tile_flush(lds, reinterpret_cast<uint16_t *>(Xn) + static_cast<int64_t>(ti) * kTile * np +
-                                static_cast<int64_t>(tj) * kTile, np, tid);
+    if constexpr (kStage) {
+      // X' tile (ti, tj), then X'^T tile (tj, ti) through the same LDS
+      stage_tile_flush<kSwzRows>(lds, reinterpret_cast<uint16_t *>(Xn) + static_cast<int64_t>(ti) * kTile * np +
+                                          static_cast<int64_t>(tj) * kTile, np, tid);
+      lds_barrier();
+#pragma unroll
+      for (int i = 0; i < kFragM; ++i)
+#pragma unroll
+        for (int j = 0; j < kFragN; ++j)
+          stage_tile_put_t(lds, wn * kWaveN + j * 16 + r16, wm * kWaveM + i * 16 + 4 * g4, acc[i][j]);
+      stage_tile_flush<kSwzCols>(lds, reinterpret_cast<uint16_t *>(XTn) + static_cast<int64_t>(tj) * kTile * mp +
+                                          static_cast<int64_t>(ti) * kTile, mp, tid);
+    }
   } else {  // kModeFinal
     const float step = s.lr * d.scale;
     // (p, q): lane's four values are C[p + v][q] of the computed product.
