@@ -291,10 +291,53 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   // step k+1 are issued unconditionally (the last step re-loads its own K
   // range into the free stage), so each iteration is one basic block the
   // compiler can interleave.  nkt >= 4 because operands are padded to 256.
+  // The aX term of Apply comes from the R operand, X^T: its rows are the tile's columns and its K range
+  // [ti*256, ti*256 + 256) holds the tile's rows.  While the K steps of the
+  // wave's 128 rows are in LDS, each lane reads its four values (four
+  // consecutive k of one R row) and adds a*X to the accumulators.
+  constexpr int kKStep = kRowBytes / static_cast<int>(sizeof(T));  // K elements per step
+  constexpr int kCapSteps = kWaveM / kKStep;                         // steps holding the wave's rows
+  constexpr int kCapFrags = kKStep / 16;                             // fragment rows per step
+  constexpr bool cap_ax = MODE == kModeApply;
+  const int cap_kt0 = ti * (kTile / kKStep) + wm * kCapSteps;
+  // Step c of the wave's kCapSteps holds fragment rows [c*kCapFrags,
+  // (c+1)*kCapFrags).  Every fragment row reads and adds at every capture
+  // step, with weight a on its own step and 0 on the others (at an address
+  // of the same step), so no accumulator is indexed by a run-time value.
+  auto capture_ax = [&](const lds_char *st, int kt) {
+    if constexpr (!cap_ax) return;
+    const int c = kt - cap_kt0;  // uniform in the wave
+    if (c < 0 || c >= kCapSteps) return;
+#pragma unroll
+    for (int i = 0; i < kFragM; ++i) {
+      const float w = (i / kCapFrags == c) ? s.a : 0.f;
+      const int kb = ((i % kCapFrags) * 16 + 4 * g4) * static_cast<int>(sizeof(T));  // byte offset in the R row
+#pragma unroll
+      for (int j = 0; j < kFragN; ++j) {
+        const int row = wn * kWaveN + j * 16 + r16;
+        const lds_char *pr = st + kOperandBytes + row * kRowBytes + swz(kb >> 4, row) * 16 + (kb & 15);
+        f32x4 xv;
+        if constexpr (sizeof(T) == 2) {
+          typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+          const u32x2 raw = *(const lds_u32x2 *)pr;
+          xv = Vec4<uint16_t>::cvt(raw);
+        } else {
+          const u32x4 raw = *(const lds_u32x4 *)pr;
+          xv = Vec4<float>::cvt(raw);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[i][j][v] = fmaf(w, xv[v], acc[i][j][v]);
+      }
+      // one fragment row per group: at most 8 VGPRs of reads in flight
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
   Frag fa, fb;
   issue(0);
   stage_barrier();
   issue(1);
+  capture_ax(lds, 0);
   read_frag(lds, 0, fa);
   read_frag(lds, 1, fb);
   mfma_frag(fa);
@@ -302,6 +345,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
     stage_barrier();  // step kt is in LDS; step kt-1's stage is free
     const lds_char *st = lds + (kt & 1) * kStageBytes;
     issue(min(kt + 1, nkt - 1));
+    capture_ax(st, kt);
     read_frag(st, 0, fa);
     mfma_frag(fb);    // sub-step 1 of step kt-1
     read_frag(st, 1, fb);
@@ -386,28 +430,17 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
       }
     }
   } else if (MODE == kModeApply) {
-    const T *XT = static_cast<const T *>(d.xt[cur]);
     T *Xn = static_cast<T *>(d.x[cur ^ 1]);
     T *XTn = static_cast<T *>(d.xt[cur ^ 1]);
     const int64_t np = d.np, mp = d.mp;
 #pragma unroll
-    for (int i0 = 0; i0 < kFragM; i0 += kReadRows) {
-    typename Vec4<T>::Raw xraw[kReadRows][kFragN];  // X[row + v][col], reads first
-#pragma unroll
-    for (int ii = 0; ii < kReadRows; ++ii)
-#pragma unroll
-      for (int j = 0; j < kFragN; ++j)
-        xraw[ii][j] = Vec4<T>::raw(XT + (col_base + j * 16) * mp + row_base + (i0 + ii) * 16);
-#pragma unroll
-    for (int ii = 0; ii < kReadRows; ++ii)
+    for (int i = 0; i < kFragM; ++i)
 #pragma unroll
       for (int j = 0; j < kFragN; ++j) {
-        const int i = i0 + ii;
         const int64_t col = col_base + j * 16, row = row_base + i * 16;
-        const f32x4 xv = Vec4<T>::cvt(xraw[ii][j]);
-        f32x4 val;
+        f32x4 val;  // a*X is already in the accumulator
 #pragma unroll
-        for (int v = 0; v < 4; ++v) val[v] = fmaf(s.a, xv[v], acc[i][j][v]) * inv;
+        for (int v = 0; v < 4; ++v) val[v] = acc[i][j][v] * inv;
         if constexpr (kStage) {
           stage_tile_put(lds, wm * kWaveM + i * 16 + 4 * g4, wn * kWaveN + j * 16 + r16, val);
           acc[i][j] = val;  // kept for the X'^T tile
@@ -417,7 +450,6 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
           for (int v = 0; v < 4; ++v) WsType<T>::st(Xn, (row + v) * np + col, val[v]);
         }
       }
-    }
     if constexpr (kStage) {
       // X' tile (ti, tj), then X'^T tile (tj, ti) through the same LDS
       stage_tile_flush<kSwzRows>(lds, reinterpret_cast<uint16_t *>(Xn) + static_cast<int64_t>(ti) * kTile * np +
