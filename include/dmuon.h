@@ -167,7 +167,7 @@ int dmuon_unpack(const dmuon_matrix *mats, int32_t n, int32_t field,
  *   workspace  device scratch of at least dmuon_workspace_bytes(); its
  *              contents on entry do not matter and are undefined on exit.
  * Writes: every param, momentum and (non-null) orth_out.  Reads: grads.
- * Errors: INVALID_ARG (null pointer, rows/cols < 1, ns_steps out of range,
+ * Errors: INVALID_ARG (null pointer, rows/cols < 1 or > 2^22, ns_steps out of range,
  * non-finite lr/momentum/scale, eps < 0, unknown flag, reserved != 0),
  * UNSUPPORTED_DTYPE, MISALIGNED, ALIAS (a written buffer overlaps any other
  * buffer of the call, the workspace included), WORKSPACE_TOO_SMALL, HIP. */

@@ -1,5 +1,5 @@
 // Memory-bound stages of the owner's Muon step on gfx950: momentum + sum of
-// squares fused with the cast to the wide orientation (X and X^T), the norm,
+// squares fused with the cast to the wide orientation (stored as X^T), the norm,
 // the direct update (ns_steps = 0, with a flat momentum pass) and the
 // packed-buffer copies.
 //
@@ -120,10 +120,10 @@ __global__ __launch_bounds__(256) void finalize_norm_kernel(const MatDev *__rest
 // padded X (m_p x n_p) per work-group:
 //   M <- mu*M + G on the caller block that maps onto the tile,
 //   U = M (or G + mu*M), its sum of squares into partials[tile],
-//   U written unnormalised as X (row-major) and X^T, zero in the padding.
+//   U written unnormalised as X^T (n_p x m_p), zero in the padding.
 // The 1/(||U||_F + eps) scale is applied by the first iteration's Gram and
 // Apply epilogues, so M is read once.  The block is staged through LDS so
-// that both X and X^T leave as 16-byte row segments.
+// that X^T leaves in row segments whichever way the caller's matrix lies.
 template <typename T>
 __global__ __launch_bounds__(kOrientThreads) void momentum_orient_kernel(
     const MatDev *__restrict__ mats, int32_t nmat, StepScalars s) {
@@ -175,17 +175,12 @@ __global__ __launch_bounds__(kOrientThreads) void momentum_orient_kernel(
     acc += (double)u[k] * u[k];
   }
   __syncthreads();
-  // write: 4 consecutive elements of an X row and of an X^T row per thread
-  T *X = static_cast<T *>(d.x[0]);
+  // write: 4 consecutive elements of an X^T row per thread
   T *XT = static_cast<T *>(d.xt[0]);
   const int a = tid >> 4, b = (tid & 15) * 4;
-  float vx[4], vt[4];
+  float vt[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    vx[k] = d.transposed ? tile[b + k][a] : tile[a][b + k];  // X[i0 + a][j0 + b + k]
-    vt[k] = d.transposed ? tile[a][b + k] : tile[b + k][a];  // X^T[j0 + a][i0 + b + k]
-  }
-  Vec4St<T>::st(X + (i0 + a) * d.np + j0 + b, vx);
+  for (int k = 0; k < 4; ++k) vt[k] = d.transposed ? tile[a][b + k] : tile[b + k][a];  // X^T[j0 + a][i0 + b + k]
   Vec4St<T>::st(XT + (j0 + a) * d.mp + i0 + b, vt);
   const double tot = block_sum_f64(acc, red);
   if (tid == 0) d.partials[t] = tot;

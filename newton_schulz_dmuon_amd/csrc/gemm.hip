@@ -1,23 +1,25 @@
 // Newton-Schulz stages of the owner's Muon step on gfx950 matrix cores.
 //
 // One iteration X <- a X + (b A + c A^2) X, A = X X^T, is three products,
-// each a grouped launch over every matrix of the step:
+// each a grouped launch over every matrix of the step.  The iterate is kept
+// only as X^T (n_p x m_p, row-major):
 //
 //   Gram    A = X X^T        upper-triangle 256x256 tiles only, each tile also
-//                            written mirrored (A is symmetric)
+//                            written mirrored (A is symmetric); both operands
+//                            are column blocks of X^T (MN-major tiles)
 //   Square  B = b A + c A A  A A = A A^T is again a Gram product of a
 //                            symmetric matrix: upper tiles + mirror, with
 //                            b A + c (.) applied in the epilogue
-//   Apply   X' = a X + B X   full tiles; the a X term is added in the
-//                            epilogue; X' is written twice, row-major and
-//                            transposed, because the next Gram reads X' by
-//                            rows and the next Apply reads it by columns
+//   Apply   X' = a X + B X   full tiles, R operand = X^T (K-contiguous); the
+//                            a X term is read from the R tile in LDS during the
+//                            mainloop; X'^T is written
 //   Final   the last Apply: P -= lr*scale*X' in the caller's orientation,
 //           and X' to orth_out; no workspace write
 //
-// Every product is C[i][j] = sum_k L[i][k] R[j][k] with both operands stored
-// k-contiguous (row-major L, row-major R), which is the operand layout the
-// MFMA instructions read.  Operands are bf16 (v_mfma_f32_16x16x32_bf16) or
+// Every product is C[i][j] = sum_k L[i][k] R[j][k].  Square and Apply read
+// both operands k-contiguous (row-major L and R), the layout the MFMA
+// instructions take; Gram's operands have k down the rows and are turned
+// into that layout by transposing LDS reads.  Operands are bf16 (v_mfma_f32_16x16x32_bf16) or
 // fp32 in the checking mode (v_mfma_f32_16x16x4_f32); accumulation is fp32.
 //
 // Tiling: 256x256 output tile per work-group of 8 waves (2 x 4), each wave
@@ -36,6 +38,8 @@
 //
 // Operands are zero-padded to multiples of 256 in the workspace, so no
 // load or store is masked except the caller-visible writes of Final.
+
+#include <type_traits>
 
 #include "device_common.h"
 
@@ -58,6 +62,7 @@ constexpr int kDmaPerWave = kOperandBytes / 1024 / 8;  // 4 KB-sized DMA instruc
 typedef __attribute__((address_space(3))) char lds_char;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ int swz(int chunk, int row) { return chunk ^ ((row >> 1) & 7); }
 
@@ -66,6 +71,31 @@ __device__ __forceinline__ int swz(int chunk, int row) { return chunk ^ ((row >>
 // from moving LDS accesses across it.
 __device__ __forceinline__ void stage_barrier() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// MN-major operand tiles (Gram reads X^T: K runs down the rows).  An LDS row
+// is one k: 256 elements, 512 bytes (bf16) or 1 KB (fp32); a stage holds
+// kRowBytes / sizeof(T) rows, 32 KB.  The 16-byte chunk of a row is XORed
+// with mn_swz(row), chosen so that the fragment reads below touch distinct
+// banks: bf16 reads 16 rows x 32 bytes (bits 0-1 and 3 of the row pick one
+// of 8 chunk pairs), fp32 reads 4 rows x 64 bytes (bits 2-3 pick the 64-byte
+// group).
+template <typename T>
+__device__ __forceinline__ int mn_swz(int row) {
+  return sizeof(T) == 2 ? ((row & 3) | (((row >> 3) & 1) << 2)) << 1 : ((row >> 2) & 3) << 2;
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane 4e+q gives the
+// address of four consecutive elements Y[k0 + e][n0 + 4q .. n0 + 4q + 3] of
+// a row-major Y; lane j of the group receives Y[k0 .. k0+3][n0 + j], i.e. four
+// consecutive k of one column, the MFMA operand layout.  Issued as inline
+// assembly: the compiler would otherwise wait for every LDS-bound global
+// load before it (it cannot tell them apart), so the caller waits with
+// wait_lds_tied() before using the result.
+__device__ __forceinline__ u32x2 ds_read_tr16(uint32_t lds_addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(lds_addr));
+  return r;
 }
 
 // Synchronises the work-group once this wave's LDS reads are complete (its
@@ -97,7 +127,6 @@ template <> struct Mfma<float> {
 // Accesses go through global (address space 1) pointers, so they count on
 // vmcnt only and never wait on LDS traffic.  raw() / cvt() split a load so
 // that a batch of loads can be issued before the first use.
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(1))) u32x2 g_u32x2;
 typedef __attribute__((address_space(1))) u32x4 g_u32x4;
 template <typename T> struct Vec4;
@@ -199,11 +228,15 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   const MatDev &d = mats[e.mat];
   const int32_t ti = e.ti, tj = e.tj;
 
+  // Gram reads X^T (n_p x m_p): its operand tiles are MN-major, K = n runs
+  // down the rows.  The other stages read K-contiguous rows.
+  constexpr bool kMN = MODE == kModeGram;
+  constexpr int kKStep = kRowBytes / static_cast<int>(sizeof(T));  // K elements per step
   const T *L, *R;
   int64_t ld;  // elements; both operands have the same leading dimension
   if (MODE == kModeGram) {
-    L = R = static_cast<const T *>(d.x[cur]);
-    ld = d.np;
+    L = R = static_cast<const T *>(d.xt[cur]);
+    ld = d.mp;
   } else if (MODE == kModeSquare) {
     L = R = static_cast<const T *>(d.a);
     ld = d.mp;
@@ -213,15 +246,11 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
     ld = d.mp;
   }
   const int64_t ld_bytes = ld * static_cast<int64_t>(sizeof(T));
-  const int nkt = static_cast<int>(ld_bytes / kRowBytes);
-  // The last Apply of a wide matrix (P is m x n, not transposed) computes
-  // the transposed tile, (B X)^T = X^T B: each lane's four consecutive
-  // values then run along a row of P, so the update is a vector access.
-  const bool swap = (MODE == kModeFinal) && !d.transposed;
-  const char *gl = reinterpret_cast<const char *>(swap ? R : L) +
-                   static_cast<int64_t>(swap ? tj : ti) * kTile * ld_bytes;
-  const char *gr = reinterpret_cast<const char *>(swap ? L : R) +
-                   static_cast<int64_t>(swap ? ti : tj) * kTile * ld_bytes;
+  const int nkt = kMN ? static_cast<int>(d.np / kKStep) : static_cast<int>(ld_bytes / kRowBytes);
+  // K-contiguous: the tile's 256 rows; MN-major: the tile's 256 columns
+  const int64_t tile_stride = kMN ? kTile * static_cast<int64_t>(sizeof(T)) : kTile * ld_bytes;
+  const char *gl = reinterpret_cast<const char *>(L) + static_cast<int64_t>(ti) * tile_stride;
+  const char *gr = reinterpret_cast<const char *>(R) + static_cast<int64_t>(tj) * tile_stride;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -231,15 +260,26 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   // filling LDS rows [8b, 8b + 8) of the operand tile, b = j*8 + wave.  Lane
   // l writes LDS byte 16*l of that KB: row 8b + l/8, physical chunk l%8,
   // which holds logical chunk swz(l%8, row) of the row.
-  int64_t goff[kDmaPerWave];
+  // MN-major: the KB of instruction b covers k rows 2b, 2b+1 (bf16, lane l:
+  // row 2b + l/32, physical chunk l%32) or k row b (fp32, chunk l).
+  // Offsets within the operand's row block fit 32 bits: the step accepts
+  // at most 2^22 elements per side, so 256 rows span < 2^32 bytes.
+  uint32_t goff[kDmaPerWave];
 #pragma unroll
   for (int j = 0; j < kDmaPerWave; ++j) {
-    const int row = (j * 8 + wave) * 8 + (lane >> 3);
-    goff[j] = static_cast<int64_t>(row) * ld_bytes + swz(lane & 7, row) * 16;
+    const int b = j * 8 + wave;
+    if constexpr (kMN) {
+      const int row = sizeof(T) == 2 ? 2 * b + (lane >> 5) : b;
+      const int pc = sizeof(T) == 2 ? (lane & 31) : lane;
+      goff[j] = static_cast<uint32_t>(row) * static_cast<uint32_t>(ld_bytes) + (pc ^ mn_swz<T>(row)) * 16;
+    } else {
+      const int row = b * 8 + (lane >> 3);
+      goff[j] = static_cast<uint32_t>(row) * static_cast<uint32_t>(ld_bytes) + swz(lane & 7, row) * 16;
+    }
   }
   auto issue = [&](int kt) {
     lds_char *st = lds + (kt & 1) * kStageBytes;
-    const int64_t kofs = static_cast<int64_t>(kt) * kRowBytes;
+    const int64_t kofs = kMN ? static_cast<int64_t>(kt) * kKStep * ld_bytes : static_cast<int64_t>(kt) * kRowBytes;
 #pragma unroll
     for (int j = 0; j < kDmaPerWave; ++j) {
       const int lofs = (j * 8 + wave) * 1024;
@@ -262,10 +302,58 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
 
   // Fragments of one K step: sub-step 0 covers k chunks 0-3, sub-step 1
   // chunks 4-7 of the 128-byte rows.
-  struct Frag {
+  // Transposed reads return 8-byte halves; they are kept as such until the
+  // explicit wait, so that no register copy can read them before they land.
+  constexpr bool kTr = kMN && sizeof(T) == 2;
+  struct FragK {
     u32x4 l[kFragM], r[kFragN];
   };
+  struct FragT {
+    u32x2 l[kFragM][2], r[kFragN][2];
+  };
+  using Frag = std::conditional_t<kTr, FragT, FragK>;
+  // MN-major bf16: lane l of 16-lane group g4 reads k rows 32*sub + 8*g4 +
+  // 4*h + te (te = (l%16)/4) at column m0 + 4*tq (tq = l%4); rows & 3 = te and
+  // bit 3 of the row = g4 & 1, so the swizzle is a lane constant.
+  const int te = (lane & 15) >> 2, tq = lane & 3;
+  const int tr_swz = mn_swz<T>(8 * g4 + te);
+  const uint32_t tr_base = static_cast<uint32_t>((8 * g4 + te) * 512 + (tq & 1) * 8);
+  auto tr_addr = [&](const lds_char *op, int sub, int h, int m0) -> uint32_t {
+    // chunk of column m0 + 4*tq: m0/8 + tq/2, XOR the swizzle (bits 1-3)
+    const int chunk = (m0 >> 3) + (tq >> 1);
+    return (uint32_t)(uintptr_t)op + tr_base +
+           static_cast<uint32_t>((32 * sub + 4 * h) * 512) + static_cast<uint32_t>((chunk ^ tr_swz) * 16);
+  };
   auto read_frag = [&](const lds_char *st, int sub, Frag &f) {
+    if constexpr (kTr) {
+#pragma unroll
+      for (int i = 0; i < kFragM; ++i) {
+        const int m0 = wm * kWaveM + i * 16;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) f.l[i][h] = ds_read_tr16(tr_addr(st, sub, h, m0));
+      }
+#pragma unroll
+      for (int j = 0; j < kFragN; ++j) {
+        const int m0 = wn * kWaveN + j * 16;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) f.r[j][h] = ds_read_tr16(tr_addr(st + kOperandBytes, sub, h, m0));
+      }
+    } else if constexpr (kMN) {  // fp32: lane (r16, g4) needs k = 16*sub + 4*g4 + t, t = 0..3, of column m
+      typedef __attribute__((address_space(3))) uint32_t lds_u32;
+      auto col = [&](const lds_char *op, int m) {
+        u32x4 v;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int row = 16 * sub + 4 * g4 + t;
+          v[t] = *(const lds_u32 *)(op + row * 1024 + (((m >> 2) ^ mn_swz<T>(row)) * 16) + (m & 3) * 4);
+        }
+        return v;
+      };
+#pragma unroll
+      for (int i = 0; i < kFragM; ++i) f.l[i] = col(st, wm * kWaveM + i * 16 + r16);
+#pragma unroll
+      for (int j = 0; j < kFragN; ++j) f.r[j] = col(st + kOperandBytes, wn * kWaveN + j * 16 + r16);
+    } else {
     const int chunk = sub * 4 + g4;
 #pragma unroll
     for (int i = 0; i < kFragM; ++i) {
@@ -277,12 +365,37 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
       const int row = wn * kWaveN + j * 16 + r16;
       f.r[j] = *(const lds_u32x4 *)(st + kOperandBytes + row * kRowBytes + swz(chunk, row) * 16);
     }
+    }
+  };
+  // The transposed reads are not counted by the compiler: wait for them
+  // explicitly, tied to every half so that no use (or copy) moves above the
+  // wait, and keep the product block between the reads and the wait.
+  auto tr_wait = [&](Frag &f) {
+    if constexpr (kTr) {
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(f.l[0][0]), "+v"(f.l[0][1]), "+v"(f.l[1][0]), "+v"(f.l[1][1]), "+v"(f.l[2][0]),
+                     "+v"(f.l[2][1]), "+v"(f.l[3][0]), "+v"(f.l[3][1]), "+v"(f.l[4][0]), "+v"(f.l[4][1]),
+                     "+v"(f.l[5][0]), "+v"(f.l[5][1]), "+v"(f.l[6][0]), "+v"(f.l[6][1]), "+v"(f.l[7][0]),
+                     "+v"(f.l[7][1]));
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(f.r[0][0]), "+v"(f.r[0][1]), "+v"(f.r[1][0]), "+v"(f.r[1][1]), "+v"(f.r[2][0]),
+                     "+v"(f.r[2][1]), "+v"(f.r[3][0]), "+v"(f.r[3][1]));
+    }
+  };
+  auto opnd = [&](const auto &x) -> u32x4 {  // one MFMA operand of a fragment
+    if constexpr (kTr)
+      return u32x4{x[0].x, x[0].y, x[1].x, x[1].y};
+    else
+      return x;
+  };
+  auto tr_fence = [&]() {
+    if constexpr (kTr) __builtin_amdgcn_sched_barrier(0);
   };
   auto mfma_frag = [&](const Frag &f) {
 #pragma unroll
     for (int i = 0; i < kFragM; ++i)
 #pragma unroll
-      for (int j = 0; j < kFragN; ++j) Mfma<T>::run(acc[i][j], f.l[i], f.r[j]);
+      for (int j = 0; j < kFragN; ++j) Mfma<T>::run(acc[i][j], opnd(f.l[i]), opnd(f.r[j]));
   };
 
   // Software pipeline across the barrier: the products of step k-1's
@@ -295,7 +408,6 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   // [ti*256, ti*256 + 256) holds the tile's rows.  While the K steps of the
   // wave's 128 rows are in LDS, each lane reads its four values (four
   // consecutive k of one R row) and adds a*X to the accumulators.
-  constexpr int kKStep = kRowBytes / static_cast<int>(sizeof(T));  // K elements per step
   constexpr int kCapSteps = kWaveM / kKStep;                         // steps holding the wave's rows
   constexpr int kCapFrags = kKStep / 16;                             // fragment rows per step
   constexpr bool cap_ax = MODE == kModeApply;
@@ -340,6 +452,8 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   capture_ax(lds, 0);
   read_frag(lds, 0, fa);
   read_frag(lds, 1, fb);
+  tr_wait(fa);
+  tr_wait(fb);
   mfma_frag(fa);
   for (int kt = 1; kt < nkt; ++kt) {
     stage_barrier();  // step kt is in LDS; step kt-1's stage is free
@@ -348,8 +462,14 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
     capture_ax(st, kt);
     read_frag(st, 0, fa);
     mfma_frag(fb);    // sub-step 1 of step kt-1
+    tr_fence();
+    tr_wait(fa);
+    tr_fence();
     read_frag(st, 1, fb);
     mfma_frag(fa);
+    tr_fence();
+    tr_wait(fb);
+    tr_fence();
   }
   mfma_frag(fb);
   // no LDS-bound load may still be in flight when the LDS is reused or the
@@ -363,13 +483,13 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   // Row-major bf16 outputs are staged through LDS (the 128 KB of the two
   // stages hold one 256 x 256 bf16 tile) and leave as 16-byte row segments.
   // rows of the computed product come from the L panel, columns from R
-  const int64_t row_base = static_cast<int64_t>(swap ? tj : ti) * kTile + wm * kWaveM + 4 * g4;
-  const int64_t col_base = static_cast<int64_t>(swap ? ti : tj) * kTile + wn * kWaveN + r16;
+  const int64_t row_base = static_cast<int64_t>(ti) * kTile + wm * kWaveM + 4 * g4;
+  const int64_t col_base = static_cast<int64_t>(tj) * kTile + wn * kWaveN + r16;
   constexpr bool kStage = sizeof(T) == 2;
   // fragment rows whose epilogue inputs are read in one batch: all of them
   // for bf16 (2 VGPRs per vector), two at a time for fp32 (4 per vector)
   constexpr int kReadRows = sizeof(T) == 2 ? kFragM : 2;
-  if (kStage && MODE != kModeFinal) stage_barrier();  // mainloop LDS reads done
+  if (kStage || MODE == kModeFinal) stage_barrier();  // mainloop LDS reads done
 
   // The first iteration's X is U unnormalised (X0 = U * inv_norm): A0 picks
   // up inv_norm^2 and the first X' (or O) inv_norm.
@@ -430,9 +550,8 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
       }
     }
   } else if (MODE == kModeApply) {
-    T *Xn = static_cast<T *>(d.x[cur ^ 1]);
     T *XTn = static_cast<T *>(d.xt[cur ^ 1]);
-    const int64_t np = d.np, mp = d.mp;
+    const int64_t mp = d.mp;
 #pragma unroll
     for (int i = 0; i < kFragM; ++i)
 #pragma unroll
@@ -441,86 +560,124 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
         f32x4 val;  // a*X is already in the accumulator
 #pragma unroll
         for (int v = 0; v < 4; ++v) val[v] = acc[i][j][v] * inv;
-        if constexpr (kStage) {
-          stage_tile_put(lds, wm * kWaveM + i * 16 + 4 * g4, wn * kWaveN + j * 16 + r16, val);
-          acc[i][j] = val;  // kept for the X'^T tile
-        } else {
+        // X'^T[col][row .. row+3]: four consecutive elements of a row
+        if constexpr (kStage)
+          stage_tile_put_t(lds, wn * kWaveN + j * 16 + r16, wm * kWaveM + i * 16 + 4 * g4, val);
+        else
           Vec4<T>::st(XTn + col * mp + row, val);
-#pragma unroll
-          for (int v = 0; v < 4; ++v) WsType<T>::st(Xn, (row + v) * np + col, val[v]);
-        }
       }
-    if constexpr (kStage) {
-      // X' tile (ti, tj), then X'^T tile (tj, ti) through the same LDS
-      stage_tile_flush<kSwzRows>(lds, reinterpret_cast<uint16_t *>(Xn) + static_cast<int64_t>(ti) * kTile * np +
-                                          static_cast<int64_t>(tj) * kTile, np, tid);
-      lds_barrier();
-#pragma unroll
-      for (int i = 0; i < kFragM; ++i)
-#pragma unroll
-        for (int j = 0; j < kFragN; ++j)
-          stage_tile_put_t(lds, wn * kWaveN + j * 16 + r16, wm * kWaveM + i * 16 + 4 * g4, acc[i][j]);
+    if constexpr (kStage)
       stage_tile_flush<kSwzCols>(lds, reinterpret_cast<uint16_t *>(XTn) + static_cast<int64_t>(tj) * kTile * mp +
                                           static_cast<int64_t>(ti) * kTile, mp, tid);
-    }
   } else {  // kModeFinal
+    // O = (aX + BX) * inv for the tile (rows over m, columns over n) goes
+    // through LDS as fp32, one half of the rows at a time (the waves with
+    // wm == h hold half h): row-major when P = O (m x n), transposed when
+    // P = O^T (n x m).  Then all threads update P in four-element pieces
+    // along its rows: P -= lr*scale*O, and orth_out = O.  The aX term is
+    // read here (X^T[col][row .. row+3], one vector per fragment).
     const float step = s.lr * d.scale;
-    // (p, q): lane's four values are C[p + v][q] of the computed product.
-    // Not swapped: p over m, q over n, P index (q, p + v) of the r x c = n x m
-    // matrix.  Swapped: the product is C^T, p over n, q over m, P index
-    // (q, p + v) of the m x n matrix.  Either way P[q][p .. p+3].
-    const int64_t p_lim = swap ? d.n : d.m, q_lim = swap ? d.m : d.n;
-    const T *Xsrc = static_cast<const T *>(swap ? d.x[cur] : d.xt[cur]);
-    const int64_t xld = swap ? d.np : d.mp;
+    const bool tp = d.transposed != 0;
     const bool vec_ok = (d.cols & 3) == 0;  // rows of P start 4-element aligned
-    // PT: the parameter's storage type.  Reads of a batch go first (X, and P
-    // on the vector path); four fragment rows per batch when both are bf16.
+    typedef __attribute__((address_space(3))) float lds_f32;
+    typedef __attribute__((address_space(3))) u32x4 lds_v4;
+    // [128][256] fp32, 1 KB rows: chunk XOR 4 * ((row / 4) mod 4), so the four
+    // rows of one put land in distinct 64-byte bank groups
+    auto o_at = [&](int r, int c) { return r * 1024 + (((c >> 2) ^ (((r >> 2) & 3) << 2)) * 16) + (c & 3) * 4; };
+    // [256][128] fp32, 512-byte rows: chunk XOR 4 * (row mod 4)
+    auto ot_at = [&](int r, int c) { return r * 512 + (((c >> 2) ^ ((r & 3) << 2)) * 16); };
     auto update = [&](auto ptag) {
       using PT = decltype(ptag);
-      constexpr int kRows = sizeof(T) == 2 ? (sizeof(PT) == 2 ? 4 : 2) : 1;
       PT *const P = static_cast<PT *>(d.param);
       PT *const Orth = static_cast<PT *>(d.orth);
 #pragma unroll
-      for (int i0 = 0; i0 < kFragM; i0 += kRows) {
-        typename Vec4<T>::Raw xraw[kRows][kFragN];
-        typename Vec4<PT>::Raw praw[kRows][kFragN];
+      for (int h = 0; h < kWavesM; ++h) {
+        if (h > 0) lds_barrier();  // the previous half has been read
+        if (wm == h) {
+          const T *XT = static_cast<const T *>(d.xt[cur]);
+          constexpr int kXRows = sizeof(T) == 2 ? 4 : 2;  // fragment rows per read batch
 #pragma unroll
-        for (int ii = 0; ii < kRows; ++ii)
+          for (int i0 = 0; i0 < kFragM; i0 += kXRows) {
+            typename Vec4<T>::Raw xraw[kXRows][kFragN];
 #pragma unroll
-          for (int j = 0; j < kFragN; ++j) {
-            const int64_t q = col_base + j * 16, p = row_base + (i0 + ii) * 16;
-            xraw[ii][j] = Vec4<T>::raw(Xsrc + q * xld + p);  // in the padded buffer
-            if (vec_ok && p + 4 <= p_lim && q < q_lim) praw[ii][j] = Vec4<PT>::raw(P + q * d.cols + p);
-          }
+            for (int ii = 0; ii < kXRows; ++ii)
 #pragma unroll
-        for (int ii = 0; ii < kRows; ++ii)
+              for (int j = 0; j < kFragN; ++j)
+                xraw[ii][j] = Vec4<T>::raw(XT + (col_base + j * 16) * d.mp + row_base + (i0 + ii) * 16);
 #pragma unroll
-          for (int j = 0; j < kFragN; ++j) {
-            const int i = i0 + ii;
-            const int64_t q = col_base + j * 16, p = row_base + i * 16;
-            if (p >= p_lim || q >= q_lim) continue;
-            const f32x4 xv = Vec4<T>::cvt(xraw[ii][j]);
-            f32x4 o;
+            for (int ii = 0; ii < kXRows; ++ii)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) o[v] = fmaf(s.a, xv[v], acc[i][j][v]) * inv;
-            const int64_t pidx = q * d.cols + p;
-            if (vec_ok && p + 4 <= p_lim) {
-              const f32x4 pv = Vec4<PT>::cvt(praw[ii][j]);
-              f32x4 nv;
+            for (int j = 0; j < kFragN; ++j) {
+              const int i = i0 + ii;
+              const int rl = i * 16 + 4 * g4, cl = wn * kWaveN + j * 16 + r16;
+              const f32x4 xv = Vec4<T>::cvt(xraw[ii][j]);
+              f32x4 o;
 #pragma unroll
-              for (int v = 0; v < 4; ++v) nv[v] = fmaf(-step, o[v], pv[v]);
-              Vec4<PT>::st(P + pidx, nv);
-              if (Orth) Vec4<PT>::st(Orth + pidx, o);
-            } else {
+              for (int v = 0; v < 4; ++v) o[v] = fmaf(s.a, xv[v], acc[i][j][v]) * inv;
+              if (tp) {
+                *(lds_v4 *)(lds + ot_at(cl, rl)) =
+                    u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
+              } else {
 #pragma unroll
-              for (int v = 0; v < 4; ++v) {
-                if (p + v >= p_lim) break;
-                if (Orth) store_elem(d.orth, d.param_dt, pidx + v, o[v]);
-                store_elem(d.param, d.param_dt, pidx + v,
-                           fmaf(-step, o[v], load_elem(d.param, d.param_dt, pidx + v)));
+                for (int v = 0; v < 4; ++v) *(lds_f32 *)(lds + o_at(rl + v, cl)) = o[v];
               }
             }
           }
+        }
+        lds_barrier();
+        // 16 pieces per thread in batches (8 for bf16 P, 4 for fp32), the P
+        // reads of a batch first.  Piece q: staged block (r, c), P element (pr, pc), n valid.
+        struct Piece {
+          int r, c, n;
+          int64_t idx;
+        };
+        auto piece = [&](int q) {
+          Piece pc_;
+          int64_t pr, pcol;
+          if (tp) {
+            pc_.r = q * 16 + (tid >> 5), pc_.c = (tid & 31) * 4;
+            pr = static_cast<int64_t>(tj) * kTile + pc_.r;
+            pcol = static_cast<int64_t>(ti) * kTile + h * kWaveM + pc_.c;
+          } else {
+            pc_.r = q * 8 + (tid >> 6), pc_.c = (tid & 63) * 4;
+            pr = static_cast<int64_t>(ti) * kTile + h * kWaveM + pc_.r;
+            pcol = static_cast<int64_t>(tj) * kTile + pc_.c;
+          }
+          pc_.n = (pr < d.rows && pcol < d.cols) ? static_cast<int>(min<int64_t>(4, d.cols - pcol)) : 0;
+          pc_.idx = pr * d.cols + pcol;
+          return pc_;
+        };
+        constexpr int kBatch = sizeof(PT) == 2 ? 8 : 4;
+#pragma unroll
+        for (int q0 = 0; q0 < 16; q0 += kBatch) {
+          typename Vec4<PT>::Raw praw[kBatch];
+#pragma unroll
+          for (int qq = 0; qq < kBatch; ++qq) {
+            const Piece pp = piece(q0 + qq);
+            if (vec_ok && pp.n == 4) praw[qq] = Vec4<PT>::raw(P + pp.idx);
+          }
+#pragma unroll
+          for (int qq = 0; qq < kBatch; ++qq) {
+            const Piece pp = piece(q0 + qq);
+            if (pp.n == 0) continue;
+            const u32x4 u = *(const lds_v4 *)(lds + (tp ? ot_at(pp.r, pp.c) : o_at(pp.r, pp.c)));
+            const f32x4 o = Vec4<float>::cvt(u);
+            if (vec_ok && pp.n == 4) {
+              const f32x4 pv = Vec4<PT>::cvt(praw[qq]);
+              f32x4 nv;
+#pragma unroll
+              for (int v = 0; v < 4; ++v) nv[v] = fmaf(-step, o[v], pv[v]);
+              Vec4<PT>::st(P + pp.idx, nv);
+              if (Orth) Vec4<PT>::st(Orth + pp.idx, o);
+            } else {
+              for (int v = 0; v < pp.n; ++v) {
+                if (d.orth) store_elem(d.orth, d.param_dt, pp.idx + v, o[v]);
+                store_elem(d.param, d.param_dt, pp.idx + v,
+                           fmaf(-step, o[v], load_elem(d.param, d.param_dt, pp.idx + v)));
+              }
+            }
+          }
+        }
       }
     };
     if (d.param_dt == kBF16)

@@ -45,6 +45,9 @@ bool dtype_ok(int32_t dt) { return dt == DMUON_BF16 || dt == DMUON_F32; }
 
 constexpr int64_t kMaxDim = int64_t(1) << 31;
 constexpr int64_t kMaxNumel = int64_t(1) << 40;
+// The step's kernels address an operand row block with 32-bit offsets
+// (256 rows x 4 bytes x 2^22 < 2^32) and tiles with 16-bit indices.
+constexpr int64_t kMaxStepDim = int64_t(1) << 22;
 
 // ---------------------------------------------------------------- aliasing --
 struct Interval {
@@ -88,6 +91,14 @@ int validate_config(const dmuon_step_config *cfg) {
   if (cfg->eps < 0.f) return fail(DMUON_ERR_INVALID_ARG, "eps < 0");
   const uint32_t known = DMUON_FLAG_NS_FP32 | DMUON_FLAG_NESTEROV;
   if (cfg->flags & ~known) return fail(DMUON_ERR_INVALID_ARG, "unknown flag bits 0x%x", cfg->flags & ~known);
+  return DMUON_OK;
+}
+
+int validate_step_shapes(const dmuon_matrix *mats, int32_t n) {
+  for (int32_t i = 0; i < n; ++i)
+    if (mats[i].rows > kMaxStepDim || mats[i].cols > kMaxStepDim)
+      return fail(DMUON_ERR_INVALID_ARG, "matrix %d: %lld x %lld exceeds the step's limit of %lld per side", i,
+                  (long long)mats[i].rows, (long long)mats[i].cols, (long long)kMaxStepDim);
   return DMUON_OK;
 }
 
@@ -247,8 +258,6 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
     const int64_t xb = d.mp * d.np * es, ab = d.mp * d.mp * es;
     const int nbuf = K >= 2 ? 2 : 1;
     for (int b = 0; b < nbuf; ++b) {
-      d.x[b] = ws ? ws + off : nullptr;
-      off = round_up(off + xb, 256);
       d.xt[b] = ws ? ws + off : nullptr;
       off = round_up(off + xb, 256);
     }
@@ -397,6 +406,8 @@ int dmuon_workspace_bytes(const dmuon_matrix *mats, int32_t n, const dmuon_step_
   if (rc) return rc;
   rc = validate_shapes(mats, n);
   if (rc) return rc;
+  rc = validate_step_shapes(mats, n);
+  if (rc) return rc;
   Plan p;
   build_plan(mats, n, *cfg, nullptr, p);
   *out_bytes = static_cast<size_t>(p.total_bytes);
@@ -412,6 +423,8 @@ static int muon_step_impl(const dmuon_matrix *mats, int32_t n, const dmuon_step_
   int rc = validate_config(cfg);
   if (rc) return rc;
   rc = validate_shapes(mats, n);
+  if (rc) return rc;
+  rc = validate_step_shapes(mats, n);
   if (rc) return rc;
   if (n == 0) return DMUON_OK;
 

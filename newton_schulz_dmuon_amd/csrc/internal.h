@@ -31,8 +31,7 @@ struct MatDev {
   float *mom;
   void *orth;
   // workspace memory (element type bf16, or fp32 in the fp32 mode)
-  void *x[2];       // m_p x n_p, row-major, ping-pong
-  void *xt[2];      // n_p x m_p, row-major: the transpose of x[i]
+  void *xt[2];      // X^T, n_p x m_p, row-major: the iterate, ping-pong
   void *a;          // m_p x m_p: A = X X^T
   void *b;          // m_p x m_p: B = b A + c A A
   double *partials; // sum of U^2 per flat chunk (ns_steps = 0) or per
