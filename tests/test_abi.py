@@ -146,6 +146,21 @@ def test_bad_config(lib, bad, code):
     assert step(lib, [mat()], cfg(**bad), nbytes=1 << 30) == code
 
 
+def test_step_side_limit(lib):
+    """The step takes at most 2^22 elements per side (the kernels' 32-bit
+    row-block offsets and 16-bit tile indices); pack and unpack do not."""
+    c = cfg()
+    ok = mat(rows=1 << 22, cols=2)
+    rc, _ = ws_bytes(lib, [ok], c)
+    assert rc == _lib.OK
+    for r, cc in ((1 << 22) + 1, 2), (2, (1 << 22) + 1):
+        m = mat(rows=r, cols=cc)
+        rc, _ = ws_bytes(lib, [m], c)
+        assert rc == _lib.ERR_INVALID_ARG
+        assert step(lib, [m], c, nbytes=1 << 30) == _lib.ERR_INVALID_ARG
+        assert b"limit" in lib.dmuon_last_error()
+
+
 def test_bad_matrices(lib):
     c = cfg()
     big = 1 << 30
