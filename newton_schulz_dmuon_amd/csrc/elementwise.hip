@@ -116,72 +116,94 @@ __global__ __launch_bounds__(256) void finalize_norm_kernel(const MatDev *__rest
   if (threadIdx.x == 0) *d.inv_norm = static_cast<float>(1.0 / (sqrt(tot) + (double)eps));
 }
 
-// Fused momentum + sum of squares + wide orientation, one 64 x 64 tile of the
-// padded X (m_p x n_p) per work-group:
-//   M <- mu*M + G on the caller block that maps onto the tile,
-//   U = M (or G + mu*M), its sum of squares into partials[tile],
+// Fused momentum + sum of squares + wide orientation:
+//   M <- mu*M + G on the caller's elements that map onto the group's block,
+//   U = M (or G + mu*M), its sum of squares into partials[group],
 //   U written unnormalised as X^T (n_p x m_p), zero in the padding.
+// A tall matrix is its own X^T: group t takes its contiguous elements
+// [4096 t, 4096 t + 4096) (long row runs keep HBM pages open).  Otherwise
+// X^T = U^T and group t takes a 64 x 128 block of U, transposed through LDS,
+// so that M is read in 512-byte and X^T written in 128-byte row segments.
 // The 1/(||U||_F + eps) scale is applied by the first iteration's Gram and
-// Apply epilogues, so M is read once.  The block is staged through LDS so
-// that X^T leaves in row segments whichever way the caller's matrix lies.
+// Apply epilogues, so M is read once.
+template <typename T>
+__device__ __forceinline__ void momentum4(const MatDev &d, int64_t ur, int64_t uc, float mu, bool nesterov,
+                                          bool vec, float (&u)[4]) {
+  u[0] = u[1] = u[2] = u[3] = 0.f;
+  if (ur >= d.rows || uc >= d.cols) return;
+  const int64_t idx = ur * d.cols + uc;
+  if (vec && uc + 4 <= d.cols) {
+    float4 mv = *reinterpret_cast<const float4 *>(d.mom + idx);
+    const f32x4 g = load_grad4(d.grad, d.grad_dt, idx);
+    mv.x = fmaf(mu, mv.x, g[0]);
+    mv.y = fmaf(mu, mv.y, g[1]);
+    mv.z = fmaf(mu, mv.z, g[2]);
+    mv.w = fmaf(mu, mv.w, g[3]);
+    *reinterpret_cast<float4 *>(d.mom + idx) = mv;
+    u[0] = mv.x; u[1] = mv.y; u[2] = mv.z; u[3] = mv.w;
+    if (nesterov)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) u[k] = fmaf(mu, u[k], g[k]);
+  } else {
+    for (int k = 0; k < 4 && uc + k < d.cols; ++k) {
+      const float g = load_elem(d.grad, d.grad_dt, idx + k);
+      const float m = fmaf(mu, d.mom[idx + k], g);
+      d.mom[idx + k] = m;
+      u[k] = nesterov ? fmaf(mu, m, g) : m;
+    }
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kOrientThreads) void momentum_orient_kernel(
     const MatDev *__restrict__ mats, int32_t nmat, StepScalars s) {
   constexpr int TT = static_cast<int>(kTrTile);
-  static_assert(TT * TT == kOrientThreads * 4, "four elements per thread");
-  __shared__ float tile[TT][TT + 1];
+  static_assert(TT * TT == kOrientThreads * 4, "four elements per thread and tile");
+  __shared__ float tile[TT][2 * TT + 1];
   __shared__ double red[kOrientThreads / 64];
   const int64_t w = blockIdx.x;
   const int32_t mi = find_range(nmat, w, [&](int32_t i) { return mats[i].tr_first; });
   const MatDev &d = mats[mi];
   const int64_t t = w - d.tr_first;
-  const int64_t tiles_n = d.np / TT;
-  const int64_t i0 = (t / tiles_n) * TT, j0 = (t % tiles_n) * TT;  // X coords
-  const int64_t ur0 = d.transposed ? j0 : i0, uc0 = d.transposed ? i0 : j0;
   const float mu = s.mu;
   const int tid = threadIdx.x;
   const bool vec = (d.cols & 3) == 0;  // rows of M start 16-byte aligned
-  // read: 4 consecutive columns of one row per thread
-  const int p = tid >> 4, q = (tid & 15) * 4;
-  const int64_t ur = ur0 + p, uc = uc0 + q;
-  float u[4] = {0.f, 0.f, 0.f, 0.f};
-  if (ur < d.rows && uc < d.cols) {
-    const int64_t idx = ur * d.cols + uc;
-    if (vec && uc + 4 <= d.cols) {
-      float4 mv = *reinterpret_cast<const float4 *>(d.mom + idx);
-      const f32x4 g = load_grad4(d.grad, d.grad_dt, idx);
-      mv.x = fmaf(mu, mv.x, g[0]);
-      mv.y = fmaf(mu, mv.y, g[1]);
-      mv.z = fmaf(mu, mv.z, g[2]);
-      mv.w = fmaf(mu, mv.w, g[3]);
-      *reinterpret_cast<float4 *>(d.mom + idx) = mv;
-      u[0] = mv.x; u[1] = mv.y; u[2] = mv.z; u[3] = mv.w;
-      if (s.nesterov)
+  T *XT = static_cast<T *>(d.xt[0]);
+  double acc = 0.0;
+  if (d.transposed) {
+    const int64_t e0 = t * (TT * TT) + 4 * tid;
+    float u[4];
+    momentum4<T>(d, e0 / d.mp, e0 % d.mp, mu, s.nesterov, vec, u);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) u[k] = fmaf(mu, u[k], g[k]);
-    } else {
-      for (int k = 0; k < 4 && uc + k < d.cols; ++k) {
-        const float g = load_elem(d.grad, d.grad_dt, idx + k);
-        const float m = fmaf(mu, d.mom[idx + k], g);
-        d.mom[idx + k] = m;
-        u[k] = s.nesterov ? fmaf(mu, m, g) : m;
+    for (int k = 0; k < 4; ++k) acc += (double)u[k] * u[k];
+    Vec4St<T>::st(XT + e0, u);  // X^T[ur][uc .. uc+3], zeros in the padding
+  } else {
+    // block rows i0 .. i0+63 (m), columns j0 .. j0+127 (n); thread: row p,
+    // columns q and q + 64 (4 each)
+    const int64_t blocks_n = d.np / (2 * TT);
+    const int64_t i0 = (t / blocks_n) * TT, j0 = (t % blocks_n) * (2 * TT);
+    const int p = tid >> 4, q = (tid & 15) * 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float u[4];
+      momentum4<T>(d, i0 + p, j0 + h * TT + q, mu, s.nesterov, vec, u);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        tile[p][h * TT + q + k] = u[k];
+        acc += (double)u[k] * u[k];
       }
     }
-  }
-  double acc = 0.0;
+    __syncthreads();
+    // X^T rows j0 + a (a < 128), elements i0 + b .. b+3
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    tile[p][q + k] = u[k];
-    acc += (double)u[k] * u[k];
-  }
-  __syncthreads();
-  // write: 4 consecutive elements of an X^T row per thread
-  T *XT = static_cast<T *>(d.xt[0]);
-  const int a = tid >> 4, b = (tid & 15) * 4;
-  float vt[4];
+    for (int h = 0; h < 2; ++h) {
+      const int a = (tid >> 4) + h * TT, b = (tid & 15) * 4;
+      float vt[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) vt[k] = d.transposed ? tile[a][b + k] : tile[b + k][a];  // X^T[j0 + a][i0 + b + k]
-  Vec4St<T>::st(XT + (j0 + a) * d.mp + i0 + b, vt);
+      for (int k = 0; k < 4; ++k) vt[k] = tile[b + k][a];
+      Vec4St<T>::st(XT + (j0 + a) * d.mp + i0 + b, vt);
+    }
+  }
   const double tot = block_sum_f64(acc, red);
   if (tid == 0) d.partials[t] = tot;
 }

@@ -186,6 +186,14 @@ void build_stage_tiles(const std::vector<MatDev> &mats, int st, std::vector<Tile
 }
 
 // Builds the plan; with ws == nullptr only sizes are computed.
+// Work-groups of the momentum / orientation pass for one matrix: a tall
+// matrix (its own X^T) in contiguous 4096-element chunks, otherwise 64 x 128
+// blocks of X (two orientation tiles each).  One sum-of-squares partial each.
+int64_t orient_groups(const MatDev &d) {
+  const int64_t tiles = (d.mp / kTrTile) * (d.np / kTrTile);
+  return d.transposed ? tiles : tiles / 2;
+}
+
 void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg, char *ws,
                 Plan &p) {
   const bool fp32 = cfg.flags & DMUON_FLAG_NS_FP32;
@@ -217,7 +225,7 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
     d.ew_count = static_cast<int32_t>((s.rows * s.cols + kEwChunk - 1) / kEwChunk);
     ew += d.ew_count;
     d.tr_first = tr;
-    tr += (d.mp / kTrTile) * (d.np / kTrTile);
+    tr += orient_groups(d);
   }
   p.ew_total = ew;
   p.tr_total = K > 0 ? tr : 0;
@@ -252,7 +260,7 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
     d.partials = ws ? reinterpret_cast<double *>(ws + p.off_partials) +
                           (K > 0 ? d.tr_first : d.ew_first)
                     : nullptr;
-    d.part_count = K > 0 ? static_cast<int32_t>((d.mp / kTrTile) * (d.np / kTrTile)) : d.ew_count;
+    d.part_count = K > 0 ? static_cast<int32_t>(orient_groups(d)) : d.ew_count;
     d.inv_norm = ws ? reinterpret_cast<float *>(ws + p.off_inv + 256 * int64_t(i)) : nullptr;
     if (K == 0) continue;
     const int64_t xb = d.mp * d.np * es, ab = d.mp * d.mp * es;
