@@ -285,8 +285,8 @@ def main(argv=None) -> int:
     elem = sum(numels)
     gsz = 2 if w.grad_dtype == "bf16" else 4
     gbytes = {"momentum_sumsq": elem * (4 + 4 + gsz),
-              # G read, M read + write, U written twice (X and X^T)
-              "momentum_orient": elem * (gsz + 4 + 4 + 2 * (4 if args.fp32_ns else 2))}
+              # G read, M read + write, U written once (as X^T)
+              "momentum_orient": elem * (gsz + 4 + 4 + (4 if args.fp32_ns else 2))}
     for nm, b in gbytes.items():
         if nm in avg:
             stages[nm] = {"ms": avg[nm], "gbs": b / (avg[nm] * 1e-3) / 1e9}
