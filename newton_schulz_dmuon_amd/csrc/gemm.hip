@@ -590,8 +590,42 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
       using PT = decltype(ptag);
       PT *const P = static_cast<PT *>(d.param);
       PT *const Orth = static_cast<PT *>(d.orth);
+      // bf16 P: all 16 pieces of a half are read before the half is staged,
+      // so their latency hides behind the X^T reads and the LDS puts; fp32 P
+      // reads its pieces in batches of 4 after staging (register budget)
+      constexpr bool kPre = sizeof(PT) == 2;
+      constexpr int kBatch = kPre ? 16 : 4;
 #pragma unroll
       for (int h = 0; h < kWavesM; ++h) {
+        // Piece q of this thread: staged block (r, c), P element (pr, pc), n valid.
+        struct Piece {
+          int r, c, n;
+          int64_t idx;
+        };
+        auto piece = [&](int q) {
+          Piece pc_;
+          int64_t pr, pcol;
+          if (tp) {
+            pc_.r = q * 16 + (tid >> 5), pc_.c = (tid & 31) * 4;
+            pr = static_cast<int64_t>(tj) * kTile + pc_.r;
+            pcol = static_cast<int64_t>(ti) * kTile + h * kWaveM + pc_.c;
+          } else {
+            pc_.r = q * 8 + (tid >> 6), pc_.c = (tid & 63) * 4;
+            pr = static_cast<int64_t>(ti) * kTile + h * kWaveM + pc_.r;
+            pcol = static_cast<int64_t>(tj) * kTile + pc_.c;
+          }
+          pc_.n = (pr < d.rows && pcol < d.cols) ? static_cast<int>(min<int64_t>(4, d.cols - pcol)) : 0;
+          pc_.idx = pr * d.cols + pcol;
+          return pc_;
+        };
+        typename Vec4<PT>::Raw pre[kPre ? 16 : 1];
+        if constexpr (kPre) {
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const Piece pp = piece(q);
+            if (vec_ok && pp.n == 4) pre[q] = Vec4<PT>::raw(P + pp.idx);
+          }
+        }
         if (h > 0) lds_barrier();  // the previous half has been read
         if (wm == h) {
           const T *XT = static_cast<const T *>(d.xt[cur]);
@@ -625,36 +659,16 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
           }
         }
         lds_barrier();
-        // 16 pieces per thread in batches (8 for bf16 P, 4 for fp32), the P
-        // reads of a batch first.  Piece q: staged block (r, c), P element (pr, pc), n valid.
-        struct Piece {
-          int r, c, n;
-          int64_t idx;
-        };
-        auto piece = [&](int q) {
-          Piece pc_;
-          int64_t pr, pcol;
-          if (tp) {
-            pc_.r = q * 16 + (tid >> 5), pc_.c = (tid & 31) * 4;
-            pr = static_cast<int64_t>(tj) * kTile + pc_.r;
-            pcol = static_cast<int64_t>(ti) * kTile + h * kWaveM + pc_.c;
-          } else {
-            pc_.r = q * 8 + (tid >> 6), pc_.c = (tid & 63) * 4;
-            pr = static_cast<int64_t>(ti) * kTile + h * kWaveM + pc_.r;
-            pcol = static_cast<int64_t>(tj) * kTile + pc_.c;
-          }
-          pc_.n = (pr < d.rows && pcol < d.cols) ? static_cast<int>(min<int64_t>(4, d.cols - pcol)) : 0;
-          pc_.idx = pr * d.cols + pcol;
-          return pc_;
-        };
-        constexpr int kBatch = sizeof(PT) == 2 ? 8 : 4;
 #pragma unroll
         for (int q0 = 0; q0 < 16; q0 += kBatch) {
           typename Vec4<PT>::Raw praw[kBatch];
 #pragma unroll
           for (int qq = 0; qq < kBatch; ++qq) {
             const Piece pp = piece(q0 + qq);
-            if (vec_ok && pp.n == 4) praw[qq] = Vec4<PT>::raw(P + pp.idx);
+            if constexpr (kPre)
+              praw[qq] = pre[q0 + qq];
+            else if (vec_ok && pp.n == 4)
+              praw[qq] = Vec4<PT>::raw(P + pp.idx);
           }
 #pragma unroll
           for (int qq = 0; qq < kBatch; ++qq) {
