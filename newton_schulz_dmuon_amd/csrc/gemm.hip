@@ -57,7 +57,7 @@ constexpr int kWaveN = kTile / kWavesN;             // 64
 constexpr int kFragM = kWaveM / 16;                 // 8
 constexpr int kFragN = kWaveN / 16;                 // 4
 constexpr int kStageBytes = 2 * kOperandBytes;     // L and R tiles of one K step
-constexpr int kDmaPerWave = kOperandBytes / 1024 / 8;  // 4 KB-sized DMA instructions
+constexpr int kOperandKBs = kOperandBytes / 1024;     // 1 KB DMA instructions per operand tile
 
 typedef __attribute__((address_space(3))) char lds_char;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -103,6 +103,13 @@ __device__ __forceinline__ u32x2 ds_read_tr16(uint32_t lds_addr) {
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+
+// Synchronises the work-group once this wave's LDS-bound loads have landed.
+__device__ __forceinline__ void dma_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ void plain_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
 template <typename T> struct Mfma;
 template <> struct Mfma<uint16_t> {
@@ -256,42 +263,66 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
-  // This wave's share of a stage: kDmaPerWave instructions per operand, each
-  // filling LDS rows [8b, 8b + 8) of the operand tile, b = j*8 + wave.  Lane
-  // l writes LDS byte 16*l of that KB: row 8b + l/8, physical chunk l%8,
-  // which holds logical chunk swz(l%8, row) of the row.
-  // MN-major: the KB of instruction b covers k rows 2b, 2b+1 (bf16, lane l:
-  // row 2b + l/32, physical chunk l%32) or k row b (fp32, chunk l).
+  const int wm = wave / kWavesN, wn = wave % kWavesN;
+
+  // K-contiguous stages run the ping-pong schedule below.  There the four
+  // waves of half h (wm = h) load L rows [128h, 128h + 128) and waves 0-3
+  // also all of R.  Gram (MN-major operands) runs a pipelined schedule in
+  // which all 8 waves load both operands.
+  constexpr bool kPingPong = !kMN;
+  constexpr int kLoaders = kPingPong ? 4 : 8;
+  // Loader v (v = wn with ping-pong, else the wave) fills KB b = j*kLoaders
+  // + v of an operand tile with its instruction j.  K-contiguous: the KB is
+  // LDS rows [8b, 8b + 8); lane l writes LDS byte 16*l of it: row 8b + l/8,
+  // physical chunk l%8, which holds logical chunk swz(l%8, row).  MN-major:
+  // the KB covers k rows 2b, 2b+1 (bf16, lane l: row 2b + l/32, physical
+  // chunk l%32) or k row b (fp32, chunk l).  The lane's offset for
+  // instruction j is goff0 + j * goff_step plus its chunk, whose swizzle
+  // depends on j only in the MN-major layouts.
   // Offsets within the operand's row block fit 32 bits: the step accepts
   // at most 2^22 elements per side, so 256 rows span < 2^32 bytes.
-  uint32_t goff[kDmaPerWave];
-#pragma unroll
-  for (int j = 0; j < kDmaPerWave; ++j) {
-    const int b = j * 8 + wave;
-    if constexpr (kMN) {
-      const int row = sizeof(T) == 2 ? 2 * b + (lane >> 5) : b;
-      const int pc = sizeof(T) == 2 ? (lane & 31) : lane;
-      goff[j] = static_cast<uint32_t>(row) * static_cast<uint32_t>(ld_bytes) + (pc ^ mn_swz<T>(row)) * 16;
-    } else {
-      const int row = b * 8 + (lane >> 3);
-      goff[j] = static_cast<uint32_t>(row) * static_cast<uint32_t>(ld_bytes) + swz(lane & 7, row) * 16;
-    }
-  }
-  auto issue = [&](int kt) {
-    lds_char *st = lds + (kt & 1) * kStageBytes;
+  const int ldr = kPingPong ? wn : wave;
+  constexpr int kRowsPerJ = kMN ? (sizeof(T) == 2 ? 2 : 1) * kLoaders : 8 * kLoaders;
+  const int lrow = kMN ? (sizeof(T) == 2 ? 2 * ldr + (lane >> 5) : ldr) : ldr * 8 + (lane >> 3);
+  const int lpc = kMN ? (sizeof(T) == 2 ? (lane & 31) : lane) : swz(lane & 7, lrow);
+  const uint32_t goff0 = static_cast<uint32_t>(lrow) * static_cast<uint32_t>(ld_bytes);
+  const uint32_t goff_step = static_cast<uint32_t>(kRowsPerJ) * static_cast<uint32_t>(ld_bytes);
+  auto issue = [&](int slot, int kt) {
+    lds_char *st = lds + slot * kStageBytes;
     const int64_t kofs = kMN ? static_cast<int64_t>(kt) * kKStep * ld_bytes : static_cast<int64_t>(kt) * kRowBytes;
-#pragma unroll
-    for (int j = 0; j < kDmaPerWave; ++j) {
-      const int lofs = (j * 8 + wave) * 1024;
-      __builtin_amdgcn_global_load_lds((const void *)(gl + goff[j] + kofs),
-                                       (__attribute__((address_space(3))) void *)(st + lofs), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void *)(gr + goff[j] + kofs),
-                                       (__attribute__((address_space(3))) void *)(st + kOperandBytes + lofs),
+    const char *const bl = gl + kofs, *const br = gr + kofs;  // uniform
+    // opaque copy: the per-instruction offsets are rebuilt at every issue
+    // instead of being kept live across the mainloop
+    uint32_t g0 = goff0;
+    asm volatile("" : "+v"(g0));
+    auto load = [&](const char *src, int op, int b, uint32_t go) {
+      __builtin_amdgcn_global_load_lds((const void *)(src + go),
+                                       (__attribute__((address_space(3))) void *)(st + op * kOperandBytes + b * 1024),
                                        16, 0, 0);
+    };
+    if constexpr (kPingPong) {
+      constexpr int kHalfKBs = kOperandKBs / 2;
+#pragma unroll
+      for (int j = 0; j < kHalfKBs / kLoaders; ++j)
+        load(bl, 0, wm * kHalfKBs + j * kLoaders + ldr,
+             g0 + static_cast<uint32_t>(wm * (kHalfKBs / kLoaders) + j) * goff_step + static_cast<uint32_t>(lpc) * 16);
+      if (wm == 0) {
+#pragma unroll
+        for (int j = 0; j < kOperandKBs / kLoaders; ++j)
+          load(br, 1, j * kLoaders + ldr, g0 + static_cast<uint32_t>(j) * goff_step + static_cast<uint32_t>(lpc) * 16);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kOperandKBs / kLoaders; ++j) {
+        int pc = lpc;
+        if constexpr (kMN) pc ^= mn_swz<T>(lrow + j * kRowsPerJ);
+        const uint32_t go = g0 + static_cast<uint32_t>(j) * goff_step + static_cast<uint32_t>(pc) * 16;
+        load(bl, 0, j * kLoaders + ldr, go);
+        load(br, 1, j * kLoaders + ldr, go);
+      }
     }
   };
 
-  const int wm = wave / kWavesN, wn = wave % kWavesN;
   const int r16 = lane & 15, g4 = lane >> 4;
 
   f32x4 acc[kFragM][kFragN];
@@ -398,12 +429,6 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
       for (int j = 0; j < kFragN; ++j) Mfma<T>::run(acc[i][j], opnd(f.l[i]), opnd(f.r[j]));
   };
 
-  // Software pipeline across the barrier: the products of step k-1's
-  // sub-step 1 (already in registers) run right after the barrier of step
-  // k, while step k's sub-step 0 fragments come out of LDS.  The loads of
-  // step k+1 are issued unconditionally (the last step re-loads its own K
-  // range into the free stage), so each iteration is one basic block the
-  // compiler can interleave.  nkt >= 4 because operands are padded to 256.
   // The aX term of Apply comes from the R operand, X^T: its rows are the tile's columns and its K range
   // [ti*256, ti*256 + 256) holds the tile's rows.  While the K steps of the
   // wave's 128 rows are in LDS, each lane reads its four values (four
@@ -446,35 +471,74 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   };
 
   Frag fa, fb;
-  issue(0);
-  stage_barrier();
-  issue(1);
-  capture_ax(lds, 0);
-  read_frag(lds, 0, fa);
-  read_frag(lds, 1, fb);
-  tr_wait(fa);
-  tr_wait(fb);
-  mfma_frag(fa);
-  for (int kt = 1; kt < nkt; ++kt) {
-    stage_barrier();  // step kt is in LDS; step kt-1's stage is free
-    const lds_char *st = lds + (kt & 1) * kStageBytes;
-    issue(min(kt + 1, nkt - 1));
-    capture_ax(st, kt);
-    read_frag(st, 0, fa);
-    mfma_frag(fb);    // sub-step 1 of step kt-1
-    tr_fence();
+  if constexpr (kPingPong) {
+    // Waves 0-3 (the tile's rows 0-127) and waves 4-7 (rows 128-255) run the
+    // same step: a read phase (next stage's loads issued, both sub-steps'
+    // fragments read) then a product phase (the step's MFMAs), each ended by
+    // a work-group barrier.  Waves 4-7 start one barrier late, so each SIMD
+    // (one wave of each half) multiplies for one half while the other half
+    // reads.  Step kt's stage takes step kt+2's loads only after both halves
+    // have read it.  The loads of step kt+1 that a half issues in its read
+    // phase of step kt are waited for at the end of its product phase: for
+    // waves 0-3 (their L rows and R) before either half reads that stage,
+    // for waves 4-7 (their L rows) before they read it.  No LDS-bound load
+    // is in flight after the loop.
+    issue(0, 0);
+    stage_barrier();
+    if (wm == 1) plain_barrier();
+    for (int kt = 0; kt < nkt; ++kt) {
+      const lds_char *st = lds + (kt & 1) * kStageBytes;
+      issue((kt + 1) & 1, min(kt + 1, nkt - 1));
+      capture_ax(st, kt);
+      read_frag(st, 0, fa);
+      read_frag(st, 1, fb);
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_frag(fa);
+      mfma_frag(fb);
+      __builtin_amdgcn_sched_barrier(0);
+      dma_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (wm == 0) plain_barrier();
+  } else {
+    // Software pipeline across the barrier: the products of step k-1's
+    // sub-step 1 (already in registers) run right after the barrier of step
+    // k, while step k's sub-step 0 fragments come out of LDS.  The loads of
+    // step k+1 go into the stage step k-1 has left; the last step re-loads
+    // its own K range there, so each iteration is one basic block the
+    // compiler can interleave.  nkt >= 4 because operands are padded to 256.
+    issue(0, 0);
+    stage_barrier();
+    issue(1, 1);
+    capture_ax(lds, 0);
+    read_frag(lds, 0, fa);
+    read_frag(lds, 1, fb);
     tr_wait(fa);
-    tr_fence();
-    read_frag(st, 1, fb);
-    mfma_frag(fa);
-    tr_fence();
     tr_wait(fb);
-    tr_fence();
+    mfma_frag(fa);
+    for (int kt = 1; kt < nkt; ++kt) {
+      stage_barrier();  // step kt is in LDS; step kt-1's stage is free
+      const lds_char *st = lds + (kt & 1) * kStageBytes;
+      issue((kt + 1) & 1, min(kt + 1, nkt - 1));
+      capture_ax(st, kt);
+      read_frag(st, 0, fa);
+      mfma_frag(fb);    // sub-step 1 of step kt-1
+      tr_fence();
+      tr_wait(fa);
+      tr_fence();
+      read_frag(st, 1, fb);
+      mfma_frag(fa);
+      tr_fence();
+      tr_wait(fb);
+      tr_fence();
+    }
+    mfma_frag(fb);
+    // no LDS-bound load may still be in flight when the LDS is reused or
+    // the work-group ends
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
-  mfma_frag(fb);
-  // no LDS-bound load may still be in flight when the LDS is reused or the
-  // work-group ends
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- epilogue: lane holds C[row0 + 4*g4 + v][col0 + r16], v = 0..3 ----
   // The four values of a lane are four consecutive rows of one column, i.e.
