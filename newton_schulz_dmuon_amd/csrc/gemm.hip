@@ -57,7 +57,6 @@ constexpr int kWaveN = kTile / kWavesN;             // 64
 constexpr int kFragM = kWaveM / 16;                 // 8
 constexpr int kFragN = kWaveN / 16;                 // 4
 constexpr int kStageBytes = 2 * kOperandBytes;     // L and R tiles of one K step
-constexpr int kOperandKBs = kOperandBytes / 1024;     // 1 KB DMA instructions per operand tile
 
 typedef __attribute__((address_space(3))) char lds_char;
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -73,13 +72,15 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// MN-major operand tiles (Gram reads X^T: K runs down the rows).  An LDS row
-// is one k: 256 elements, 512 bytes (bf16) or 1 KB (fp32); a stage holds
-// kRowBytes / sizeof(T) rows, 32 KB.  The 16-byte chunk of a row is XORed
-// with mn_swz(row), chosen so that the fragment reads below touch distinct
-// banks: bf16 reads 16 rows x 32 bytes (bits 0-1 and 3 of the row pick one
-// of 8 chunk pairs), fp32 reads 4 rows x 64 bytes (bits 2-3 pick the 64-byte
-// group).
+// MN-major operand tiles (Gram reads X^T: K runs down the rows) are held as
+// two 16 KB halves, columns 0-127 and 128-255 of the tile, so that each half
+// of the work-group can load its own.  An LDS row of a half is one k: 128
+// elements, 256 bytes (bf16) or 512 bytes (fp32); a stage holds kRowBytes /
+// sizeof(T) rows.  The 16-byte chunk of a row is XORed with mn_swz(row),
+// chosen so that the fragment reads below touch distinct banks: bf16 reads
+// 16 rows x 32 bytes (bits 0-1 and 3 of the row pick one of 8 chunk pairs),
+// fp32 reads 4 rows x 64 bytes (bits 2-3 pick the 64-byte group).
+constexpr int kHalfBytes = kOperandBytes / 2;
 template <typename T>
 __device__ __forceinline__ int mn_swz(int row) {
   return sizeof(T) == 2 ? ((row & 3) | (((row >> 3) & 1) << 2)) << 1 : ((row >> 2) & 3) << 2;
@@ -265,28 +266,28 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
 
   const int wm = wave / kWavesN, wn = wave % kWavesN;
 
-  // K-contiguous stages run the ping-pong schedule below.  There the four
-  // waves of half h (wm = h) load L rows [128h, 128h + 128) and waves 0-3
-  // also all of R.  Gram (MN-major operands) runs a pipelined schedule in
-  // which all 8 waves load both operands.
-  constexpr bool kPingPong = !kMN;
-  constexpr int kLoaders = kPingPong ? 4 : 8;
-  // Loader v (v = wn with ping-pong, else the wave) fills KB b = j*kLoaders
-  // + v of an operand tile with its instruction j.  K-contiguous: the KB is
-  // LDS rows [8b, 8b + 8); lane l writes LDS byte 16*l of it: row 8b + l/8,
-  // physical chunk l%8, which holds logical chunk swz(l%8, row).  MN-major:
-  // the KB covers k rows 2b, 2b+1 (bf16, lane l: row 2b + l/32, physical
-  // chunk l%32) or k row b (fp32, chunk l).  The lane's offset for
-  // instruction j is goff0 + j * goff_step plus its chunk, whose swizzle
-  // depends on j only in the MN-major layouts.
+  // The four waves of half h (wm = h) load the rows of L that make the
+  // tile's rows [128h, 128h + 128) (K-contiguous: L rows; MN-major: L's
+  // column half h); waves 0-3 also load all of R.  Loader v = wn issues the
+  // 1 KB instructions j*4 + v of each of its operand halves.
+  // K-contiguous: KB b of the tile is LDS rows [8b, 8b + 8); lane l writes
+  // LDS byte 16*l of it: row 8b + l/8, physical chunk l%8, which holds
+  // logical chunk swz(l%8, row).  MN-major: KB b of a half is k rows
+  // [4b, 4b + 4) (bf16, lane l: row 4b + l/16, physical chunk l%16) or
+  // [2b, 2b + 2) (fp32: row 2b + l/32, chunk l%32), physical chunk c holding
+  // logical chunk c ^ mn_swz(row).
   // Offsets within the operand's row block fit 32 bits: the step accepts
   // at most 2^22 elements per side, so 256 rows span < 2^32 bytes.
-  const int ldr = kPingPong ? wn : wave;
-  constexpr int kRowsPerJ = kMN ? (sizeof(T) == 2 ? 2 : 1) * kLoaders : 8 * kLoaders;
-  const int lrow = kMN ? (sizeof(T) == 2 ? 2 * ldr + (lane >> 5) : ldr) : ldr * 8 + (lane >> 3);
-  const int lpc = kMN ? (sizeof(T) == 2 ? (lane & 31) : lane) : swz(lane & 7, lrow);
+  constexpr int kRowsPerKB = kMN ? 1024 / (kHalfBytes / (kRowBytes / static_cast<int>(sizeof(T)))) : 8;
+  constexpr int kChunksPerRow = 64 / kRowsPerKB;
+  constexpr int kKBsPerHalf = kHalfBytes / 1024;  // 16
+  constexpr int kPerLoader = kKBsPerHalf / 4;     // 4 instructions per half and loader
+  // a row of a half: MN-major 128 elements of one k; K-contiguous a tile row
+  const int lrow = wn * kRowsPerKB + lane / kChunksPerRow;
+  const int lpc = lane % kChunksPerRow;
   const uint32_t goff0 = static_cast<uint32_t>(lrow) * static_cast<uint32_t>(ld_bytes);
-  const uint32_t goff_step = static_cast<uint32_t>(kRowsPerJ) * static_cast<uint32_t>(ld_bytes);
+  // rows between instruction j and j + 1 of a loader within one half
+  const uint32_t goff_step = static_cast<uint32_t>(4 * kRowsPerKB) * static_cast<uint32_t>(ld_bytes);
   auto issue = [&](int slot, int kt) {
     lds_char *st = lds + slot * kStageBytes;
     const int64_t kofs = kMN ? static_cast<int64_t>(kt) * kKStep * ld_bytes : static_cast<int64_t>(kt) * kRowBytes;
@@ -295,31 +296,29 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
     // instead of being kept live across the mainloop
     uint32_t g0 = goff0;
     asm volatile("" : "+v"(g0));
-    auto load = [&](const char *src, int op, int b, uint32_t go) {
-      __builtin_amdgcn_global_load_lds((const void *)(src + go),
-                                       (__attribute__((address_space(3))) void *)(st + op * kOperandBytes + b * 1024),
-                                       16, 0, 0);
+    // instruction j of half h of an operand (src, LDS operand op)
+    auto load = [&](const char *src, int op, int h, int j) {
+      const int row = lrow + j * 4 * kRowsPerKB;  // row within the half
+      uint32_t go = g0 + static_cast<uint32_t>(j) * goff_step;
+      if constexpr (kMN)
+        go += static_cast<uint32_t>(h * (kHalfBytes / (kRowBytes / static_cast<int>(sizeof(T))))) +
+              static_cast<uint32_t>(lpc ^ mn_swz<T>(row)) * 16;
+      else
+        go += static_cast<uint32_t>(h * 128) * static_cast<uint32_t>(ld_bytes) +
+              static_cast<uint32_t>(swz(lpc, row)) * 16;
+      __builtin_amdgcn_global_load_lds(
+          (const void *)(src + go),
+          (__attribute__((address_space(3))) void *)(st + op * kOperandBytes + h * kHalfBytes +
+                                                     (j * 4 + wn) * 1024),
+          16, 0, 0);
     };
-    if constexpr (kPingPong) {
-      constexpr int kHalfKBs = kOperandKBs / 2;
 #pragma unroll
-      for (int j = 0; j < kHalfKBs / kLoaders; ++j)
-        load(bl, 0, wm * kHalfKBs + j * kLoaders + ldr,
-             g0 + static_cast<uint32_t>(wm * (kHalfKBs / kLoaders) + j) * goff_step + static_cast<uint32_t>(lpc) * 16);
-      if (wm == 0) {
+    for (int j = 0; j < kPerLoader; ++j) load(bl, 0, wm, j);
+    if (wm == 0) {
 #pragma unroll
-        for (int j = 0; j < kOperandKBs / kLoaders; ++j)
-          load(br, 1, j * kLoaders + ldr, g0 + static_cast<uint32_t>(j) * goff_step + static_cast<uint32_t>(lpc) * 16);
-      }
-    } else {
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int j = 0; j < kOperandKBs / kLoaders; ++j) {
-        int pc = lpc;
-        if constexpr (kMN) pc ^= mn_swz<T>(lrow + j * kRowsPerJ);
-        const uint32_t go = g0 + static_cast<uint32_t>(j) * goff_step + static_cast<uint32_t>(pc) * 16;
-        load(bl, 0, j * kLoaders + ldr, go);
-        load(br, 1, j * kLoaders + ldr, go);
-      }
+        for (int j = 0; j < kPerLoader; ++j) load(br, 1, h, j);
     }
   };
 
@@ -348,12 +347,13 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   // bit 3 of the row = g4 & 1, so the swizzle is a lane constant.
   const int te = (lane & 15) >> 2, tq = lane & 3;
   const int tr_swz = mn_swz<T>(8 * g4 + te);
-  const uint32_t tr_base = static_cast<uint32_t>((8 * g4 + te) * 512 + (tq & 1) * 8);
+  const uint32_t tr_base = static_cast<uint32_t>((8 * g4 + te) * 256 + (tq & 1) * 8);
   auto tr_addr = [&](const lds_char *op, int sub, int h, int m0) -> uint32_t {
-    // chunk of column m0 + 4*tq: m0/8 + tq/2, XOR the swizzle (bits 1-3)
-    const int chunk = (m0 >> 3) + (tq >> 1);
-    return (uint32_t)(uintptr_t)op + tr_base +
-           static_cast<uint32_t>((32 * sub + 4 * h) * 512) + static_cast<uint32_t>((chunk ^ tr_swz) * 16);
+    // column m0 + 4*tq lies in half m0/128, chunk (m0%128)/8 + tq/2 of its
+    // 256-byte row, XOR the swizzle (bits 1-3)
+    const int chunk = ((m0 & 127) >> 3) + (tq >> 1);
+    return (uint32_t)(uintptr_t)op + static_cast<uint32_t>((m0 >> 7) * kHalfBytes) + tr_base +
+           static_cast<uint32_t>((32 * sub + 4 * h) * 256) + static_cast<uint32_t>((chunk ^ tr_swz) * 16);
   };
   auto read_frag = [&](const lds_char *st, int sub, Frag &f) {
     if constexpr (kTr) {
@@ -376,7 +376,8 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
           const int row = 16 * sub + 4 * g4 + t;
-          v[t] = *(const lds_u32 *)(op + row * 1024 + (((m >> 2) ^ mn_swz<T>(row)) * 16) + (m & 3) * 4);
+          v[t] = *(const lds_u32 *)(op + (m >> 7) * kHalfBytes + row * 512 +
+                                    ((((m & 127) >> 2) ^ mn_swz<T>(row)) * 16) + (m & 3) * 4);
         }
         return v;
       };
@@ -471,74 +472,39 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   };
 
   Frag fa, fb;
-  if constexpr (kPingPong) {
-    // Waves 0-3 (the tile's rows 0-127) and waves 4-7 (rows 128-255) run the
-    // same step: a read phase (next stage's loads issued, both sub-steps'
-    // fragments read) then a product phase (the step's MFMAs), each ended by
-    // a work-group barrier.  Waves 4-7 start one barrier late, so each SIMD
-    // (one wave of each half) multiplies for one half while the other half
-    // reads.  Step kt's stage takes step kt+2's loads only after both halves
-    // have read it.  The loads of step kt+1 that a half issues in its read
-    // phase of step kt are waited for at the end of its product phase: for
-    // waves 0-3 (their L rows and R) before either half reads that stage,
-    // for waves 4-7 (their L rows) before they read it.  No LDS-bound load
-    // is in flight after the loop.
-    issue(0, 0);
-    stage_barrier();
-    if (wm == 1) plain_barrier();
-    for (int kt = 0; kt < nkt; ++kt) {
-      const lds_char *st = lds + (kt & 1) * kStageBytes;
-      issue((kt + 1) & 1, min(kt + 1, nkt - 1));
-      capture_ax(st, kt);
-      read_frag(st, 0, fa);
-      read_frag(st, 1, fb);
-      __builtin_amdgcn_sched_barrier(0);
-      lds_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      mfma_frag(fa);
-      mfma_frag(fb);
-      __builtin_amdgcn_sched_barrier(0);
-      dma_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (wm == 0) plain_barrier();
-  } else {
-    // Software pipeline across the barrier: the products of step k-1's
-    // sub-step 1 (already in registers) run right after the barrier of step
-    // k, while step k's sub-step 0 fragments come out of LDS.  The loads of
-    // step k+1 go into the stage step k-1 has left; the last step re-loads
-    // its own K range there, so each iteration is one basic block the
-    // compiler can interleave.  nkt >= 4 because operands are padded to 256.
-    issue(0, 0);
-    stage_barrier();
-    issue(1, 1);
-    capture_ax(lds, 0);
-    read_frag(lds, 0, fa);
-    read_frag(lds, 1, fb);
+  // Waves 0-3 (the tile's rows 0-127) and waves 4-7 (rows 128-255) run the
+  // same step: a read phase (next stage's loads issued, both sub-steps'
+  // fragments read) then a product phase (the step's MFMAs), each ended by
+  // a work-group barrier.  Waves 4-7 start one barrier late, so each SIMD
+  // (one wave of each half) multiplies for one half while the other half
+  // reads.  Step kt's stage takes step kt+2's loads only after both halves
+  // have read it.  The loads of step kt+1 that a half issues in its read
+  // phase of step kt are waited for at the end of its product phase: for
+  // waves 0-3 (their L rows and R) before either half reads that stage,
+  // for waves 4-7 (their L rows) before they read it.  No LDS-bound load
+  // is in flight after the loop.
+  issue(0, 0);
+  stage_barrier();
+  if (wm == 1) plain_barrier();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const lds_char *st = lds + (kt & 1) * kStageBytes;
+    issue((kt + 1) & 1, min(kt + 1, nkt - 1));
+    capture_ax(st, kt);
+    read_frag(st, 0, fa);
+    read_frag(st, 1, fb);
+    tr_fence();
     tr_wait(fa);
     tr_wait(fb);
+    __builtin_amdgcn_sched_barrier(0);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
     mfma_frag(fa);
-    for (int kt = 1; kt < nkt; ++kt) {
-      stage_barrier();  // step kt is in LDS; step kt-1's stage is free
-      const lds_char *st = lds + (kt & 1) * kStageBytes;
-      issue((kt + 1) & 1, min(kt + 1, nkt - 1));
-      capture_ax(st, kt);
-      read_frag(st, 0, fa);
-      mfma_frag(fb);    // sub-step 1 of step kt-1
-      tr_fence();
-      tr_wait(fa);
-      tr_fence();
-      read_frag(st, 1, fb);
-      mfma_frag(fa);
-      tr_fence();
-      tr_wait(fb);
-      tr_fence();
-    }
     mfma_frag(fb);
-    // no LDS-bound load may still be in flight when the LDS is reused or
-    // the work-group ends
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    dma_barrier();
+    __builtin_amdgcn_sched_barrier(0);
   }
+  if (wm == 0) plain_barrier();
 
   // ---- epilogue: lane holds C[row0 + 4*g4 + v][col0 + r16], v = 0..3 ----
   // The four values of a lane are four consecutive rows of one column, i.e.
