@@ -436,7 +436,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   // consecutive k of one R row) and adds a*X to the accumulators.
   constexpr int kCapSteps = kWaveM / kKStep;                         // steps holding the wave's rows
   constexpr int kCapFrags = kKStep / 16;                             // fragment rows per step
-  constexpr bool cap_ax = MODE == kModeApply;
+  constexpr bool cap_ax = MODE == kModeApply || MODE == kModeFinal;
   const int cap_kt0 = ti * (kTile / kKStep) + wm * kCapSteps;
   // Step c of the wave's kCapSteps holds fragment rows [c*kCapFrags,
   // (c+1)*kCapFrags).  Every fragment row reads and adds at every capture
@@ -658,26 +658,14 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
         }
         if (h > 0) lds_barrier();  // the previous half has been read
         if (wm == h) {
-          const T *XT = static_cast<const T *>(d.xt[cur]);
-          constexpr int kXRows = sizeof(T) == 2 ? 4 : 2;  // fragment rows per read batch
 #pragma unroll
-          for (int i0 = 0; i0 < kFragM; i0 += kXRows) {
-            typename Vec4<T>::Raw xraw[kXRows][kFragN];
-#pragma unroll
-            for (int ii = 0; ii < kXRows; ++ii)
-#pragma unroll
-              for (int j = 0; j < kFragN; ++j)
-                xraw[ii][j] = Vec4<T>::raw(XT + (col_base + j * 16) * d.mp + row_base + (i0 + ii) * 16);
-#pragma unroll
-            for (int ii = 0; ii < kXRows; ++ii)
+          for (int i = 0; i < kFragM; ++i)
 #pragma unroll
             for (int j = 0; j < kFragN; ++j) {
-              const int i = i0 + ii;
               const int rl = i * 16 + 4 * g4, cl = wn * kWaveN + j * 16 + r16;
-              const f32x4 xv = Vec4<T>::cvt(xraw[ii][j]);
-              f32x4 o;
+              f32x4 o;  // a*X is already in the accumulator
 #pragma unroll
-              for (int v = 0; v < 4; ++v) o[v] = fmaf(s.a, xv[v], acc[i][j][v]) * inv;
+              for (int v = 0; v < 4; ++v) o[v] = acc[i][j][v] * inv;
               if (tp) {
                 *(lds_v4 *)(lds + ot_at(cl, rl)) =
                     u32x4{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]), __float_as_uint(o[3])};
@@ -686,7 +674,6 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
                 for (int v = 0; v < 4; ++v) *(lds_f32 *)(lds + o_at(rl + v, cl)) = o[v];
               }
             }
-          }
         }
         lds_barrier();
 #pragma unroll
