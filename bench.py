@@ -2,10 +2,12 @@
 
 A step is the owner's whole per-step work on its share of matrices: momentum
 accumulation and Frobenius normalisation, ns_steps Newton-Schulz iterations
-(bf16 MFMA), the scaled parameter update (all in ``dmuon_muon_step``, with the
-gradients read in place from the owner's packed gradient buffer), then
-``dmuon_pack`` of the updated parameters into the packed buffer the owner
-broadcasts.  Inputs are seeded synthetic tensors already resident in HBM.
+(bf16 MFMA), the scaled parameter update and the packing of the updated
+parameters into the packed buffer the owner broadcasts, all in one
+``dmuon_muon_step_packed`` call (the gradients read in place from the owner's
+packed gradient buffer; the last Apply writes each updated parameter to its
+tensor and to its packed slot).  Inputs are seeded synthetic tensors already
+resident in HBM.
 
 Prints one JSON line.  ``value`` is algorithmic Newton-Schulz TFLOP/s over
 the whole step time (symmetric products counted as their upper triangle:
@@ -218,21 +220,21 @@ def main(argv=None) -> int:
     log(f"workspace {ws_bytes / 2**30:.2f} GiB")
 
     lib = nsd.load()
-    arr, n = nsd.api.matrices(P, G, M, scales)
+    arr, n = nsd.api.matrices(P, G, M, scales, packed_offsets=offsets)
     cfg = opts.to_c()
     stream = torch.cuda.current_stream(dev)
     n_launch = 2 + 3 * K if K > 0 else 3
 
+    pk_dtype = nsd._lib.BF16 if pdt == torch.bfloat16 else nsd._lib.F32
+
     def step(ev=None):
-        if ev is None:
-            rc = lib.dmuon_muon_step(arr, n, ctypes.byref(cfg), wsbuf.data_ptr(), wsbuf.numel(),
-                                     stream.cuda_stream)
-        else:
-            rc = lib.dmuon_muon_step_traced(arr, n, ctypes.byref(cfg), wsbuf.data_ptr(),
-                                            wsbuf.numel(), stream.cuda_stream, ev.handles,
-                                            len(ev.handles))
+        # the step writes the updated params into the packed buffer too (the
+        # last Apply stores both), which is the owner's dmuon_pack of them
+        rc = lib.dmuon_muon_step_packed(arr, n, ctypes.byref(cfg), wsbuf.data_ptr(), wsbuf.numel(),
+                                        param_packed.data_ptr(), pk_dtype, param_packed.numel(),
+                                        stream.cuda_stream, ev.handles if ev else None,
+                                        len(ev.handles) if ev else 0)
         nsd._lib.check(rc)
-        nsd.pack(P, offsets, param_packed, stream=stream)
 
     for i in range(args.warmup):
         step()

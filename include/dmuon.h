@@ -209,6 +209,28 @@ typedef struct {
 int dmuon_adamw_step(const dmuon_tensor *tensors, int32_t n,
                      const dmuon_adamw_config *cfg, void *stream);
 
+/* dmuon_muon_step that also writes every updated param into a packed buffer,
+ * the buffer an owner broadcasts its updated params from ("Z2 vs Z3 Modes",
+ * "The two packed-buffer lifecycles").  The result equals dmuon_muon_step
+ * followed on the same stream by
+ *   dmuon_pack(mats, n, DMUON_FIELD_PARAM, packed, packed_dtype, packed_numel)
+ * bit for bit, but the last launch (the last Apply, or the direct update when
+ * ns_steps = 0) stores each updated element to both places, so the params are
+ * not read back.
+ *   packed        packed_numel elements of packed_dtype; matrix i occupies
+ *                 [packed_offset_i, packed_offset_i + rows*cols); elements
+ *                 outside the matrices are not written
+ *   events, n_events  as for dmuon_muon_step_traced (n_events = 0: none)
+ * Errors: those of dmuon_muon_step_traced; INVALID_ARG (NULL packed, a slot
+ * outside the buffer), UNSUPPORTED_DTYPE (param dtype != packed_dtype),
+ * MISALIGNED (slot not 16-byte aligned), ALIAS (a slot overlaps another slot
+ * or any buffer of the step, the workspace included). */
+int dmuon_muon_step_packed(const dmuon_matrix *mats, int32_t n,
+                           const dmuon_step_config *cfg, void *workspace,
+                           size_t workspace_bytes, void *packed,
+                           int32_t packed_dtype, int64_t packed_numel,
+                           void *stream, void *const *events, int32_t n_events);
+
 /* dmuon_muon_step that also records caller-created HIP events (hipEvent_t,
  * passed as void*) on `stream`, for per-kernel timing: events[0] before the
  * first launch and events[j] right after the j-th launch.  Launch order:

@@ -31,7 +31,7 @@ FLAG_NESTEROV = 1 << 1
 EXPORTED = ("dmuon_abi_version", "dmuon_error_string", "dmuon_last_error",
             "dmuon_partition_lpt", "dmuon_pack_offsets", "dmuon_workspace_bytes",
             "dmuon_pack", "dmuon_unpack", "dmuon_muon_step", "dmuon_muon_step_traced",
-            "dmuon_adamw_step")
+            "dmuon_muon_step_packed", "dmuon_adamw_step")
 
 
 class Matrix(ctypes.Structure):
@@ -120,10 +120,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dmuon_muon_step.argtypes = [P(Matrix), c_i32, P(StepConfig), vp, ctypes.c_size_t, vp]
     lib.dmuon_muon_step_traced.argtypes = [P(Matrix), c_i32, P(StepConfig), vp,
                                            ctypes.c_size_t, vp, P(vp), c_i32]
+    lib.dmuon_muon_step_packed.argtypes = [P(Matrix), c_i32, P(StepConfig), vp, ctypes.c_size_t,
+                                           vp, c_i32, c_i64, vp, P(vp), c_i32]
     lib.dmuon_adamw_step.argtypes = [P(Tensor), c_i32, P(AdamWConfig), vp]
     for name in ("dmuon_partition_lpt", "dmuon_pack_offsets", "dmuon_workspace_bytes",
                  "dmuon_pack", "dmuon_unpack", "dmuon_muon_step", "dmuon_muon_step_traced",
-            "dmuon_adamw_step"):
+                 "dmuon_muon_step_packed", "dmuon_adamw_step"):
         getattr(lib, name).restype = ctypes.c_int
     if lib.dmuon_abi_version() != ABI_VERSION:
         raise ImportError(f"libdmuon ABI {lib.dmuon_abi_version()} != {ABI_VERSION}")

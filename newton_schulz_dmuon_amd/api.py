@@ -108,22 +108,33 @@ class Workspace:
 
 def muon_step(params: Sequence, grads: Sequence, momenta: Sequence, scales: Sequence[float],
               opts: StepOptions = StepOptions(), orth_out: Optional[Sequence] = None,
-              workspace: Optional[Workspace] = None, stream=None) -> None:
+              workspace: Optional[Workspace] = None, stream=None, packed=None,
+              packed_offsets: Optional[Sequence[int]] = None) -> None:
     """One owner-side Muon step over the matrices, in place on ``params`` and
-    ``momenta`` (and ``orth_out`` when given).  Enqueued on ``stream`` (the
-    current stream by default); synchronise before reading the results."""
+    ``momenta`` (and ``orth_out`` when given).  With ``packed`` (and the
+    matrices' ``packed_offsets``), the updated params are also written into
+    that buffer, as ``pack`` would right after the step.  Enqueued on
+    ``stream`` (the current stream by default); synchronise before reading
+    the results."""
     n = len(params)
     if n == 0:
         return
     device = params[0].device
-    arr, n = matrices(params, grads, momenta, scales, orth_out)
+    if (packed is None) != (packed_offsets is None):
+        raise DmuonError(_lib.ERR_INVALID_ARG, "packed and packed_offsets go together")
+    arr, n = matrices(params, grads, momenta, scales, orth_out, packed_offsets)
     cfg = opts.to_c()
     lib = load()
     need = ctypes.c_size_t(0)
     check(lib.dmuon_workspace_bytes(arr, n, ctypes.byref(cfg), ctypes.byref(need)))
     ws = (workspace or Workspace()).get(need.value, device)
-    check(lib.dmuon_muon_step(arr, n, ctypes.byref(cfg), ws.data_ptr(), ws.numel(),
-                              _stream_handle(device, stream)))
+    if packed is None:
+        check(lib.dmuon_muon_step(arr, n, ctypes.byref(cfg), ws.data_ptr(), ws.numel(),
+                                  _stream_handle(device, stream)))
+    else:
+        check(lib.dmuon_muon_step_packed(arr, n, ctypes.byref(cfg), ws.data_ptr(), ws.numel(),
+                                         _ptr(packed), _dtype_code(packed), packed.numel(),
+                                         _stream_handle(device, stream), None, 0))
 
 
 def pack(tensors: Sequence, offsets: Sequence[int], packed, stream=None) -> None:

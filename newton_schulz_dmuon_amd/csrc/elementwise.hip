@@ -225,7 +225,9 @@ __global__ __launch_bounds__(kEwThreads) void update_direct_kernel(
     if (s.nesterov) u = fmaf(s.mu, u, load_elem(d.grad, d.grad_dt, i));
     const float o = u * inv;
     if (d.orth) store_elem(d.orth, d.param_dt, i, o);
-    store_elem(d.param, d.param_dt, i, fmaf(-step, o, load_elem(d.param, d.param_dt, i)));
+    const float nv = fmaf(-step, o, load_elem(d.param, d.param_dt, i));
+    store_elem(d.param, d.param_dt, i, nv);
+    if (d.packed) store_elem(d.packed, d.param_dt, i, nv);
   }
 }
 

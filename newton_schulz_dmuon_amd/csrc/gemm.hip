@@ -620,6 +620,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
       using PT = decltype(ptag);
       PT *const P = static_cast<PT *>(d.param);
       PT *const Orth = static_cast<PT *>(d.orth);
+      PT *const Packed = static_cast<PT *>(d.packed);  // nullable copy of the updated P
       // bf16 P: all 16 pieces of a half are read before the half is staged,
       // so their latency hides behind the X^T reads and the LDS puts; fp32 P
       // reads its pieces in batches of 4 after staging (register budget)
@@ -699,12 +700,14 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
 #pragma unroll
               for (int v = 0; v < 4; ++v) nv[v] = fmaf(-step, o[v], pv[v]);
               Vec4<PT>::st(P + pp.idx, nv);
+              if (Packed) Vec4<PT>::st(Packed + pp.idx, nv);
               if (Orth) Vec4<PT>::st(Orth + pp.idx, o);
             } else {
               for (int v = 0; v < pp.n; ++v) {
                 if (d.orth) store_elem(d.orth, d.param_dt, pp.idx + v, o[v]);
-                store_elem(d.param, d.param_dt, pp.idx + v,
-                           fmaf(-step, o[v], load_elem(d.param, d.param_dt, pp.idx + v)));
+                const float nv1 = fmaf(-step, o[v], load_elem(d.param, d.param_dt, pp.idx + v));
+                store_elem(d.param, d.param_dt, pp.idx + v, nv1);
+                if (d.packed) store_elem(d.packed, d.param_dt, pp.idx + v, nv1);
               }
             }
           }

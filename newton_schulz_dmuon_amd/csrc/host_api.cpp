@@ -422,12 +422,19 @@ int dmuon_workspace_bytes(const dmuon_matrix *mats, int32_t n, const dmuon_step_
   return DMUON_OK;
 }
 
+// packed == nullptr: no packed copy of the updated params.
 static int muon_step_impl(const dmuon_matrix *mats, int32_t n, const dmuon_step_config *cfg,
                           void *workspace, size_t workspace_bytes, void *stream,
-                          void *const *events, int32_t n_events) {
+                          void *const *events, int32_t n_events, void *packed = nullptr,
+                          int32_t packed_dtype = DMUON_BF16, int64_t packed_numel = 0) {
   g_last_error.clear();
   if (n_events < 0 || (n_events > 0 && !events))
     return fail(DMUON_ERR_INVALID_ARG, "bad event list");
+  if (packed) {
+    if (!dtype_ok(packed_dtype))
+      return fail(DMUON_ERR_UNSUPPORTED_DTYPE, "packed dtype %d", packed_dtype);
+    if (packed_numel < 0) return fail(DMUON_ERR_INVALID_ARG, "packed_numel < 0");
+  }
   int rc = validate_config(cfg);
   if (rc) return rc;
   rc = validate_shapes(mats, n);
@@ -454,6 +461,19 @@ static int muon_step_impl(const dmuon_matrix *mats, int32_t n, const dmuon_step_
     add(d.grad, elem_size(d.grad_dtype), false, "grad");
     add(d.momentum, 4, true, "momentum");
     if (d.orth_out) add(d.orth_out, elem_size(d.param_dtype), true, "orth_out");
+    if (packed) {
+      if (d.param_dtype != packed_dtype)
+        return fail(DMUON_ERR_UNSUPPORTED_DTYPE, "matrix %d: param dtype %d != packed dtype %d", i,
+                    d.param_dtype, packed_dtype);
+      const int64_t ne = d.rows * d.cols;
+      if (d.packed_offset < 0 || d.packed_offset > packed_numel - ne)
+        return fail(DMUON_ERR_INVALID_ARG, "matrix %d: [%lld, +%lld) outside packed buffer of %lld", i,
+                    (long long)d.packed_offset, (long long)ne, (long long)packed_numel);
+      const char *slot = static_cast<const char *>(packed) + d.packed_offset * elem_size(packed_dtype);
+      if (!aligned16(slot))
+        return fail(DMUON_ERR_MISALIGNED, "matrix %d: packed slot not 16-byte aligned", i);
+      add(slot, elem_size(packed_dtype), true, "packed slot");
+    }
   }
 
   rc = check_aliasing(iv);  // caller buffers among themselves
@@ -476,6 +496,9 @@ static int muon_step_impl(const dmuon_matrix *mats, int32_t n, const dmuon_step_
   // ---- validated: plan with real addresses, upload tables, launch ----
   char *ws = static_cast<char *>(workspace);
   build_plan(mats, n, *cfg, ws, p);
+  if (packed)
+    for (int32_t i = 0; i < n; ++i)
+      p.mats[i].packed = static_cast<char *>(packed) + mats[i].packed_offset * elem_size(packed_dtype);
   std::vector<char> tables(static_cast<size_t>(p.table_bytes), 0);
   std::memcpy(tables.data() + p.off_mats, p.mats.data(), sizeof(MatDev) * n);
   for (int st = 0; st < 3; ++st)
@@ -546,6 +569,18 @@ int dmuon_muon_step_traced(const dmuon_matrix *mats, int32_t n, const dmuon_step
                            void *workspace, size_t workspace_bytes, void *stream,
                            void *const *events, int32_t n_events) {
   return muon_step_impl(mats, n, cfg, workspace, workspace_bytes, stream, events, n_events);
+}
+
+int dmuon_muon_step_packed(const dmuon_matrix *mats, int32_t n, const dmuon_step_config *cfg,
+                           void *workspace, size_t workspace_bytes, void *packed,
+                           int32_t packed_dtype, int64_t packed_numel, void *stream,
+                           void *const *events, int32_t n_events) {
+  if (!packed) {
+    g_last_error.clear();
+    return fail(DMUON_ERR_INVALID_ARG, "packed is NULL");
+  }
+  return muon_step_impl(mats, n, cfg, workspace, workspace_bytes, stream, events, n_events, packed,
+                        packed_dtype, packed_numel);
 }
 
 // ------------------------------------------------------------------ AdamW --

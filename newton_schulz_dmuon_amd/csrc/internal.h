@@ -30,6 +30,7 @@ struct MatDev {
   const void *grad;
   float *mom;
   void *orth;
+  void *packed;     // nullable: this matrix's slot of the packed param buffer
   // workspace memory (element type bf16, or fp32 in the fp32 mode)
   void *xt[2];      // X^T, n_p x m_p, row-major: the iterate, ping-pong
   void *a;          // m_p x m_p: A = X X^T

@@ -236,6 +236,37 @@ def test_pack_errors(lib):
     assert lib.dmuon_pack(arr, 0, 0, packed, _lib.BF16, 0, None) == _lib.OK
 
 
+def test_step_packed_errors(lib):
+    """Argument errors of dmuon_muon_step_packed, all reported before any HIP
+    call; valid slots pass every packed check and stop at the small workspace."""
+    c = cfg()
+    packed = FAKE + (1 << 41)
+
+    def sp(mats, packed=packed, pdt=_lib.BF16, numel=1 << 20, nbytes=1):
+        arr = (_lib.Matrix * max(len(mats), 1))(*mats)
+        return lib.dmuon_muon_step_packed(arr, len(mats), ctypes.byref(c), FAKE + (1 << 40), nbytes,
+                                          packed, pdt, numel, None, None, 0)
+
+    a, b = mat(0), mat(1)                     # 8 x 16 = 128 elements each
+    a.packed_offset, b.packed_offset = 0, 128
+    assert sp([a, b]) == _lib.ERR_WORKSPACE_TOO_SMALL
+    assert sp([a, b], packed=None) == _lib.ERR_INVALID_ARG
+    assert sp([a, b], pdt=_lib.F32) == _lib.ERR_UNSUPPORTED_DTYPE   # params are bf16
+    assert sp([a, b], pdt=9) == _lib.ERR_UNSUPPORTED_DTYPE
+    assert sp([a, b], numel=255) == _lib.ERR_INVALID_ARG             # b's slot runs past the end
+    assert sp([a, b], numel=-1) == _lib.ERR_INVALID_ARG
+    b.packed_offset = 100                                             # 200 bytes: misaligned
+    assert sp([a, b]) == _lib.ERR_MISALIGNED
+    b.packed_offset = 64                                              # overlaps a's slot
+    assert sp([a, b]) == _lib.ERR_ALIAS
+    m = mat(0)
+    assert sp([m], packed=m.grad) == _lib.ERR_ALIAS                   # slot over a read buffer
+    assert sp([m], packed=m.param + 128) == _lib.ERR_ALIAS            # slot over the param
+    m.packed_offset = -8
+    assert sp([m]) == _lib.ERR_INVALID_ARG
+    assert sp([], nbytes=0) == _lib.OK
+
+
 # ------------------------------------------------ AdamW validation, no GPU ---
 
 def tensor(i=0, numel=100, pdt=_lib.BF16, gdt=_lib.BF16):

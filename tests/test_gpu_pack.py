@@ -58,3 +58,46 @@ def test_pack_llama8b_owner_share_offsets(nsd):
     owner, _ = nsd.partition_lpt(numels, 8)
     mine = [numels[i] for i in range(len(numels)) if owner[i] == 0]
     assert nsd.pack_offsets(mine, 128) == refp.pack_offsets(mine, 128)
+
+
+@pytest.mark.parametrize("pdt,k", [("bf16", 5), ("bf16", 0), ("f32", 2)])
+def test_step_packed_equals_step_then_pack(nsd, pdt, k):
+    """dmuon_muon_step_packed against dmuon_muon_step followed by dmuon_pack,
+    both through the C ABI on the same inputs: params, momenta and the packed
+    buffer bit for bit (the gaps between slots keep their fill).  The step's
+    own parity with the oracle is checked in test_gpu_step.py."""
+    from _gpu_util import Case, to_dev, torch_dtype
+    shapes = [(300, 700), (700, 300), (17, 33), (256, 256), (1, 300)]
+    case = Case(shapes, pdt, "bf16", seed=11, m_std=1e-3)
+    opts = nsd.StepOptions(ns_steps=k)
+    offs, total = nsd.pack_offsets([r * c for r, c in shapes], 128)
+
+    def run(fused):
+        P = [to_dev(p, pdt) for p in case.P]
+        G = [to_dev(g, "bf16") for g in case.G]
+        M = [to_dev(m, "f32") for m in case.M]
+        packed = torch.full((total,), -3.0, dtype=torch_dtype(pdt), device="cuda")
+        if fused:
+            nsd.muon_step(P, G, M, case.scales, opts, packed=packed, packed_offsets=offs)
+        else:
+            nsd.muon_step(P, G, M, case.scales, opts)
+            nsd.pack(P, offs, packed)
+        torch.cuda.synchronize()
+        return P, M, packed
+
+    P1, M1, k1 = run(True)
+    P2, M2, k2 = run(False)
+    for a, b in zip(P1, P2):
+        assert np.array_equal(bits(a), bits(b))
+    for a, b in zip(M1, M2):
+        assert np.array_equal(bits(a), bits(b))
+    assert np.array_equal(bits(k1), bits(k2))
+    fill = bits(torch.tensor([-3.0], dtype=torch_dtype(pdt)))[0]
+    kb = bits(k1)
+    for p, off in zip(P1, offs):
+        assert np.array_equal(kb[off:off + p.numel()], bits(p).reshape(-1))
+    ends = [off + p.numel() for p, off in zip(P1, offs)]
+    gaps = np.ones(total, bool)
+    for off, end in zip(offs, ends):
+        gaps[off:end] = False
+    assert np.all(kb[gaps] == fill)
