@@ -250,6 +250,11 @@ def main(argv=None) -> int:
     dt = time.perf_counter() - t0
     ms = dt * 1e3 / args.steps
     log(f"timed {args.steps} steps: {ms:.3f} ms/step")
+    # Outside the timed region: one plain copy of known size (the updated
+    # params into the packed buffer, 2 x elements x param bytes), which a
+    # counter profile of this run uses to scale FETCH_SIZE / WRITE_SIZE.
+    nsd.pack(P, offsets, param_packed, stream=stream)
+    torch.cuda.synchronize()
 
     # per-launch durations from the traced events
     names = ["momentum_orient", "norm"] if K > 0 else ["momentum_sumsq", "norm", "update_direct"]
