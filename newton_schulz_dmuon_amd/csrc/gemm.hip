@@ -436,7 +436,14 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   // consecutive k of one R row) and adds a*X to the accumulators.
   constexpr int kCapSteps = kWaveM / kKStep;                         // steps holding the wave's rows
   constexpr int kCapFrags = kKStep / 16;                             // fragment rows per step
-  constexpr bool cap_ax = MODE == kModeApply || MODE == kModeFinal;
+  constexpr bool cap_ax = MODE == kModeApply || MODE == kModeFinal || MODE == kModeSquare;
+  // Square's R operand is A and A is symmetric, so the same K steps hold
+  // A[row][col] (= A[col][row]); it adds (b/c) A, the epilogue scales by c.
+  // With c = 0 (or b/c not finite) it captures nothing and the epilogue
+  // reads A instead.
+  const float sq_w = s.c != 0.f ? s.b / s.c : 0.f;
+  const bool sq_cap = MODE == kModeSquare && s.c != 0.f && __builtin_isfinite(sq_w);
+  const float cap_w = MODE == kModeSquare ? (sq_cap ? sq_w : 0.f) : s.a;
   const int cap_kt0 = ti * (kTile / kKStep) + wm * kCapSteps;
   // Step c of the wave's kCapSteps holds fragment rows [c*kCapFrags,
   // (c+1)*kCapFrags).  Every fragment row reads and adds at every capture
@@ -448,7 +455,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
     if (c < 0 || c >= kCapSteps) return;
 #pragma unroll
     for (int i = 0; i < kFragM; ++i) {
-      const float w = (i / kCapFrags == c) ? s.a : 0.f;
+      const float w = (i / kCapFrags == c) ? cap_w : 0.f;
       const int kb = ((i % kCapFrags) * 16 + 4 * g4) * static_cast<int>(sizeof(T));  // byte offset in the R row
 #pragma unroll
       for (int j = 0; j < kFragN; ++j) {
@@ -536,7 +543,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
 #pragma unroll
     for (int i0 = 0; i0 < kFragM; i0 += kReadRows) {
     typename Vec4<T>::Raw araw[kReadRows][kFragN];
-    if (MODE == kModeSquare)
+    if (MODE == kModeSquare && !sq_cap)
 #pragma unroll
       for (int ii = 0; ii < kReadRows; ++ii)
 #pragma unroll
@@ -552,9 +559,14 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
         f32x4 val = acc[i][j];
         if (MODE == kModeGram) val *= gram_scale;
         if (MODE == kModeSquare) {
-          const f32x4 av = Vec4<T>::cvt(araw[ii][j]);
+          if (sq_cap) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) val[v] = fmaf(s.b, av[v], s.c * val[v]);
+            for (int v = 0; v < 4; ++v) val[v] = s.c * val[v];  // b A is in the accumulator as (b/c) A
+          } else {
+            const f32x4 av = Vec4<T>::cvt(araw[ii][j]);
+#pragma unroll
+            for (int v = 0; v < 4; ++v) val[v] = fmaf(s.b, av[v], s.c * val[v]);
+          }
         }
         if constexpr (kStage) {
           stage_tile_put(lds, wm * kWaveM + i * 16 + 4 * g4, wn * kWaveN + j * 16 + r16, val);
