@@ -8,13 +8,15 @@
 //                            written mirrored (A is symmetric); both operands
 //                            are column blocks of X^T (MN-major tiles)
 //   Square  B = b A + c A A  A A = A A^T is again a Gram product of a
-//                            symmetric matrix: upper tiles + mirror, with
-//                            b A + c (.) applied in the epilogue
+//                            symmetric matrix: upper tiles + mirror; the
+//                            b A term is taken from the R tile in LDS (as
+//                            (b/c) A, scaled by c in the epilogue)
 //   Apply   X' = a X + B X   full tiles, R operand = X^T (K-contiguous); the
 //                            a X term is read from the R tile in LDS during the
 //                            mainloop; X'^T is written
 //   Final   the last Apply: P -= lr*scale*X' in the caller's orientation,
-//           and X' to orth_out; no workspace write
+//           also stored to the packed slot when the step has one, and X'
+//           to orth_out; no workspace write
 //
 // Every product is C[i][j] = sum_k L[i][k] R[j][k].  Square and Apply read
 // both operands k-contiguous (row-major L and R), the layout the MFMA
@@ -27,11 +29,12 @@
 // 32 fp32).  Operand tiles go straight from global memory into LDS with
 // global_load_lds_dwordx4 (no register staging): each wave instruction fills
 // one contiguous KB of LDS, and every lane picks the global 16-byte chunk that
-// belongs at its LDS slot.  Two LDS stages (2 x 64 KB) form a ring: after the
-// barrier that opens step k, the loads of step k+1 go into the stage step k-1
-// used, and run while step k is on the matrix cores.
+// belongs at its LDS slot.  Two LDS stages (2 x 64 KB) form a ring, and the
+// two halves of the work-group run the K loop in ping-pong: one half's waves
+// read fragments (and issue the next stage's loads) while the other half's
+// multiply, switching at every work-group barrier (the mainloop below).
 //
-// LDS rows are 128 bytes; the 16-byte chunk index is XOR-swizzled with
+// K-contiguous LDS rows are 128 bytes; the 16-byte chunk index is XOR-swizzled with
 // (row / 2) mod 8.  A fragment read of 16 consecutive rows then touches 16
 // distinct 16-byte bank groups of the 256-byte LDS line (two rows per line),
 // which the bank-conflict counter confirms at zero.
