@@ -171,12 +171,18 @@ __global__ __launch_bounds__(kOrientThreads) void momentum_orient_kernel(
   T *XT = static_cast<T *>(d.xt[0]);
   double acc = 0.0;
   if (d.transposed) {
-    const int64_t e0 = t * (TT * TT) + 4 * tid;
-    float u[4];
-    momentum4<T>(d, e0 / d.mp, e0 % d.mp, mu, s.nesterov, vec, u);
+    // 8192 contiguous elements of X^T per group: two runs of 4096, four
+    // elements per thread in each (a run lies within one row: m_p is a
+    // multiple of 256)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) acc += (double)u[k] * u[k];
-    Vec4St<T>::st(XT + e0, u);  // X^T[ur][uc .. uc+3], zeros in the padding
+    for (int h = 0; h < 2; ++h) {
+      const int64_t e0 = t * (2 * TT * TT) + h * (TT * TT) + 4 * tid;
+      float u[4];
+      momentum4<T>(d, e0 / d.mp, e0 % d.mp, mu, s.nesterov, vec, u);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) acc += (double)u[k] * u[k];
+      Vec4St<T>::st(XT + e0, u);  // X^T[ur][uc .. uc+3], zeros in the padding
+    }
   } else {
     // block rows i0 .. i0+63 (m), columns j0 .. j0+127 (n); thread: row p,
     // columns q and q + 64 (4 each)

@@ -186,13 +186,10 @@ void build_stage_tiles(const std::vector<MatDev> &mats, int st, std::vector<Tile
 }
 
 // Builds the plan; with ws == nullptr only sizes are computed.
-// Work-groups of the momentum / orientation pass for one matrix: a tall
-// matrix (its own X^T) in contiguous 4096-element chunks, otherwise 64 x 128
-// blocks of X (two orientation tiles each).  One sum-of-squares partial each.
-int64_t orient_groups(const MatDev &d) {
-  const int64_t tiles = (d.mp / kTrTile) * (d.np / kTrTile);
-  return d.transposed ? tiles : tiles / 2;
-}
+// Work-groups of the momentum / orientation pass for one matrix, 8192
+// elements each: a tall matrix (its own X^T) in contiguous 8192-element
+// runs, otherwise 64 x 128 blocks of X.  One sum-of-squares partial each.
+int64_t orient_groups(const MatDev &d) { return (d.mp / kTrTile) * (d.np / kTrTile) / 2; }
 
 void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg, char *ws,
                 Plan &p) {
