@@ -15,7 +15,7 @@ namespace dmuon {
 namespace {
 
 constexpr int kEwThreads = 256;
-constexpr int kOrientThreads = 1024;  // one 64 x 64 tile, four elements per thread
+constexpr int kOrientThreads = 1024;  // 8192 elements per group, eight per thread
 constexpr int kEwPerThread = static_cast<int>(kEwChunk / kEwThreads);  // 32
 static_assert(kEwPerThread % 4 == 0, "4-wide vectors");
 

@@ -36,7 +36,7 @@ struct MatDev {
   void *a;          // m_p x m_p: A = X X^T
   void *b;          // m_p x m_p: B = b A + c A A
   double *partials; // sum of U^2 per flat chunk (ns_steps = 0) or per
-                    // 64 x 64 orientation tile (ns_steps >= 1)
+                    // 8192-element momentum-pass group (ns_steps >= 1)
   float *inv_norm;  // one float: 1 / (||U||_F + eps)
   int64_t rows, cols;   // caller shape r x c
   int64_t m, n;         // wide orientation m = min(r, c), n = max(r, c)
