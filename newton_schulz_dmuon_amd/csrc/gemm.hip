@@ -531,7 +531,8 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   // fragment rows whose epilogue inputs are read in one batch: all of them
   // for bf16 (2 VGPRs per vector), two at a time for fp32 (4 per vector)
   constexpr int kReadRows = sizeof(T) == 2 ? kFragM : 2;
-  if (kStage || MODE == kModeFinal) stage_barrier();  // mainloop LDS reads done
+  // The loop's last barrier is passed by every wave after all of the
+  // mainloop's LDS reads and LDS-bound loads: the LDS is free for staging.
 
   // The first iteration's X is U unnormalised (X0 = U * inv_norm): A0 picks
   // up inv_norm^2 and the first X' (or O) inv_norm.
