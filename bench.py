@@ -171,8 +171,8 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs the owner's step on one GPU; "
-                                   "--gpus above 1 is not supported"}))
+        print(json.dumps({"error": "bench.py measures one owner's step on one GPU (each owner "
+                                   "runs its share independently); --gpus above 1 is not supported"}))
         return 2
 
     import torch
