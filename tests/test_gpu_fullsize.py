@@ -1,7 +1,9 @@
 """Parity at full workload sizes, in the launch configuration bench.py times.
 
-The whole matrix set runs in one ``muon_step`` call, with the gradients read
-from one packed buffer.  A sample of matrices (one of every shape, from the
+The whole matrix set runs in one ``muon_step`` call with a packed param
+buffer (``dmuon_muon_step_packed``, as bench.py times it), with the gradients
+read from one packed buffer; every packed slot must equal its updated param
+bit for bit.  A sample of matrices (one of every shape, from the
 first and the last layer) gets seeded inputs from ``synth`` and is checked
 against the fp64 oracle; the other matrices get device-generated values and
 only shape the launch.
@@ -56,8 +58,12 @@ def run_set(nsd, w, shapes, sample, opts):
     scales = [update_scale(r, c) for _, _, r, c in shapes]
     # orth_out only for the sampled matrices: the binding takes None entries
     # as "no output" (NULL pointer)
-    nsd.muon_step(P, G, M, scales, opts, orth_out=O)
+    ppacked = torch.empty(total, dtype=torch.bfloat16, device=dev)
+    nsd.muon_step(P, G, M, scales, opts, orth_out=O, packed=ppacked, packed_offsets=offs)
     torch.cuda.synchronize()
+    for p, off in zip(P, offs):
+        slot = ppacked[off:off + p.numel()].view(p.shape)
+        assert torch.equal(slot.view(torch.int16), p.view(torch.int16))
     gpu = ([to_host(P[i]) for i in sorted(sample)], [to_host(M[i]) for i in sorted(sample)],
            [to_host(O[i]) for i in sorted(sample)])
     say(f"  gpu step done ({len(shapes)} matrices); oracle on {len(sample)}")
