@@ -209,7 +209,7 @@ __device__ __forceinline__ void stage_tile_put_t(lds_char *lds, int r, int c0, c
 // Writes the staged tile to dst (row-major, leading dimension ld elements)
 // with 16-byte stores: thread t moves chunks t, t + 512, ... (row = f / 32).
 // Starts with a barrier (the puts are visible); a later put into the same
-// LDS needs stage_barrier() first.
+// LDS needs lds_barrier() first (every wave's flush reads done).
 template <int SW>
 __device__ __forceinline__ void stage_tile_flush(lds_char *lds, uint16_t *dst, int64_t ld, int tid) {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
