@@ -98,6 +98,17 @@ def test_mixed_dtypes_and_coefficients(nsd):
     check_step(case, opts, case.run_gpu(opts), case.run_oracle(opts))
 
 
+@pytest.mark.parametrize("c", [1e-30, 1e-40, 0.0])
+def test_square_term_with_tiny_c(nsd, c):
+    """The Square stage takes its b*A term from the operand tiles as (b/c)*A
+    when b/c is finite (1e-30) and reads A instead when it is not (1e-40:
+    b/c overflows fp32) or c = 0: all three agree with the oracle."""
+    case = Case([(300, 700), (513, 513)], "bf16", "bf16", seed=9, m_std=1e-3)
+    opts = nsd.StepOptions(a=1.5, b=-0.5, c=c, ns_steps=7, lr=0.1, momentum=0.9)
+    err = check_step(case, opts, case.run_gpu(opts), case.run_oracle(opts))
+    say(f"  c={c}: O rel err {err:.3e}")
+
+
 def test_heterogeneous_group(nsd):
     """Many shapes in one grouped launch per stage."""
     shapes = [(300, 700), (700, 300), (17, 33), (513, 513), (1, 1), (256, 1024), (1024, 256),
@@ -114,6 +125,26 @@ def test_zero_gradient_and_momentum(nsd):
     P, M, O = case.run_gpu(opts)
     assert np.all(O[0] == 0) and np.all(M[0] == 0)
     assert np.array_equal(P[0], case.P[0].astype(np.float64))
+
+
+def test_nonfinite_input_propagates_within_its_matrix(nsd):
+    """Non-finite inputs propagate and are not clamped (reading R13): a NaN in
+    one gradient element makes that momentum element NaN, the matrix's norm
+    NaN and so its whole O and P; the other matrix of the same grouped
+    launches is unaffected and matches the oracle."""
+    case = Case([(300, 700), (257, 1000)], "bf16", "bf16", seed=21, m_std=1e-3)
+    g0 = case.G[0].copy()
+    g0[5, 7] = np.nan
+    case.G[0] = g0
+    opts = nsd.StepOptions()
+    P, M, O = case.run_gpu(opts)
+    nan_m = np.isnan(M[0])
+    assert nan_m[5, 7] and nan_m.sum() == 1
+    assert np.all(np.isnan(O[0])) and np.all(np.isnan(P[0]))
+    clean = Case([(257, 1000)], "bf16", "bf16")
+    clean.P, clean.G, clean.M, clean.scales = case.P[1:], case.G[1:], case.M[1:], case.scales[1:]
+    err = check_step(clean, opts, (P[1:], M[1:], O[1:]), clean.run_oracle(opts))
+    say(f"  clean matrix O rel err {err:.3e}")
 
 
 def test_qwen25_1p5b_layer(nsd):
