@@ -147,8 +147,18 @@ def cpu_baseline(w, shapes, ns_steps, budget_s: float):
         log(f"cpu oracle {r}x{c}: {dt:.2f} s")
         if t_total > budget_s:
             break
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
     return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle", "matrices_per_s": round(len(done) / t_total, 4),
+            "kind": "oracle", "cpu_model": cpu_model, "host_cpus": os.cpu_count(),
+            "matrices_per_s": round(len(done) / t_total, 4),
             "seconds": round(t_total, 3),
             "sample": f"fp64 NumPy oracle, one step of {len(done)} matrices "
                       f"({', '.join(done)}), algorithmic NS flops / wall time"}
