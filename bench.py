@@ -308,6 +308,13 @@ def main(argv=None) -> int:
         if nm in avg:
             stages[nm] = {"ms": avg[nm], "gbs": b / (avg[nm] * 1e-3) / 1e9}
     stages["norm"] = {"ms": avg["norm"]}
+    # median launch duration of each stage over all its launches in the timed steps
+    for nm, v in stages.items():
+        src = (per.get("apply") or per["final"]) if nm == "apply" else per.get(nm)
+        if src:
+            srt = sorted(src)
+            v["median_ms"] = srt[len(srt) // 2] if len(srt) % 2 else 0.5 * (srt[len(srt) // 2 - 1] + srt[len(srt) // 2])
+            v["launches"] = len(srt)
     for v in stages.values():
         for kk in list(v):
             v[kk] = round(v[kk], 4)
