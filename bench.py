@@ -147,6 +147,24 @@ def cpu_baseline(w, shapes, ns_steps, budget_s: float):
         log(f"cpu oracle {r}x{c}: {dt:.2f} s")
         if t_total > budget_s:
             break
+    # the smallest sampled matrix again on one BLAS thread
+    one_thread = None
+    try:
+        from threadpoolctl import threadpool_limits
+        idx, name, r, c = sample[0]
+        P = normal(w.wid, idx, 1, r, c, w.param_std, w.param_dtype)
+        G = normal(w.wid, idx, 0, r, c, w.grad_std, w.grad_dtype)
+        M = np.zeros((r, c), np.float32)
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            ref.muon_step_matrix(P, G, M, update_scale(r, c), cfg)
+            dt1 = time.perf_counter() - t0
+        f1 = sum(ns_flops(min(r, c), max(r, c), ns_steps).values())
+        one_thread = {"value": round(f1 / dt1 / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+                      "sample": f"{name.split('.')[-1]} {r}x{c}", "seconds": round(dt1, 3)}
+        log(f"cpu oracle {r}x{c} on one thread: {dt1:.2f} s")
+    except Exception:  # pragma: no cover
+        pass
     cpu_model = "unknown"
     try:
         with open("/proc/cpuinfo") as f:
@@ -158,6 +176,7 @@ def cpu_baseline(w, shapes, ns_steps, budget_s: float):
         pass
     return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle", "cpu_model": cpu_model, "host_cpus": os.cpu_count(),
+            "one_thread": one_thread,
             "matrices_per_s": round(len(done) / t_total, 4),
             "seconds": round(t_total, 3),
             "sample": f"fp64 NumPy oracle, one step of {len(done)} matrices "
