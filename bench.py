@@ -9,9 +9,14 @@ packed gradient buffer; the last Apply writes each updated parameter to its
 tensor and to its packed slot).  Inputs are seeded synthetic tensors already
 resident in HBM.
 
+The Gram-space chain (DMUON_FLAG_GRAM_NS) runs for the matrices with
+max(r,c) >= 2 min(r,c); ``--direct-ns`` runs the direct chain for all.
+
 Prints one JSON line.  ``value`` is algorithmic Newton-Schulz TFLOP/s over
-the whole step time (symmetric products counted as their upper triangle:
-m(m+1)n + m^2(m+1) + 2m^2 n per matrix per iteration).
+the whole step time, counted as the direct chain's flops whichever chain
+runs (symmetric products counted as their upper triangle: m(m+1)n +
+m^2(m+1) + 2m^2 n per matrix per iteration), so that it compares across
+chains; ``executed_tflops`` counts the flops the launches actually do.
 """
 
 from __future__ import annotations
@@ -59,20 +64,22 @@ class TraceEvents:
         return self.ev[j].elapsed_time(self.ev[j + 1])
 
 
-def measured_traffic(workload_name: str, fp32: bool):
-    """HBM bytes per Apply launch from the committed rocprofv3 counter
-    summary (FETCH_SIZE and WRITE_SIZE scaled by a copy kernel of known
-    size), or None when the summary is for another workload or the GEMM
-    source has changed since the counters were taken."""
+def measured_traffic(workload_name: str, fp32: bool, kind: str, gram_ns: bool):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 counter summary (FETCH_SIZE and WRITE_SIZE scaled by a copy
+    kernel of known size), or None when the summary is for another workload,
+    kernel or chain, or the GEMM source has changed since the counters were
+    taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "apply_traffic_llama31_8b_owner0.json")
+    path = os.path.join(ROOT, "profiles", "dominant_kernel_traffic_llama31_8b_owner0.json")
     src = os.path.join(ROOT, "newton_schulz_dmuon_amd", "csrc", "gemm.hip")
     try:
         rec = json.load(open(path))
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     except OSError:
         return None
-    if fp32 or rec.get("workload") != workload_name or rec.get("gemm_source_sha256") != sha:
+    if fp32 or rec.get("workload") != workload_name or rec.get("gemm_source_sha256") != sha \
+            or rec.get("kind") != kind or rec.get("gram_ns") != gram_ns:
         return None
     return rec["traffic_bytes_per_launch"]
 
@@ -195,6 +202,8 @@ def main(argv=None) -> int:
     ap.add_argument("--repeat", type=int, default=1, help="copies of each --shape")
     ap.add_argument("--ns-steps", type=int, default=None)
     ap.add_argument("--fp32-ns", action="store_true", help="fp32 checking mode")
+    ap.add_argument("--direct-ns", action="store_true",
+                    help="direct chain for every matrix (default: Gram-space chain where n >= 2m)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
     args = ap.parse_args(argv)
@@ -242,7 +251,7 @@ def main(argv=None) -> int:
         P.append((torch.randn(r, c, generator=gen, device=dev) * w.param_std).to(pdt))
         M.append(torch.zeros(r, c, dtype=torch.float32, device=dev))
     scales = [update_scale(r, c) for _, r, c in shapes]
-    opts = nsd.StepOptions(ns_steps=K, ns_fp32=args.fp32_ns)
+    opts = nsd.StepOptions(ns_steps=K, ns_fp32=args.fp32_ns, gram_ns=not args.direct_ns)
     ws = nsd.Workspace()
     ws_bytes = nsd.workspace_bytes(P, opts)
     wsbuf = ws.get(ws_bytes, dev)
@@ -252,7 +261,10 @@ def main(argv=None) -> int:
     arr, n = nsd.api.matrices(P, G, M, scales, packed_offsets=offsets)
     cfg = opts.to_c()
     stream = torch.cuda.current_stream(dev)
-    n_launch = 2 + 3 * K if K > 0 else 3
+    # the step's launches in order, with the algorithmic flops of each
+    launches = nsd.step_launches([(r, c) for _, r, c in shapes], opts)
+    n_launch = len(launches)
+    log("launches: " + " ".join(k for k, _ in launches))
 
     pk_dtype = nsd._lib.BF16 if pdt == torch.bfloat16 else nsd._lib.F32
 
@@ -285,39 +297,34 @@ def main(argv=None) -> int:
     nsd.pack(P, offsets, param_packed, stream=stream)
     torch.cuda.synchronize()
 
-    # per-launch durations from the traced events
-    names = ["momentum_orient", "norm"] if K > 0 else ["momentum_sumsq", "norm", "update_direct"]
-    for k in range(K):
-        names += ["gram", "square", "final" if k == K - 1 else "apply"]
+    # per-launch durations from the traced events, grouped by launch kind
+    names = [k for k, _ in launches]
     per = {nm: [] for nm in set(names)}
     for ev in evs:
         for j, nm in enumerate(names):
             per[nm].append(ev.elapsed_ms(j))
     avg = {nm: sum(v) / len(v) for nm, v in per.items()}
+    kind_flops = {nm: sum(f for k, f in launches if k == nm) for nm in set(names)}
 
+    # the metric's count: the direct chain's algorithmic flops, whichever
+    # chain runs, so that the rate compares across chains
     flops = {"gram": 0, "square": 0, "apply": 0}
     for _, r, c in shapes:
         for kk, v in ns_flops(min(r, c), max(r, c), K).items():
             flops[kk] += v
     ns_total = sum(flops.values())
-    ns_ms = sum(sum(v) for nm, v in per.items()
-                if nm in ("gram", "square", "apply", "final")) / args.steps
+    executed = sum(f for _, f in launches)
+    gemm_kinds = ("gram", "square", "apply", "final")
+    ns_ms = sum(sum(v) for nm, v in per.items() if nm in gemm_kinds) / args.steps
     peak = PEAK_FP32_TFLOPS if args.fp32_ns else PEAK_BF16_TFLOPS
     value = ns_total / (ms * 1e-3) / 1e12
 
     stages = {}
-    if K > 0:
-        # per launch: one iteration's flops; apply and final share a shape
-        stages["gram"] = {"ms": avg["gram"], "tflops": flops["gram"] / K / (avg["gram"] * 1e-3) / 1e12}
-        stages["square"] = {"ms": avg["square"],
-                            "tflops": flops["square"] / K / (avg["square"] * 1e-3) / 1e12}
-        # Apply launches without the fused update (the dominant kernel); with
-        # ns_steps = 1 only the final launch exists
-        ap = per.get("apply") or per["final"]
-        apply_ms = sum(ap) / len(ap)
-        stages["apply"] = {"ms": apply_ms, "tflops": flops["apply"] / K / (apply_ms * 1e-3) / 1e12}
-        stages["final"] = {"ms": avg["final"],
-                           "tflops": flops["apply"] / K / (avg["final"] * 1e-3) / 1e12}
+    for nm in gemm_kinds:
+        if nm in per:
+            t = sum(per[nm]) / args.steps   # ms per step in this kind
+            stages[nm] = {"ms": avg[nm], "ms_per_step": t, "launches_per_step": names.count(nm),
+                          "tflops": kind_flops[nm] / (t * 1e-3) / 1e12}
     elem = sum(numels)
     gsz = 2 if w.grad_dtype == "bf16" else 4
     gbytes = {"momentum_sumsq": elem * (4 + 4 + gsz),
@@ -329,7 +336,7 @@ def main(argv=None) -> int:
     stages["norm"] = {"ms": avg["norm"]}
     # median launch duration of each stage over all its launches in the timed steps
     for nm, v in stages.items():
-        src = (per.get("apply") or per["final"]) if nm == "apply" else per.get(nm)
+        src = per.get(nm)
         if src:
             srt = sorted(src)
             v["median_ms"] = srt[len(srt) // 2] if len(srt) % 2 else 0.5 * (srt[len(srt) // 2 - 1] + srt[len(srt) // 2])
@@ -340,13 +347,20 @@ def main(argv=None) -> int:
 
     roofline = None
     if K > 0:
-        apply_flops = flops["apply"] / K
-        ach = apply_flops / (stages["apply"]["ms"] * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "kernel": "ns_gemm_kernel<Apply> (X <- aX + BX)",
+        # the dominant kernel: the GEMM stage with the most time per step;
+        # achieved = its algorithmic flops over its launches' summed durations
+        dom = max((nm for nm in gemm_kinds if nm in per), key=lambda nm: sum(per[nm]))
+        ach = kind_flops[dom] / (sum(per[dom]) / args.steps * 1e-3) / 1e12
+        kernel = {"gram": "ns_gemm_kernel<Gram> (A = X X^T)",
+                  "square": "ns_gemm_kernel<Square> (symmetric m x m products)",
+                  "apply": "ns_gemm_kernel<Apply> (X <- aX + BX / X <- QX)",
+                  "final": "ns_gemm_kernel<Final> (last apply + update)"}[dom]
+        roofline = {"bound": "mfma", "kernel": kernel,
                     "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
                     "frac": round(ach / peak, 4),
-                    "traffic": measured_traffic(w.name, args.fp32_ns),
-                    "algorithmic_flops_per_launch": apply_flops}
+                    "traffic": measured_traffic(w.name, args.fp32_ns, dom, opts.gram_ns),
+                    "algorithmic_flops_per_launch": kind_flops[dom] / names.count(dom),
+                    "launches_per_step": names.count(dom)}
 
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
@@ -354,13 +368,20 @@ def main(argv=None) -> int:
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32" if args.fp32_ns else "bf16", "data": "synthetic",
         "config": {"workload": w.name, "matrices": len(shapes), "elements": elem,
-                   "ns_steps": K, "param_dtype": w.param_dtype, "grad_dtype": w.grad_dtype,
+                   "ns_steps": K, "gram_ns": opts.gram_ns,
+                   "param_dtype": w.param_dtype, "grad_dtype": w.grad_dtype,
                    "parallelism": "one owner's share on 1 GPU"},
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "matrices_per_s": round(len(shapes) / (ms * 1e-3), 2),
         "steps_per_s": round(1e3 / ms, 3),
+        "ns_chain": "gram-space where max(r,c) >= 2 min(r,c), direct otherwise" if opts.gram_ns
+                    else "direct",
+        "flop_count": "direct-chain algorithmic count m(m+1)n + m^2(m+1) + 2m^2 n per matrix "
+                      "per iteration, whichever chain runs",
+        "executed_tflop_per_step": round(executed / 1e12, 3),
+        "executed_tflops": round(executed / (ms * 1e-3) / 1e12, 3),
         "ns_kernels_ms": round(ns_ms, 4),
-        "ns_kernels_tflops": round(ns_total / (ns_ms * 1e-3) / 1e12, 3) if ns_ms else None,
+        "ns_kernels_executed_tflops": round(executed / (ns_ms * 1e-3) / 1e12, 3) if ns_ms else None,
         "stages": stages,
         "roofline": roofline,
         "cpu_baseline": None,

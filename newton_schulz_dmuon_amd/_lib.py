@@ -27,11 +27,16 @@ FIELD_PARAM = 0
 FIELD_GRAD = 1
 FLAG_NS_FP32 = 1 << 0
 FLAG_NESTEROV = 1 << 1
+FLAG_GRAM_NS = 1 << 2
+
+# dmuon_launch_info.kind
+LAUNCH_KINDS = ("momentum_sumsq", "momentum_orient", "norm", "update_direct", "gram", "square",
+                "apply", "final")
 
 EXPORTED = ("dmuon_abi_version", "dmuon_error_string", "dmuon_last_error",
             "dmuon_partition_lpt", "dmuon_pack_offsets", "dmuon_workspace_bytes",
             "dmuon_pack", "dmuon_unpack", "dmuon_muon_step", "dmuon_muon_step_traced",
-            "dmuon_muon_step_packed", "dmuon_adamw_step")
+            "dmuon_muon_step_packed", "dmuon_adamw_step", "dmuon_step_launches")
 
 
 class Matrix(ctypes.Structure):
@@ -59,6 +64,11 @@ class StepConfig(ctypes.Structure):
         ("lr", ctypes.c_float), ("momentum", ctypes.c_float), ("eps", ctypes.c_float),
         ("flags", ctypes.c_uint32),
     ]
+
+
+class LaunchInfo(ctypes.Structure):
+    """``dmuon_launch_info``"""
+    _fields_ = [("kind", ctypes.c_int32), ("reserved", ctypes.c_int32), ("flops", ctypes.c_double)]
 
 
 class Tensor(ctypes.Structure):
@@ -123,9 +133,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dmuon_muon_step_packed.argtypes = [P(Matrix), c_i32, P(StepConfig), vp, ctypes.c_size_t,
                                            vp, c_i32, c_i64, vp, P(vp), c_i32]
     lib.dmuon_adamw_step.argtypes = [P(Tensor), c_i32, P(AdamWConfig), vp]
+    lib.dmuon_step_launches.argtypes = [P(Matrix), c_i32, P(StepConfig), P(LaunchInfo), c_i32,
+                                        P(c_i32)]
     for name in ("dmuon_partition_lpt", "dmuon_pack_offsets", "dmuon_workspace_bytes",
                  "dmuon_pack", "dmuon_unpack", "dmuon_muon_step", "dmuon_muon_step_traced",
-                 "dmuon_muon_step_packed", "dmuon_adamw_step"):
+                 "dmuon_muon_step_packed", "dmuon_adamw_step", "dmuon_step_launches"):
         getattr(lib, name).restype = ctypes.c_int
     if lib.dmuon_abi_version() != ABI_VERSION:
         raise ImportError(f"libdmuon ABI {lib.dmuon_abi_version()} != {ABI_VERSION}")

@@ -12,7 +12,7 @@ from dataclasses import dataclass
 from typing import Optional, Sequence
 
 from . import _lib
-from ._lib import AdamWConfig, DmuonError, Matrix, StepConfig, Tensor, check, load
+from ._lib import AdamWConfig, DmuonError, LaunchInfo, Matrix, StepConfig, Tensor, check, load
 
 # Public Muon quintic (Jordan et al., 2024); the DMuon pages print none.
 QUINTIC = (3.4445, -4.7750, 2.0315)
@@ -56,10 +56,14 @@ class StepOptions:
     eps: float = 1e-7
     nesterov: bool = False
     ns_fp32: bool = False
+    # Gram-space chain for matrices with max(r,c) >= 2 min(r,c) (see
+    # DMUON_FLAG_GRAM_NS); the others keep the direct chain
+    gram_ns: bool = False
 
     def to_c(self) -> StepConfig:
         flags = (_lib.FLAG_NESTEROV if self.nesterov else 0) | \
-                (_lib.FLAG_NS_FP32 if self.ns_fp32 else 0)
+                (_lib.FLAG_NS_FP32 if self.ns_fp32 else 0) | \
+                (_lib.FLAG_GRAM_NS if self.gram_ns else 0)
         return StepConfig(self.a, self.b, self.c, int(self.ns_steps), self.lr,
                           self.momentum, self.eps, flags)
 
@@ -82,6 +86,23 @@ def matrices(params, grads=None, momenta=None, scales=None, orth_out=None,
             float(scales[i]) if scales is not None else 1.0, 0,
             int(packed_offsets[i]) if packed_offsets is not None else 0)
     return arr, n
+
+
+def step_launches(shapes: Sequence, opts: StepOptions):
+    """The step's launch sequence for matrices of these ``(rows, cols)``
+    shapes: a list of ``(kind, algorithmic_flops)``, kind a name from
+    ``_lib.LAUNCH_KINDS``.  Host-only."""
+    n = len(shapes)
+    arr = (Matrix * max(n, 1))()
+    for i, (r, c) in enumerate(shapes):
+        arr[i] = Matrix(None, _lib.BF16, _lib.BF16, None, None, None, int(r), int(c), 1.0, 0, 0)
+    cfg = opts.to_c()
+    lib = load()
+    count = ctypes.c_int32(0)
+    check(lib.dmuon_step_launches(arr, n, ctypes.byref(cfg), None, 0, ctypes.byref(count)))
+    out = (LaunchInfo * max(count.value, 1))()
+    check(lib.dmuon_step_launches(arr, n, ctypes.byref(cfg), out, count.value, ctypes.byref(count)))
+    return [(_lib.LAUNCH_KINDS[out[j].kind], out[j].flops) for j in range(count.value)]
 
 
 def workspace_bytes(params, opts: StepOptions) -> int:

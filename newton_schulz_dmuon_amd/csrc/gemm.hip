@@ -5,12 +5,19 @@
 // only as X^T (n_p x m_p, row-major):
 //
 //   Gram    A = X X^T        upper-triangle 256x256 tiles only, each tile also
-//                            written mirrored (A is symmetric); both operands
+//                            written mirrored (A is symmetric; a diagonal
+//                            tile stores its upper triangle and the mirror
+//                            of it, so the stored A is exactly symmetric,
+//                            as is every Square output); both operands
 //                            are column blocks of X^T (MN-major tiles)
 //   Square  B = b A + c A A  A A = A A^T is again a Gram product of a
 //                            symmetric matrix: upper tiles + mirror; the
 //                            b A term is taken from the R tile in LDS (as
-//                            (b/c) A, scaled by c in the epilogue)
+//                            (b/c) A, scaled by c in the epilogue).  The
+//                            Gram-space chain also runs it with its own R
+//                            (sq_r: A P^2, Q P, products of commuting
+//                            symmetric matrices) and a diagonal term
+//                            (P = a I + b A + c A A)
 //   Apply   X' = a X + B X   full tiles, R operand = X^T (K-contiguous); the
 //                            a X term is read from the R tile in LDS during the
 //                            mainloop; X'^T is written
@@ -196,6 +203,23 @@ __device__ __forceinline__ void stage_tile_put(lds_char *lds, int r0, int c, con
   }
 }
 
+// Diagonal tiles of the symmetric outputs: the upper triangle (c >= row)
+// of rows r0 .. r0+3 at column c, each value also at its mirror (c, row)
+// when c > row.  Every element of the tile is written once, so the stored
+// tile is exactly symmetric even when the product is only symmetric in
+// exact arithmetic (A P^2 and Q P of the Gram-space chain).
+__device__ __forceinline__ void stage_tile_put_sym(lds_char *lds, int r0, int c, const f32x4 &v) {
+  typedef __attribute__((address_space(3))) uint16_t lds_u16;
+  auto at = [](int row, int col) { return row * 512 + tile_swz<kSwzRows>(row, col >> 3) * 16 + (col & 7) * 2; };
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int row = r0 + k;
+    const uint16_t bits = f32_to_bf16_bits(v[k]);
+    if (c >= row) *(lds_u16 *)(lds + at(row, c)) = bits;
+    if (c > row) *(lds_u16 *)(lds + at(c, row)) = bits;
+  }
+}
+
 // Puts elements c0 .. c0+3 of row r (c0 a multiple of four) as bf16: the
 // transposed placement of a lane's four values.
 __device__ __forceinline__ void stage_tile_put_t(lds_char *lds, int r, int c0, const f32x4 &v) {
@@ -249,7 +273,8 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
     L = R = static_cast<const T *>(d.xt[cur]);
     ld = d.mp;
   } else if (MODE == kModeSquare) {
-    L = R = static_cast<const T *>(d.a);
+    L = static_cast<const T *>(d.a);
+    R = d.sq_r ? static_cast<const T *>(d.sq_r) : L;
     ld = d.mp;
   } else {
     L = static_cast<const T *>(d.b);
@@ -571,14 +596,28 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
 #pragma unroll
             for (int v = 0; v < 4; ++v) val[v] = fmaf(s.b, av[v], s.c * val[v]);
           }
+          // diag I on the true diagonal only: the padding stays zero
+          if (ti == tj && col < d.m)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              if (row + v == col) val[v] += s.diag;
         }
         if constexpr (kStage) {
-          stage_tile_put(lds, wm * kWaveM + i * 16 + 4 * g4, wn * kWaveN + j * 16 + r16, val);
+          if (ti != tj)
+            stage_tile_put(lds, wm * kWaveM + i * 16 + 4 * g4, wn * kWaveN + j * 16 + r16, val);
+          else
+            stage_tile_put_sym(lds, wm * kWaveM + i * 16 + 4 * g4, wn * kWaveN + j * 16 + r16, val);
           acc[i][j] = val;  // kept for the mirror tile
-        } else {
+        } else if (ti != tj) {
 #pragma unroll
           for (int v = 0; v < 4; ++v) WsType<T>::st(out, (row + v) * mp + col, val[v]);
-          if (ti != tj) Vec4<T>::st(out + col * mp + row, val);
+          Vec4<T>::st(out + col * mp + row, val);
+        } else {  // diagonal tile: upper triangle and its mirror, as above
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            if (col >= row + v) WsType<T>::st(out, (row + v) * mp + col, val[v]);
+            if (col > row + v) WsType<T>::st(out, col * mp + row + v, val[v]);
+          }
         }
       }
     }

@@ -89,7 +89,7 @@ int validate_config(const dmuon_step_config *cfg) {
   for (float v : vals)
     if (!std::isfinite(v)) return fail(DMUON_ERR_INVALID_ARG, "non-finite step coefficient");
   if (cfg->eps < 0.f) return fail(DMUON_ERR_INVALID_ARG, "eps < 0");
-  const uint32_t known = DMUON_FLAG_NS_FP32 | DMUON_FLAG_NESTEROV;
+  const uint32_t known = DMUON_FLAG_NS_FP32 | DMUON_FLAG_NESTEROV | DMUON_FLAG_GRAM_NS;
   if (cfg->flags & ~known) return fail(DMUON_ERR_INVALID_ARG, "unknown flag bits 0x%x", cfg->flags & ~known);
   return DMUON_OK;
 }
@@ -121,13 +121,54 @@ int validate_shapes(const dmuon_matrix *mats, int32_t n) {
 }
 
 // ------------------------------------------------------------------- plan --
+// Launch kinds, in the order of the DMUON_LAUNCH_* codes of the C ABI.
+enum LaunchKind : int32_t {
+  kLkMomentumSumsq = DMUON_LAUNCH_MOMENTUM_SUMSQ,
+  kLkMomentumOrient = DMUON_LAUNCH_MOMENTUM_ORIENT,
+  kLkNorm = DMUON_LAUNCH_NORM,
+  kLkUpdateDirect = DMUON_LAUNCH_UPDATE_DIRECT,
+  kLkGram = DMUON_LAUNCH_GRAM,
+  kLkSquare = DMUON_LAUNCH_SQUARE,
+  kLkApply = DMUON_LAUNCH_APPLY,
+  kLkFinal = DMUON_LAUNCH_FINAL
+};
+
+// Workspace buffers a GEMM launch can name per matrix: the direct chain uses
+// A and B; the Gram-space chain also A', T, Q0, Q1 (m_p x m_p each).
+enum Buf : int32_t { kBufNone = -1, kBufA = 0, kBufB, kBufA1, kBufT, kBufQ0, kBufQ1, kBufCount };
+
+// Which buffer each MatDev pointer of a grouped launch names, for every
+// matrix of the group: a (Gram output, Square L), b (Square output, Apply
+// L) and sq_r (Square R).
+struct Recipe {
+  int32_t group, a, b, r;
+  bool operator<(const Recipe &o) const {
+    return group != o.group ? group < o.group : a != o.a ? a < o.a : b != o.b ? b < o.b : r < o.r;
+  }
+};
+
+struct Launch {
+  int32_t kind;
+  int32_t table = 0;  // MatDev table (GEMM launches)
+  int32_t list = 0;   // tile list (GEMM launches)
+  int32_t cur = 0;
+  bool first = false;
+  StepScalars sc{};
+  double flops = 0;   // algorithmic flops (symmetric products: upper triangle)
+};
+
 struct Plan {
-  std::vector<MatDev> mats;
-  std::vector<TileEntry> tiles[3];  // gram, square, apply: XCD lists back to back
-  StageXcd xcd[3];
+  std::vector<MatDev> mats;                  // every matrix: table 0
+  std::vector<std::vector<void *>> extra;    // Gram-space buffers A', T, Q0, Q1 per matrix
+  std::vector<int32_t> groups[2];            // matrix indices: direct chain, Gram-space chain
+  std::vector<Recipe> recipes;               // tables 1..: one per distinct recipe
+  std::vector<std::vector<TileEntry>> lists; // [group * 3 + stage]
+  std::vector<StageXcd> list_xcd;
+  std::vector<Launch> prog;
   int64_t ew_total = 0, tr_total = 0;
   // workspace layout (byte offsets)
-  int64_t off_mats = 0, off_stage[3] = {0, 0, 0}, off_partials = 0, off_inv = 0, off_ns = 0;
+  std::vector<int64_t> off_table, off_list;
+  int64_t off_partials = 0, off_inv = 0;
   int64_t table_bytes = 0;  // [0, table_bytes) is uploaded
   int64_t total_bytes = 0;
 };
@@ -185,18 +226,41 @@ void build_stage_tiles(const std::vector<MatDev> &mats, int st, std::vector<Tile
   }
 }
 
-// Builds the plan; with ws == nullptr only sizes are computed.
 // Work-groups of the momentum / orientation pass for one matrix, 8192
 // elements each: a tall matrix (its own X^T) in contiguous 8192-element
 // runs, otherwise 64 x 128 blocks of X.  One sum-of-squares partial each.
 int64_t orient_groups(const MatDev &d) { return (d.mp / kTrTile) * (d.np / kTrTile) / 2; }
 
+// A matrix takes the Gram-space chain when asked for, with at least two
+// iterations (one is the same product either way) and n >= 2m: the m x m
+// chain then costs fewer flops than K direct iterations, and the iterate's
+// singular values stay within a factor (sqrt(n)+sqrt(m))/(sqrt(n)-sqrt(m))
+// < 6 of each other for Gaussian-like inputs, which keeps bf16 storage of
+// the accumulated polynomial Q accurate.
+bool uses_gram(const MatDev &d, const dmuon_step_config &cfg) {
+  return (cfg.flags & DMUON_FLAG_GRAM_NS) && cfg.ns_steps >= 2 && d.n >= 2 * d.m;
+}
+
+// Phases of the Gram-space chain: at most 3 iterations each, as even as
+// possible, longer ones first (5 -> 3 + 2, 8 -> 3 + 3 + 2).  Each phase
+// starts from an explicit X (a fresh A = X X^T) and ends with X <- Q X.
+std::vector<int> gram_phases(int K) {
+  const int np = (K + 2) / 3, base = K / np, extra = K % np;
+  std::vector<int> L(np, base);
+  for (int i = 0; i < extra; ++i) ++L[i];
+  return L;
+}
+
+// Builds the plan; with ws == nullptr only sizes are computed.
 void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg, char *ws,
                 Plan &p) {
   const bool fp32 = cfg.flags & DMUON_FLAG_NS_FP32;
   const int64_t es = fp32 ? 4 : 2;
   const int K = cfg.ns_steps;
   p.mats.resize(n);
+  p.extra.assign(n, {});
+  p.groups[0].clear();
+  p.groups[1].clear();
   int64_t ew = 0, tr = 0;
   for (int32_t i = 0; i < n; ++i) {
     const dmuon_matrix &s = in[i];
@@ -223,33 +287,132 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
     ew += d.ew_count;
     d.tr_first = tr;
     tr += orient_groups(d);
+    if (K > 0) p.groups[uses_gram(d, cfg) ? 1 : 0].push_back(i);
   }
   p.ew_total = ew;
   p.tr_total = K > 0 ? tr : 0;
 
-  for (int st = 0; st < 3; ++st) {
-    if (K > 0) {
-      build_stage_tiles(p.mats, st, p.tiles[st], p.xcd[st]);
-    } else {
-      p.tiles[st].clear();
-      std::memset(&p.xcd[st], 0, sizeof(StageXcd));
+  // ---- the launch program ----
+  const StepScalars step_sc{cfg.a, cfg.b, cfg.c, cfg.lr, cfg.momentum, cfg.eps,
+                            (cfg.flags & DMUON_FLAG_NESTEROV) ? 1 : 0, 0.f};
+  p.recipes.clear();
+  p.prog.clear();
+  std::map<Recipe, int32_t> table_of;
+  auto table = [&](Recipe r) {
+    auto it = table_of.find(r);
+    if (it != table_of.end()) return it->second;
+    const int32_t t = 1 + static_cast<int32_t>(p.recipes.size());
+    p.recipes.push_back(r);
+    table_of[r] = t;
+    return t;
+  };
+  // algorithmic flops of one stage over a group
+  auto flops = [&](int g, int32_t kind) {
+    double f = 0;
+    for (int32_t i : p.groups[g]) {
+      const double m = static_cast<double>(p.mats[i].m), nn = static_cast<double>(p.mats[i].n);
+      f += kind == kLkGram ? m * (m + 1) * nn : kind == kLkSquare ? m * m * (m + 1) : 2 * m * m * nn;
+    }
+    return f;
+  };
+  auto gemm = [&](int32_t kind, int g, Recipe r, int cur, bool first, StepScalars sc) {
+    Launch l;
+    l.kind = kind;
+    l.table = table(r);
+    l.list = g * 3 + (kind == kLkGram ? 0 : kind == kLkSquare ? 1 : 2);
+    l.cur = cur;
+    l.first = first;
+    l.sc = sc;
+    l.flops = flops(g, kind);
+    p.prog.push_back(l);
+  };
+  if (K == 0) {
+    p.prog.push_back(Launch{kLkMomentumSumsq});
+    p.prog.push_back(Launch{kLkNorm});
+    p.prog.push_back(Launch{kLkUpdateDirect});
+  } else {
+    p.prog.push_back(Launch{kLkMomentumOrient});
+    p.prog.push_back(Launch{kLkNorm});
+    // direct chain: K x (A = X X^T; B = b A + c A A; X <- a X + B X)
+    if (!p.groups[0].empty()) {
+      const Recipe r{0, kBufA, kBufB, kBufNone};
+      for (int k = 0; k < K; ++k) {
+        gemm(kLkGram, 0, r, k & 1, k == 0, step_sc);
+        gemm(kLkSquare, 0, r, k & 1, k == 0, step_sc);
+        gemm(k + 1 == K ? kLkFinal : kLkApply, 0, r, k & 1, k == 0, step_sc);
+      }
+    }
+    // Gram-space chain, per phase of L iterations from X:
+    //   A = X X^T; Q = I
+    //   L times: P = a I + b A + c A A;  A <- A P P (not after the last);  Q <- Q P
+    //   X <- Q X   (the step's last phase: the update instead)
+    // A, P, Q are polynomials in the phase's first A, so every product is of
+    // commuting symmetric matrices: upper tiles + mirror.  P of the first
+    // iteration is written to Q0 and is Q.
+    if (!p.groups[1].empty()) {
+      StepScalars poly = step_sc;  // P = a I + b A + c A A
+      poly.diag = cfg.a;
+      StepScalars prod = step_sc;  // plain product
+      prod.b = 0.f;
+      prod.c = 1.f;
+      StepScalars apply = step_sc;  // X <- Q X: no a X term
+      apply.a = 0.f;
+      const std::vector<int> phases = gram_phases(K);
+      int cur = 0;
+      for (size_t ph = 0; ph < phases.size(); ++ph) {
+        const bool first = ph == 0, last_phase = ph + 1 == phases.size();
+        gemm(kLkGram, 1, Recipe{1, kBufA, kBufB, kBufNone}, cur, first, step_sc);
+        int32_t acur = kBufA, anext = kBufA1, qcur = kBufQ0;
+        for (int i = 0; i < phases[ph]; ++i) {
+          const int32_t pbuf = i == 0 ? kBufQ0 : kBufB;
+          gemm(kLkSquare, 1, Recipe{1, acur, pbuf, kBufNone}, cur, false, poly);
+          if (i + 1 < phases[ph]) {
+            gemm(kLkSquare, 1, Recipe{1, pbuf, kBufT, kBufNone}, cur, false, prod);  // T = P P
+            gemm(kLkSquare, 1, Recipe{1, acur, anext, kBufT}, cur, false, prod);     // A T
+            std::swap(acur, anext);
+          }
+          if (i > 0) {
+            const int32_t qnext = qcur == kBufQ0 ? kBufQ1 : kBufQ0;
+            gemm(kLkSquare, 1, Recipe{1, qcur, qnext, pbuf}, cur, false, prod);      // Q P
+            qcur = qnext;
+          }
+        }
+        gemm(last_phase ? kLkFinal : kLkApply, 1, Recipe{1, kBufA, qcur, kBufNone}, cur, first, apply);
+        cur ^= 1;
+      }
     }
   }
 
-  // workspace layout
+  // ---- tile lists: per group, Gram / Square / Apply ----
+  p.lists.assign(6, {});
+  p.list_xcd.assign(6, StageXcd{});
+  std::vector<MatDev> gm;
+  for (int g = 0; g < 2; ++g) {
+    if (p.groups[g].empty()) continue;
+    gm.clear();
+    for (int32_t i : p.groups[g]) gm.push_back(p.mats[i]);
+    for (int st = 0; st < 3; ++st) build_stage_tiles(gm, st, p.lists[g * 3 + st], p.list_xcd[g * 3 + st]);
+  }
+
+  // ---- workspace layout ----
   int64_t off = 0;
-  p.off_mats = off;
-  off = round_up(off + int64_t(sizeof(MatDev)) * n, 256);
-  for (int st = 0; st < 3; ++st) {
-    p.off_stage[st] = off;
-    off = round_up(off + int64_t(sizeof(TileEntry)) * static_cast<int64_t>(p.tiles[st].size()), 256);
+  const size_t ntab = 1 + p.recipes.size();
+  p.off_table.assign(ntab, 0);
+  for (size_t t = 0; t < ntab; ++t) {
+    p.off_table[t] = off;
+    const int64_t cnt = t == 0 ? n : static_cast<int64_t>(p.groups[p.recipes[t - 1].group].size());
+    off = round_up(off + int64_t(sizeof(MatDev)) * cnt, 256);
+  }
+  p.off_list.assign(p.lists.size(), 0);
+  for (size_t l = 0; l < p.lists.size(); ++l) {
+    p.off_list[l] = off;
+    off = round_up(off + int64_t(sizeof(TileEntry)) * static_cast<int64_t>(p.lists[l].size()), 256);
   }
   p.table_bytes = off;
   p.off_partials = off;
   off = round_up(off + 8 * (K > 0 ? tr : ew), 256);
   p.off_inv = off;
   off = round_up(off + 256 * int64_t(n), 256);  // one 256-byte slot per matrix
-  p.off_ns = off;
   for (int32_t i = 0; i < n; ++i) {
     MatDev &d = p.mats[i];
     // sum-of-squares partials: one per orientation tile, or per flat chunk
@@ -270,8 +433,37 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
     off = round_up(off + ab, 256);
     d.b = ws ? ws + off : nullptr;
     off = round_up(off + ab, 256);
+    if (uses_gram(d, cfg)) {
+      p.extra[i].resize(4);
+      for (int b = 0; b < 4; ++b) {
+        p.extra[i][b] = ws ? ws + off : nullptr;
+        off = round_up(off + ab, 256);
+      }
+    }
   }
   p.total_bytes = off;
+}
+
+// The MatDev array of table t (0: every matrix; else a recipe over its
+// group, in group order, with a / b / sq_r pointing at the named buffers).
+std::vector<MatDev> table_contents(const Plan &p, size_t t) {
+  if (t == 0) return p.mats;
+  const Recipe &r = p.recipes[t - 1];
+  std::vector<MatDev> out;
+  for (int32_t i : p.groups[r.group]) {
+    MatDev d = p.mats[i];
+    auto buf = [&](int32_t b) -> void * {
+      if (b == kBufNone) return nullptr;
+      if (b == kBufA) return p.mats[i].a;
+      if (b == kBufB) return p.mats[i].b;
+      return p.extra[i][b - kBufA1];
+    };
+    d.a = buf(r.a);
+    d.b = buf(r.b);
+    d.sq_r = buf(r.r);
+    out.push_back(d);
+  }
+  return out;
 }
 
 // ------------------------------------------------- pinned staging uploads --
@@ -497,21 +689,22 @@ static int muon_step_impl(const dmuon_matrix *mats, int32_t n, const dmuon_step_
     for (int32_t i = 0; i < n; ++i)
       p.mats[i].packed = static_cast<char *>(packed) + mats[i].packed_offset * elem_size(packed_dtype);
   std::vector<char> tables(static_cast<size_t>(p.table_bytes), 0);
-  std::memcpy(tables.data() + p.off_mats, p.mats.data(), sizeof(MatDev) * n);
-  for (int st = 0; st < 3; ++st)
-    if (!p.tiles[st].empty())
-      std::memcpy(tables.data() + p.off_stage[st], p.tiles[st].data(),
-                  sizeof(TileEntry) * p.tiles[st].size());
+  for (size_t t = 0; t < p.off_table.size(); ++t) {
+    const std::vector<MatDev> tab = table_contents(p, t);
+    if (!tab.empty()) std::memcpy(tables.data() + p.off_table[t], tab.data(), sizeof(MatDev) * tab.size());
+  }
+  for (size_t l = 0; l < p.lists.size(); ++l)
+    if (!p.lists[l].empty())
+      std::memcpy(tables.data() + p.off_list[l], p.lists[l].data(), sizeof(TileEntry) * p.lists[l].size());
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   rc = upload(ws, tables, s);
   if (rc) return rc;
 
-  const MatDev *dm = reinterpret_cast<const MatDev *>(ws + p.off_mats);
-  const TileEntry *dst[3];
-  for (int st = 0; st < 3; ++st) dst[st] = reinterpret_cast<const TileEntry *>(ws + p.off_stage[st]);
-  StepScalars sc{cfg->a, cfg->b, cfg->c, cfg->lr, cfg->momentum, cfg->eps,
-                 (cfg->flags & DMUON_FLAG_NESTEROV) ? 1 : 0, 0};
+  auto dtab = [&](int32_t t) { return reinterpret_cast<const MatDev *>(ws + p.off_table[t]); };
+  const MatDev *dm = dtab(0);
+  const StepScalars sc{cfg->a, cfg->b, cfg->c, cfg->lr, cfg->momentum, cfg->eps,
+                       (cfg->flags & DMUON_FLAG_NESTEROV) ? 1 : 0, 0.f};
   const bool fp32 = cfg->flags & DMUON_FLAG_NS_FP32;
 
   // events[0] before the first launch, events[j] after launch j
@@ -530,29 +723,58 @@ static int muon_step_impl(const dmuon_matrix *mats, int32_t n, const dmuon_step_
   };
 
   if ((rc = mark())) return rc;
-  if (cfg->ns_steps == 0) {
-    if ((rc = launched(launch_momentum_sumsq(dm, n, p.ew_total, sc, s), "momentum_sumsq launch")))
-      return rc;
-    if ((rc = launched(launch_finalize_norm(dm, n, cfg->eps, s), "finalize_norm launch"))) return rc;
-    return launched(launch_update_direct(dm, n, p.ew_total, sc, s), "update_direct launch");
+  for (const Launch &l : p.prog) {
+    switch (l.kind) {
+      case kLkMomentumSumsq:
+        rc = launched(launch_momentum_sumsq(dm, n, p.ew_total, sc, s), "momentum_sumsq launch");
+        break;
+      case kLkMomentumOrient:
+        rc = launched(launch_momentum_orient(dm, n, p.tr_total, sc, fp32, s), "momentum_orient launch");
+        break;
+      case kLkNorm:
+        rc = launched(launch_finalize_norm(dm, n, cfg->eps, s), "finalize_norm launch");
+        break;
+      case kLkUpdateDirect:
+        rc = launched(launch_update_direct(dm, n, p.ew_total, sc, s), "update_direct launch");
+        break;
+      default: {
+        const GemmMode mode = l.kind == kLkGram     ? kModeGram
+                              : l.kind == kLkSquare ? kModeSquare
+                              : l.kind == kLkApply  ? kModeApply
+                                                    : kModeFinal;
+        const TileEntry *tl = reinterpret_cast<const TileEntry *>(ws + p.off_list[l.list]);
+        rc = launched(launch_ns_stage(mode, fp32, dtab(l.table), tl, p.list_xcd[l.list], l.cur, l.first,
+                                      l.sc, s),
+                      "Newton-Schulz stage launch");
+      }
+    }
+    if (rc) return rc;
   }
-  if ((rc = launched(launch_momentum_orient(dm, n, p.tr_total, sc, fp32, s),
-                     "momentum_orient launch")))
-    return rc;
-  if ((rc = launched(launch_finalize_norm(dm, n, cfg->eps, s), "finalize_norm launch"))) return rc;
-  for (int k = 0; k < cfg->ns_steps; ++k) {
-    const int32_t cur = k & 1;
-    const bool last = k + 1 == cfg->ns_steps, first = k == 0;
-    if ((rc = launched(launch_ns_stage(kModeGram, fp32, dm, dst[0], p.xcd[0], cur, first, sc, s),
-                       "gram launch")))
-      return rc;
-    if ((rc = launched(launch_ns_stage(kModeSquare, fp32, dm, dst[1], p.xcd[1], cur, first, sc, s),
-                       "square launch")))
-      return rc;
-    if ((rc = launched(launch_ns_stage(last ? kModeFinal : kModeApply, fp32, dm, dst[2], p.xcd[2],
-                                       cur, first, sc, s),
-                       "apply launch")))
-      return rc;
+  return DMUON_OK;
+}
+
+int dmuon_step_launches(const dmuon_matrix *mats, int32_t n, const dmuon_step_config *cfg,
+                        dmuon_launch_info *out, int32_t cap, int32_t *count) {
+  g_last_error.clear();
+  if (!count) return fail(DMUON_ERR_INVALID_ARG, "count is NULL");
+  if (cap < 0 || (cap > 0 && !out)) return fail(DMUON_ERR_INVALID_ARG, "bad output array");
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  rc = validate_shapes(mats, n);
+  if (rc) return rc;
+  rc = validate_step_shapes(mats, n);
+  if (rc) return rc;
+  if (n == 0) {
+    *count = 0;
+    return DMUON_OK;
+  }
+  Plan p;
+  build_plan(mats, n, *cfg, nullptr, p);
+  *count = static_cast<int32_t>(p.prog.size());
+  for (int32_t j = 0; j < cap && j < *count; ++j) {
+    out[j].kind = p.prog[j].kind;
+    out[j].reserved = 0;
+    out[j].flops = p.prog[j].flops;
   }
   return DMUON_OK;
 }

@@ -33,8 +33,9 @@ struct MatDev {
   void *packed;     // nullable: this matrix's slot of the packed param buffer
   // workspace memory (element type bf16, or fp32 in the fp32 mode)
   void *xt[2];      // X^T, n_p x m_p, row-major: the iterate, ping-pong
-  void *a;          // m_p x m_p: A = X X^T
-  void *b;          // m_p x m_p: B = b A + c A A
+  void *a;          // m_p x m_p: A = X X^T (Gram output, Square's L operand)
+  void *b;          // m_p x m_p: B = b A + c A A (Square output, Apply's L operand)
+  const void *sq_r; // Square's R operand; nullptr: R = a (the product A A)
   double *partials; // sum of U^2 per flat chunk (ns_steps = 0) or per
                     // 8192-element momentum-pass group (ns_steps >= 1)
   float *inv_norm;  // one float: 1 / (||U||_F + eps)
@@ -70,12 +71,14 @@ struct StepScalars {
   float a, b, c;
   float lr, mu, eps;
   int32_t nesterov;
-  int32_t pad_;
+  float diag;  // Square only: added to the diagonal (rows < m) of its output
 };
 
 enum GemmMode : int32_t {
   kModeGram = 0,    // C = X X^T (upper tiles, mirrored)        -> A
-  kModeSquare = 1,  // C = b A + c A A^T (upper tiles, mirrored) -> B
+  kModeSquare = 1,  // C = b A + c A R^T + diag I (upper tiles, mirrored) -> B;
+                    // R = A unless sq_r is set (then b = 0: a product of two
+                    // commuting symmetric matrices, itself symmetric)
   kModeApply = 2,   // C = a X + B X                             -> X', X'^T
   kModeFinal = 3    // last apply: P -= lr*scale*C, orth <- C
 };

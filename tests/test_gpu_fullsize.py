@@ -83,8 +83,11 @@ def sample_positions(shapes):
     return pos
 
 
-def test_llama31_8b_owner0_share(nsd):
-    """The benchmark workload: owner 0's 28 matrices of Llama-3.1-8B."""
+@pytest.mark.parametrize("gram_ns", [False, True])
+def test_llama31_8b_owner0_share(nsd, gram_ns):
+    """The benchmark workload: owner 0's 28 matrices of Llama-3.1-8B, with the
+    direct chain and with the Gram-space chain (k, gate, up and down take it;
+    q keeps the direct one)."""
     from synth import workload
     w = workload(4)
     numels = [r * c for _, r, c in w.shapes]
@@ -96,15 +99,16 @@ def test_llama31_8b_owner0_share(nsd):
         if (r, c) not in seen:
             seen.add((r, c)); sample.add(pos)
     assert len(sample) == 4   # q, k, gate/up (tall), down (wide)
-    say("llama-3.1-8b owner 0: 28 matrices")
-    opts = nsd.StepOptions()
+    say(f"llama-3.1-8b owner 0: 28 matrices, gram_ns {gram_ns}")
+    opts = nsd.StepOptions(gram_ns=gram_ns)
     case, gpu = run_set(nsd, w, shapes, sample, opts)
     err = check_step(case, opts, gpu, case.run_oracle(opts))
     say(f"  worst O rel err {err:.3e}")
 
 
-@pytest.mark.parametrize("wid,k_values", [(3, (5,)), (5, (3, 5, 8))])
-def test_full_model_sets(nsd, wid, k_values):
+@pytest.mark.parametrize("wid,k_values,gram_ns", [(3, (5,), False), (5, (3, 5, 8), False),
+                                                  (3, (5,), True), (5, (3, 5, 8), True)])
+def test_full_model_sets(nsd, wid, k_values, gram_ns):
     """All 28 layers of Llama-3.2-3B and Qwen2.5-7B (196 matrices) in one step;
     sampled matrices of the first and last layer checked.  The sweep over
     ns_steps checks the small shapes at every K and every shape at K = 5."""
@@ -117,8 +121,8 @@ def test_full_model_sets(nsd, wid, k_values):
         sample = {p for p in pos if k == 5 or shapes[p][2] * shapes[p][3] <= 4096 * 4096}
         if k == 5 and wid == 5:
             sample = {p for p in pos if int(shapes[p][1].split(".")[1]) == 0}
-        say(f"{w.name}: {len(shapes)} matrices, ns_steps {k}, {len(sample)} checked")
-        opts = nsd.StepOptions(ns_steps=k)
+        say(f"{w.name}: {len(shapes)} matrices, ns_steps {k}, gram_ns {gram_ns}, {len(sample)} checked")
+        opts = nsd.StepOptions(ns_steps=k, gram_ns=gram_ns)
         case, gpu = run_set(nsd, w, shapes, sample, opts)
         err = check_step(case, opts, gpu, case.run_oracle(opts))
         say(f"  worst O rel err {err:.3e}")

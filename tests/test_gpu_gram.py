@@ -1,0 +1,136 @@
+"""GPU parity of the Gram-space Newton-Schulz chain (DMUON_FLAG_GRAM_NS)
+against the fp64 oracle of the direct iteration.
+
+The Gram-space chain computes the same X_K in exact arithmetic (every
+iterate is a polynomial in the first A = X X^T); the bars are the direct
+chain's: <= 2e-2 relative Frobenius for the bf16 chain up to 5 iterations,
+the 6-8 iteration bar above that, <= 1e-4 in the fp32 checking mode.
+Matrices with max(r, c) >= 2 min(r, c) take it; the others of the same call
+keep the direct chain.
+"""
+
+import numpy as np
+import pytest
+
+from _gpu_util import Case, check_step, say
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def nsd():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import newton_schulz_dmuon_amd as m
+    m.load()
+    return m
+
+
+WIDE = [
+    (128, 256),     # aspect exactly 2: one tile each way
+    (300, 700),     # ragged both ways, 2 x 3 tiles
+    (700, 300),     # tall: transposed
+    (257, 1000),    # one row past a tile boundary
+    (1000, 257),
+    (100, 1000),    # aspect 10
+    (17, 100),
+    (1, 300),       # m = 1: A is 1 x 1
+    (300, 1),
+    (520, 1100),    # 3 x 5 tiles
+]
+
+
+def _kinds(nsd, shapes, opts):
+    return [k for k, _ in nsd.step_launches(shapes, opts)]
+
+
+@pytest.mark.parametrize("shape", WIDE)
+def test_gram_single_matrix_bf16(nsd, shape):
+    say(f"gram bf16 step {shape}")
+    opts = nsd.StepOptions(gram_ns=True)
+    kinds = _kinds(nsd, [shape], opts)
+    assert kinds.count("gram") == 2 and kinds.count("square") == 14   # phases 3 + 2
+    case = Case([shape], "bf16", "bf16", seed=31, m_std=1e-3)
+    err = check_step(case, opts, case.run_gpu(opts), case.run_oracle(opts))
+    say(f"  O rel err {err:.3e}")
+
+
+@pytest.mark.parametrize("k", [2, 3, 4, 5, 6, 8])
+def test_gram_ns_steps(nsd, k):
+    """Every phase split: 2, 3 (one phase), 2+2, 3+2, 3+3, 3+3+2."""
+    say(f"gram ns_steps {k}")
+    shapes = [(300, 700), (1000, 257), (17, 100)]
+    case = Case(shapes, "bf16", "bf16", seed=40 + k, m_std=1e-3)
+    opts = nsd.StepOptions(ns_steps=k, gram_ns=True)
+    err = check_step(case, opts, case.run_gpu(opts), case.run_oracle(opts))
+    say(f"  worst O rel err {err:.3e}")
+
+
+@pytest.mark.parametrize("shape", [(128, 256), (300, 700), (700, 300), (100, 1000), (1, 300)])
+def test_gram_fp32_mode(nsd, shape):
+    say(f"gram fp32-mode step {shape}")
+    case = Case([shape], "f32", "f32", seed=32, g_std=1.0, m_std=0.5)
+    opts = nsd.StepOptions(ns_fp32=True, gram_ns=True)
+    err = check_step(case, opts, case.run_gpu(opts), case.run_oracle(opts))
+    say(f"  O rel err {err:.3e}")
+
+
+def test_gram_mixed_with_direct_chain(nsd):
+    """One call whose square and near-square matrices keep the direct chain
+    while the wide and tall ones take the Gram-space chain; twice, bitwise
+    equal (deterministic)."""
+    shapes = [(513, 513), (300, 700), (300, 500), (700, 300), (17, 33), (1, 1), (256, 1024),
+              (1024, 256), (64, 64), (129, 900)]
+    opts = nsd.StepOptions(gram_ns=True)
+    kinds = _kinds(nsd, shapes, opts)
+    assert kinds.count("final") == 2   # one per chain
+    case = Case(shapes, "bf16", "bf16", seed=33, m_std=1e-3)
+    a = case.run_gpu(opts)
+    err = check_step(case, opts, a, case.run_oracle(opts))
+    say(f"  worst O rel err {err:.3e}")
+    b = case.run_gpu(opts)
+    for x, y in zip(a, b):
+        for u, v in zip(x, y):
+            assert np.array_equal(u, v)
+
+
+def test_gram_cubic_and_custom_coefficients(nsd):
+    """c = 0 (the cubic): the P = aI + bA + cA^2 epilogue reads A instead
+    of the captured R tile.  Also fp32 params with bf16 grads."""
+    for coef, k in (((1.5, -0.5, 0.0), 8), ((3.0, -3.2, 1.2), 5)):
+        say(f"gram coefficients {coef}, ns_steps {k}")
+        case = Case([(300, 700), (700, 300)], "f32", "bf16", seed=34, m_std=1e-3)
+        opts = nsd.StepOptions(a=coef[0], b=coef[1], c=coef[2], ns_steps=k, gram_ns=True)
+        err = check_step(case, opts, case.run_gpu(opts), case.run_oracle(opts))
+        say(f"  worst O rel err {err:.3e}")
+
+
+def test_gram_packed_step_matches_step_plus_pack(nsd):
+    """dmuon_muon_step_packed with the Gram-space chain equals
+    dmuon_muon_step + dmuon_pack bit for bit."""
+    from oracle import partition as refp
+    from _gpu_util import to_dev
+    shapes = [(300, 700), (700, 300), (513, 513)]
+    case = Case(shapes, "bf16", "bf16", seed=35, m_std=1e-3)
+    offs, total = refp.pack_offsets([r * c for r, c in shapes], 128)
+    opts = nsd.StepOptions(gram_ns=True)
+    outs = []
+    for packed_step in (False, True):
+        P = [to_dev(p, "bf16") for p in case.P]
+        G = [to_dev(g, "bf16") for g in case.G]
+        M = [to_dev(m, "f32") for m in case.M]
+        buf = torch.zeros(total, dtype=torch.bfloat16, device="cuda")
+        if packed_step:
+            nsd.muon_step(P, G, M, case.scales, opts, packed=buf, packed_offsets=offs)
+        else:
+            nsd.muon_step(P, G, M, case.scales, opts)
+            nsd.pack(P, offs, buf)
+        torch.cuda.synchronize()
+        outs.append((P, buf))
+    for p0, p1 in zip(outs[0][0], outs[1][0]):
+        assert torch.equal(p0.view(torch.int16), p1.view(torch.int16))
+    for o, (r, c) in zip(offs, shapes):
+        assert torch.equal(outs[0][1][o:o + r * c].view(torch.int16),
+                           outs[1][1][o:o + r * c].view(torch.int16))

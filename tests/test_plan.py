@@ -1,0 +1,104 @@
+"""Host-side launch plan of the step (dmuon_step_launches), no GPU: which
+matrices take the Gram-space chain, its phase split, the launch sequence
+and the algorithmic flop count of every launch."""
+
+import ctypes
+import math
+
+import pytest
+
+nsd = pytest.importorskip("newton_schulz_dmuon_amd")
+from newton_schulz_dmuon_amd import _lib  # noqa: E402
+
+LLAMA8B_OWNER0 = [(4096, 4096)] * 8 + [(1024, 4096)] * 8 + [(14336, 4096)] * 8 + \
+    [(4096, 14336)] * 4
+
+
+def direct_flops(m, n, k):
+    return k * (m * (m + 1) * n + m * m * (m + 1) + 2 * m * m * n)
+
+
+def phases(k):
+    n = math.ceil(k / 3)
+    return [k // n + (1 if i < k % n else 0) for i in range(n)]
+
+
+def gram_flops(m, n, k):
+    ph = phases(k)
+    return len(ph) * (m * (m + 1) * n + 2 * m * m * n) + sum(4 * L - 3 for L in ph) * m * m * (m + 1)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 6, 7, 8, 10])
+def test_phase_split(k):
+    ph = phases(k)
+    assert sum(ph) == k and max(ph) <= 3 and max(ph) - min(ph) <= 1 and ph == sorted(ph, reverse=True)
+    kinds = [kd for kd, _ in nsd.step_launches([(256, 1024)], nsd.StepOptions(ns_steps=k, gram_ns=True))]
+    assert kinds[:2] == ["momentum_orient", "norm"] and kinds[-1] == "final"
+    if k == 1:   # one iteration is the same product either way: direct chain
+        assert kinds[2:] == ["gram", "square", "final"]
+        return
+    assert kinds.count("gram") == len(ph)
+    assert kinds.count("apply") == len(ph) - 1
+    assert kinds.count("square") == sum(4 * L - 3 for L in ph)
+
+
+def test_direct_chain_sequence_and_flops():
+    L = nsd.step_launches(LLAMA8B_OWNER0, nsd.StepOptions())
+    kinds = [k for k, _ in L]
+    assert kinds == ["momentum_orient", "norm"] + ["gram", "square", "apply"] * 4 + \
+        ["gram", "square", "final"]
+    total = sum(f for _, f in L)
+    want = sum(direct_flops(min(r, c), max(r, c), 5) for r, c in LLAMA8B_OWNER0)
+    assert total == want
+    assert abs(total - 58.98e12) < 0.01e12
+
+
+def test_gram_chain_selection_and_flops():
+    shapes = LLAMA8B_OWNER0 + [(300, 599), (300, 600), (601, 300), (1, 1)]
+    L = nsd.step_launches(shapes, nsd.StepOptions(gram_ns=True))
+    total = sum(f for _, f in L)
+    want = 0
+    for r, c in shapes:
+        m, n = min(r, c), max(r, c)
+        want += gram_flops(m, n, 5) if n >= 2 * m else direct_flops(m, n, 5)
+    assert total == want
+    # the direct group's launches come first, then the Gram-space group's
+    kinds = [k for k, _ in L]
+    assert kinds.count("final") == 2
+    assert kinds[2:17] == ["gram", "square", "apply"] * 4 + ["gram", "square", "final"]
+
+
+def test_gram_needs_more_workspace():
+    def ws(opts, shapes):
+        arr = (_lib.Matrix * len(shapes))()
+        for i, (r, c) in enumerate(shapes):
+            arr[i] = _lib.Matrix(None, 0, 0, None, None, None, r, c, 1.0, 0, 0)
+        out = ctypes.c_size_t(0)
+        cfg = opts.to_c()
+        _lib.check(_lib.load().dmuon_workspace_bytes(arr, len(shapes), ctypes.byref(cfg),
+                                                     ctypes.byref(out)))
+        return out.value
+    for shapes, extra in (([(300, 700)], 4 * 512 * 512 * 2), ([(300, 500)], 0),
+                          ([(513, 513)], 0)):
+        # four more m_p x m_p buffers per Gram-space matrix, plus its launch tables
+        d = ws(nsd.StepOptions(gram_ns=True), shapes) - ws(nsd.StepOptions(), shapes)
+        assert extra <= d < extra + 65536 and (d == 0) == (extra == 0), (shapes, d)
+
+
+def test_step_launches_errors():
+    lib = _lib.load()
+    arr = (_lib.Matrix * 1)(_lib.Matrix(None, 0, 0, None, None, None, 8, 8, 1.0, 0, 0))
+    cfg = nsd.StepOptions().to_c()
+    cnt = ctypes.c_int32(0)
+    assert lib.dmuon_step_launches(arr, 1, ctypes.byref(cfg), None, 0, None) == _lib.ERR_INVALID_ARG
+    assert lib.dmuon_step_launches(arr, 1, ctypes.byref(cfg), None, 2, ctypes.byref(cnt)) == \
+        _lib.ERR_INVALID_ARG
+    assert lib.dmuon_step_launches(arr, 1, ctypes.byref(cfg), None, 0, ctypes.byref(cnt)) == _lib.OK
+    assert cnt.value == 17
+    bad = _lib.Matrix(None, 0, 0, None, None, None, 0, 8, 1.0, 0, 0)
+    arr2 = (_lib.Matrix * 1)(bad)
+    assert lib.dmuon_step_launches(arr2, 1, ctypes.byref(cfg), None, 0, ctypes.byref(cnt)) == \
+        _lib.ERR_INVALID_ARG
+    out = (_lib.LaunchInfo * 4)()
+    assert lib.dmuon_step_launches(arr, 1, ctypes.byref(cfg), out, 4, ctypes.byref(cnt)) == _lib.OK
+    assert cnt.value == 17 and [out[j].kind for j in range(4)] == [1, 2, 4, 5]
