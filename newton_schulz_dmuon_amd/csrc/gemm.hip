@@ -249,8 +249,7 @@ __device__ __forceinline__ void stage_tile_flush(lds_char *lds, uint16_t *dst, i
 template <typename T, int MODE>
 __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restrict__ mats,
                                                            const TileEntry *__restrict__ tiles,
-                                                           StageXcd xcd, int32_t cur,
-                                                           int32_t first, StepScalars s) {
+                                                           StageXcd xcd, StepScalars s) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * kOperandBytes];  // 128 KB
   // C cast: generic -> LDS address space.  [2 stages][L, R][256 rows][128 B]
   lds_char *const lds = (lds_char *)smem;
@@ -270,7 +269,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   const T *L, *R;
   int64_t ld;  // elements; both operands have the same leading dimension
   if (MODE == kModeGram) {
-    L = R = static_cast<const T *>(d.xt[cur]);
+    L = R = static_cast<const T *>(d.xt[0]);
     ld = d.mp;
   } else if (MODE == kModeSquare) {
     L = static_cast<const T *>(d.a);
@@ -278,7 +277,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
     ld = d.mp;
   } else {
     L = static_cast<const T *>(d.b);
-    R = static_cast<const T *>(d.xt[cur]);
+    R = static_cast<const T *>(d.xt[0]);
     ld = d.mp;
   }
   const int64_t ld_bytes = ld * static_cast<int64_t>(sizeof(T));
@@ -469,9 +468,9 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   // A[row][col] (= A[col][row]); it adds (b/c) A, the epilogue scales by c.
   // With c = 0 (or b/c not finite) it captures nothing and the epilogue
   // reads A instead.
-  const float sq_w = s.c != 0.f ? s.b / s.c : 0.f;
-  const bool sq_cap = MODE == kModeSquare && s.c != 0.f && __builtin_isfinite(sq_w);
-  const float cap_w = MODE == kModeSquare ? (sq_cap ? sq_w : 0.f) : s.a;
+  const float sq_w = d.cc != 0.f ? d.cb / d.cc : 0.f;
+  const bool sq_cap = MODE == kModeSquare && d.cc != 0.f && __builtin_isfinite(sq_w);
+  const float cap_w = MODE == kModeSquare ? (sq_cap ? sq_w : 0.f) : d.ca;
   const int cap_kt0 = ti * (kTile / kKStep) + wm * kCapSteps;
   // Step c of the wave's kCapSteps holds fragment rows [c*kCapFrags,
   // (c+1)*kCapFrags).  Every fragment row reads and adds at every capture
@@ -561,7 +560,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
 
   // The first iteration's X is U unnormalised (X0 = U * inv_norm): A0 picks
   // up inv_norm^2 and the first X' (or O) inv_norm.
-  const float inv = first ? *d.inv_norm : 1.f;
+  const float inv = d.first_it ? *d.inv_norm : 1.f;
   const float gram_scale = inv * inv;
   if (MODE == kModeGram || MODE == kModeSquare) {
     T *out = static_cast<T *>(MODE == kModeGram ? d.a : d.b);
@@ -590,17 +589,17 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
         if (MODE == kModeSquare) {
           if (sq_cap) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v) val[v] = s.c * val[v];  // b A is in the accumulator as (b/c) A
+            for (int v = 0; v < 4; ++v) val[v] = d.cc * val[v];  // b A is in the accumulator as (b/c) A
           } else {
             const f32x4 av = Vec4<T>::cvt(araw[ii][j]);
 #pragma unroll
-            for (int v = 0; v < 4; ++v) val[v] = fmaf(s.b, av[v], s.c * val[v]);
+            for (int v = 0; v < 4; ++v) val[v] = fmaf(d.cb, av[v], d.cc * val[v]);
           }
           // diag I on the true diagonal only: the padding stays zero
           if (ti == tj && col < d.m)
 #pragma unroll
             for (int v = 0; v < 4; ++v)
-              if (row + v == col) val[v] += s.diag;
+              if (row + v == col) val[v] += d.cdiag;
         }
         if constexpr (kStage) {
           if (ti != tj)
@@ -637,7 +636,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
       }
     }
   } else if (MODE == kModeApply) {
-    T *XTn = static_cast<T *>(d.xt[cur ^ 1]);
+    T *XTn = static_cast<T *>(d.xt[1]);
     const int64_t mp = d.mp;
 #pragma unroll
     for (int i = 0; i < kFragM; ++i)
@@ -780,23 +779,23 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
 
 template <typename T>
 hipError_t launch_t(GemmMode mode, const MatDev *mats, const TileEntry *tiles, const StageXcd &xcd,
-                    int32_t cur, int32_t first, StepScalars s, hipStream_t st) {
+                    StepScalars s, hipStream_t st) {
   int32_t longest = 0;
   for (int x = 0; x < kXcds; ++x) longest = xcd.count[x] > longest ? xcd.count[x] : longest;
   if (longest == 0) return hipSuccess;
   const dim3 grid(static_cast<uint32_t>(longest) * kXcds), block(kThreads);
   switch (mode) {
     case kModeGram:
-      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeGram>), grid, block, 0, st, mats, tiles, xcd, cur, first, s);
+      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeGram>), grid, block, 0, st, mats, tiles, xcd, s);
       break;
     case kModeSquare:
-      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeSquare>), grid, block, 0, st, mats, tiles, xcd, cur, first, s);
+      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeSquare>), grid, block, 0, st, mats, tiles, xcd, s);
       break;
     case kModeApply:
-      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeApply>), grid, block, 0, st, mats, tiles, xcd, cur, first, s);
+      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeApply>), grid, block, 0, st, mats, tiles, xcd, s);
       break;
     default:
-      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeFinal>), grid, block, 0, st, mats, tiles, xcd, cur, first, s);
+      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeFinal>), grid, block, 0, st, mats, tiles, xcd, s);
       break;
   }
   return hipGetLastError();
@@ -805,11 +804,9 @@ hipError_t launch_t(GemmMode mode, const MatDev *mats, const TileEntry *tiles, c
 }  // namespace
 
 hipError_t launch_ns_stage(GemmMode mode, bool fp32, const MatDev *mats, const TileEntry *tiles,
-                           const StageXcd &xcd, int32_t cur, bool first, StepScalars s,
-                           hipStream_t st) {
-  const int32_t f = first ? 1 : 0;
-  return fp32 ? launch_t<float>(mode, mats, tiles, xcd, cur, f, s, st)
-              : launch_t<uint16_t>(mode, mats, tiles, xcd, cur, f, s, st);
+                           const StageXcd &xcd, StepScalars s, hipStream_t st) {
+  return fp32 ? launch_t<float>(mode, mats, tiles, xcd, s, st)
+              : launch_t<uint16_t>(mode, mats, tiles, xcd, s, st);
 }
 
 }  // namespace dmuon

@@ -12,6 +12,7 @@
 #include <mutex>
 #include <numeric>
 #include <string>
+#include <tuple>
 #include <vector>
 
 #include "../../include/dmuon.h"
@@ -137,32 +138,32 @@ enum LaunchKind : int32_t {
 // A and B; the Gram-space chain also A', T, Q0, Q1 (m_p x m_p each).
 enum Buf : int32_t { kBufNone = -1, kBufA = 0, kBufB, kBufA1, kBufT, kBufQ0, kBufQ1, kBufCount };
 
-// Which buffer each MatDev pointer of a grouped launch names, for every
-// matrix of the group: a (Gram output, Square L), b (Square output, Apply
-// L) and sq_r (Square R).
-struct Recipe {
-  int32_t group, a, b, r;
-  bool operator<(const Recipe &o) const {
-    return group != o.group ? group < o.group : a != o.a ? a < o.a : b != o.b ? b < o.b : r < o.r;
-  }
+// One part of a grouped GEMM launch: a group of matrices (0 direct chain, 1
+// Gram-space chain) and, for every matrix of it, which buffer each MatDev
+// pointer names (a: Gram output, Square L; b: Square output, Apply L; r:
+// Square R), which X^T buffer is read (cur; the other one is written), and
+// the stage's coefficients.
+struct Part {
+  int32_t group, a, b, r, cur, first;
+  float ca, cb, cc, cdiag;
+  auto key() const { return std::make_tuple(group, a, b, r, cur, first, ca, cb, cc, cdiag); }
+  bool operator<(const Part &o) const { return key() < o.key(); }
 };
 
 struct Launch {
   int32_t kind;
-  int32_t table = 0;  // MatDev table (GEMM launches)
-  int32_t list = 0;   // tile list (GEMM launches)
-  int32_t cur = 0;
-  bool first = false;
-  StepScalars sc{};
-  double flops = 0;   // algorithmic flops (symmetric products: upper triangle)
+  std::vector<Part> parts;  // GEMM launches; all of one kind
+  int32_t table = 0;        // MatDev table: the parts' matrices, in order
+  int32_t list = 0;         // tile list over that table
+  double flops = 0;         // algorithmic flops (symmetric products: upper triangle)
 };
 
 struct Plan {
-  std::vector<MatDev> mats;                  // every matrix: table 0
-  std::vector<std::vector<void *>> extra;    // Gram-space buffers A', T, Q0, Q1 per matrix
-  std::vector<int32_t> groups[2];            // matrix indices: direct chain, Gram-space chain
-  std::vector<Recipe> recipes;               // tables 1..: one per distinct recipe
-  std::vector<std::vector<TileEntry>> lists; // [group * 3 + stage]
+  std::vector<MatDev> mats;                   // every matrix: table 0
+  std::vector<std::vector<void *>> extra;     // Gram-space buffers A', T, Q0, Q1 per matrix
+  std::vector<int32_t> groups[2];             // matrix indices: direct chain, Gram-space chain
+  std::vector<std::vector<Part>> tables;      // tables 1..: the parts of a launch
+  std::vector<std::vector<TileEntry>> lists;
   std::vector<StageXcd> list_xcd;
   std::vector<Launch> prog;
   int64_t ew_total = 0, tr_total = 0;
@@ -293,19 +294,10 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
   p.tr_total = K > 0 ? tr : 0;
 
   // ---- the launch program ----
-  const StepScalars step_sc{cfg.a, cfg.b, cfg.c, cfg.lr, cfg.momentum, cfg.eps,
-                            (cfg.flags & DMUON_FLAG_NESTEROV) ? 1 : 0, 0.f};
-  p.recipes.clear();
+  p.tables.clear();
+  p.lists.clear();
+  p.list_xcd.clear();
   p.prog.clear();
-  std::map<Recipe, int32_t> table_of;
-  auto table = [&](Recipe r) {
-    auto it = table_of.find(r);
-    if (it != table_of.end()) return it->second;
-    const int32_t t = 1 + static_cast<int32_t>(p.recipes.size());
-    p.recipes.push_back(r);
-    table_of[r] = t;
-    return t;
-  };
   // algorithmic flops of one stage over a group
   auto flops = [&](int g, int32_t kind) {
     double f = 0;
@@ -315,17 +307,90 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
     }
     return f;
   };
-  auto gemm = [&](int32_t kind, int g, Recipe r, int cur, bool first, StepScalars sc) {
+  auto gemm = [&](std::vector<Launch> &chain, int32_t kind, std::vector<Part> parts) {
     Launch l;
     l.kind = kind;
-    l.table = table(r);
-    l.list = g * 3 + (kind == kLkGram ? 0 : kind == kLkSquare ? 1 : 2);
-    l.cur = cur;
-    l.first = first;
-    l.sc = sc;
-    l.flops = flops(g, kind);
-    p.prog.push_back(l);
+    l.parts = std::move(parts);
+    for (const Part &pt : l.parts) l.flops += flops(pt.group, kind);
+    chain.push_back(std::move(l));
   };
+  std::vector<Launch> chain[2];
+  if (K > 0 && !p.groups[0].empty()) {
+    // direct chain: K x (A = X X^T; B = b A + c A A; X <- a X + B X)
+    for (int k = 0; k < K; ++k) {
+      const int32_t cur = k & 1, first = k == 0;
+      const Part pt{0, kBufA, kBufB, kBufNone, cur, first, cfg.a, cfg.b, cfg.c, 0.f};
+      gemm(chain[0], kLkGram, {pt});
+      gemm(chain[0], kLkSquare, {pt});
+      gemm(chain[0], k + 1 == K ? kLkFinal : kLkApply, {pt});
+    }
+  }
+  if (K > 0 && !p.groups[1].empty()) {
+    // Gram-space chain, per phase of L iterations from X:
+    //   A = X X^T; Q = I
+    //   L times: P = a I + b A + c A A;  A <- A P P (not after the last);  Q <- Q P
+    //   X <- Q X   (the step's last phase: the update instead)
+    // A, P, Q are polynomials in the phase's first A, so every product is of
+    // commuting symmetric matrices: upper tiles + mirror.  P of the first
+    // iteration is written to Q0 and is Q.  T = P P and Q P both read only
+    // P: one launch.
+    const std::vector<int> phases = gram_phases(K);
+    int32_t cur = 0;
+    for (size_t ph = 0; ph < phases.size(); ++ph) {
+      const int32_t first = ph == 0, last_phase = ph + 1 == phases.size();
+      auto part = [&](int32_t a_, int32_t b_, int32_t r_, float cb, float cc, float cdiag) {
+        return Part{1, a_, b_, r_, cur, 0, 0.f, cb, cc, cdiag};
+      };
+      gemm(chain[1], kLkGram, {Part{1, kBufA, kBufB, kBufNone, cur, first, 0.f, 0.f, 0.f, 0.f}});
+      int32_t acur = kBufA, anext = kBufA1, qcur = kBufQ0;
+      for (int i = 0; i < phases[ph]; ++i) {
+        const int32_t pbuf = i == 0 ? kBufQ0 : kBufB;
+        gemm(chain[1], kLkSquare, {part(acur, pbuf, kBufNone, cfg.b, cfg.c, cfg.a)});  // P
+        std::vector<Part> next;
+        if (i + 1 < phases[ph]) next.push_back(part(pbuf, kBufT, kBufNone, 0.f, 1.f, 0.f));  // T = P P
+        if (i > 0) {
+          const int32_t qnext = qcur == kBufQ0 ? kBufQ1 : kBufQ0;
+          next.push_back(part(qcur, qnext, pbuf, 0.f, 1.f, 0.f));  // Q P
+          qcur = qnext;
+        }
+        if (!next.empty()) gemm(chain[1], kLkSquare, next);
+        if (i + 1 < phases[ph]) {
+          gemm(chain[1], kLkSquare, {part(acur, anext, kBufT, 0.f, 1.f, 0.f)});  // A T
+          std::swap(acur, anext);
+        }
+      }
+      gemm(chain[1], last_phase ? kLkFinal : kLkApply,
+           {Part{1, kBufA, qcur, kBufNone, cur, first, 0.f, 0.f, 0.f, 0.f}});
+      cur ^= 1;
+    }
+  }
+  // The two chains touch disjoint matrices: merge them into one sequence
+  // that keeps each chain's order and runs a launch of each chain of the
+  // same kind as one grouped launch (a longest common subsequence of the
+  // kinds), which fills the chip better than either launch alone.
+  std::vector<Launch> merged;
+  {
+    const size_t n0 = chain[0].size(), n1 = chain[1].size();
+    std::vector<std::vector<int32_t>> lcs(n0 + 1, std::vector<int32_t>(n1 + 1, 0));
+    for (size_t i = n0; i-- > 0;)
+      for (size_t j = n1; j-- > 0;)
+        lcs[i][j] = chain[0][i].kind == chain[1][j].kind ? lcs[i + 1][j + 1] + 1
+                                                         : std::max(lcs[i + 1][j], lcs[i][j + 1]);
+    size_t i = 0, j = 0;
+    while (i < n0 || j < n1) {
+      if (i < n0 && j < n1 && chain[0][i].kind == chain[1][j].kind && lcs[i][j] == lcs[i + 1][j + 1] + 1) {
+        Launch l = chain[0][i];
+        l.parts.insert(l.parts.end(), chain[1][j].parts.begin(), chain[1][j].parts.end());
+        l.flops += chain[1][j].flops;
+        merged.push_back(std::move(l));
+        ++i, ++j;
+      } else if (j >= n1 || (i < n0 && lcs[i + 1][j] >= lcs[i][j + 1])) {
+        merged.push_back(chain[0][i++]);
+      } else {
+        merged.push_back(chain[1][j++]);
+      }
+    }
+  }
   if (K == 0) {
     p.prog.push_back(Launch{kLkMomentumSumsq});
     p.prog.push_back(Launch{kLkNorm});
@@ -333,74 +398,44 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
   } else {
     p.prog.push_back(Launch{kLkMomentumOrient});
     p.prog.push_back(Launch{kLkNorm});
-    // direct chain: K x (A = X X^T; B = b A + c A A; X <- a X + B X)
-    if (!p.groups[0].empty()) {
-      const Recipe r{0, kBufA, kBufB, kBufNone};
-      for (int k = 0; k < K; ++k) {
-        gemm(kLkGram, 0, r, k & 1, k == 0, step_sc);
-        gemm(kLkSquare, 0, r, k & 1, k == 0, step_sc);
-        gemm(k + 1 == K ? kLkFinal : kLkApply, 0, r, k & 1, k == 0, step_sc);
-      }
-    }
-    // Gram-space chain, per phase of L iterations from X:
-    //   A = X X^T; Q = I
-    //   L times: P = a I + b A + c A A;  A <- A P P (not after the last);  Q <- Q P
-    //   X <- Q X   (the step's last phase: the update instead)
-    // A, P, Q are polynomials in the phase's first A, so every product is of
-    // commuting symmetric matrices: upper tiles + mirror.  P of the first
-    // iteration is written to Q0 and is Q.
-    if (!p.groups[1].empty()) {
-      StepScalars poly = step_sc;  // P = a I + b A + c A A
-      poly.diag = cfg.a;
-      StepScalars prod = step_sc;  // plain product
-      prod.b = 0.f;
-      prod.c = 1.f;
-      StepScalars apply = step_sc;  // X <- Q X: no a X term
-      apply.a = 0.f;
-      const std::vector<int> phases = gram_phases(K);
-      int cur = 0;
-      for (size_t ph = 0; ph < phases.size(); ++ph) {
-        const bool first = ph == 0, last_phase = ph + 1 == phases.size();
-        gemm(kLkGram, 1, Recipe{1, kBufA, kBufB, kBufNone}, cur, first, step_sc);
-        int32_t acur = kBufA, anext = kBufA1, qcur = kBufQ0;
-        for (int i = 0; i < phases[ph]; ++i) {
-          const int32_t pbuf = i == 0 ? kBufQ0 : kBufB;
-          gemm(kLkSquare, 1, Recipe{1, acur, pbuf, kBufNone}, cur, false, poly);
-          if (i + 1 < phases[ph]) {
-            gemm(kLkSquare, 1, Recipe{1, pbuf, kBufT, kBufNone}, cur, false, prod);  // T = P P
-            gemm(kLkSquare, 1, Recipe{1, acur, anext, kBufT}, cur, false, prod);     // A T
-            std::swap(acur, anext);
-          }
-          if (i > 0) {
-            const int32_t qnext = qcur == kBufQ0 ? kBufQ1 : kBufQ0;
-            gemm(kLkSquare, 1, Recipe{1, qcur, qnext, pbuf}, cur, false, prod);      // Q P
-            qcur = qnext;
-          }
-        }
-        gemm(last_phase ? kLkFinal : kLkApply, 1, Recipe{1, kBufA, qcur, kBufNone}, cur, first, apply);
-        cur ^= 1;
-      }
-    }
   }
-
-  // ---- tile lists: per group, Gram / Square / Apply ----
-  p.lists.assign(6, {});
-  p.list_xcd.assign(6, StageXcd{});
-  std::vector<MatDev> gm;
-  for (int g = 0; g < 2; ++g) {
-    if (p.groups[g].empty()) continue;
-    gm.clear();
-    for (int32_t i : p.groups[g]) gm.push_back(p.mats[i]);
-    for (int st = 0; st < 3; ++st) build_stage_tiles(gm, st, p.lists[g * 3 + st], p.list_xcd[g * 3 + st]);
+  // tables and tile lists, shared by launches with equal parts / groups
+  std::map<std::vector<Part>, int32_t> table_of;
+  std::map<std::pair<int32_t, std::vector<int32_t>>, int32_t> list_of;
+  for (Launch &l : merged) {
+    auto t = table_of.find(l.parts);
+    if (t == table_of.end()) {
+      t = table_of.emplace(l.parts, 1 + static_cast<int32_t>(p.tables.size())).first;
+      p.tables.push_back(l.parts);
+    }
+    l.table = t->second;
+    const int32_t st = l.kind == kLkGram ? 0 : l.kind == kLkSquare ? 1 : 2;
+    std::vector<int32_t> gs;
+    for (const Part &pt : l.parts) gs.push_back(pt.group);
+    auto key = std::make_pair(st, gs);
+    auto li = list_of.find(key);
+    if (li == list_of.end()) {
+      std::vector<MatDev> shapes;
+      for (int32_t g : gs)
+        for (int32_t i : p.groups[g]) shapes.push_back(p.mats[i]);
+      p.lists.emplace_back();
+      p.list_xcd.emplace_back();
+      build_stage_tiles(shapes, st, p.lists.back(), p.list_xcd.back());
+      li = list_of.emplace(key, static_cast<int32_t>(p.lists.size()) - 1).first;
+    }
+    l.list = li->second;
+    p.prog.push_back(std::move(l));
   }
 
   // ---- workspace layout ----
   int64_t off = 0;
-  const size_t ntab = 1 + p.recipes.size();
+  const size_t ntab = 1 + p.tables.size();
   p.off_table.assign(ntab, 0);
   for (size_t t = 0; t < ntab; ++t) {
     p.off_table[t] = off;
-    const int64_t cnt = t == 0 ? n : static_cast<int64_t>(p.groups[p.recipes[t - 1].group].size());
+    int64_t cnt = t == 0 ? n : 0;
+    if (t > 0)
+      for (const Part &pt : p.tables[t - 1]) cnt += static_cast<int64_t>(p.groups[pt.group].size());
     off = round_up(off + int64_t(sizeof(MatDev)) * cnt, 256);
   }
   p.off_list.assign(p.lists.size(), 0);
@@ -444,24 +479,65 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
   p.total_bytes = off;
 }
 
-// The MatDev array of table t (0: every matrix; else a recipe over its
-// group, in group order, with a / b / sq_r pointing at the named buffers).
+// Internal consistency of a plan, checked on the host before any launch:
+// every tile of every GEMM launch names a matrix of that launch's table and
+// a tile inside it (upper triangle for the symmetric stages), and each
+// table's X^T buffers exist where the launch reads or writes them.
+bool plan_consistent(const Plan &p) {
+  for (const Launch &l : p.prog) {
+    if (l.kind < kLkGram) continue;
+    if (l.table < 1 || l.table > static_cast<int32_t>(p.tables.size())) return false;
+    if (l.list < 0 || l.list >= static_cast<int32_t>(p.lists.size())) return false;
+    std::vector<const MatDev *> rows;
+    for (const Part &pt : p.tables[l.table - 1]) {
+      if (pt.group < 0 || pt.group > 1) return false;
+      for (int32_t i : p.groups[pt.group]) {
+        rows.push_back(&p.mats[i]);
+        const bool gram_buf = pt.a >= kBufA1 || pt.b >= kBufA1 || pt.r >= kBufA1;
+        if (gram_buf && p.extra[i].size() != 4) return false;
+        // the second X^T buffer is read (cur = 1) or written (Apply); the
+        // sizing pass has no addresses yet
+        const bool needs_xt1 = pt.cur || l.kind == kLkApply;
+        if (needs_xt1 && p.mats[i].xt[0] && !p.mats[i].xt[1]) return false;
+      }
+    }
+    const bool sym = l.kind == kLkGram || l.kind == kLkSquare;
+    const int32_t n = static_cast<int32_t>(rows.size());
+    for (const TileEntry &e : p.lists[l.list]) {
+      if (e.mat < 0 || e.mat >= n) return false;
+      const MatDev &d = *rows[e.mat];
+      if (e.ti >= d.tm || e.tj >= (sym ? d.tm : d.tn) || (sym && e.tj < e.ti)) return false;
+    }
+  }
+  return true;
+}
+
+// The MatDev array of table t (0: every matrix; else, for each part of the
+// launch in turn, its group's matrices with the part's buffers, X^T order
+// and coefficients).
 std::vector<MatDev> table_contents(const Plan &p, size_t t) {
   if (t == 0) return p.mats;
-  const Recipe &r = p.recipes[t - 1];
   std::vector<MatDev> out;
-  for (int32_t i : p.groups[r.group]) {
-    MatDev d = p.mats[i];
-    auto buf = [&](int32_t b) -> void * {
-      if (b == kBufNone) return nullptr;
-      if (b == kBufA) return p.mats[i].a;
-      if (b == kBufB) return p.mats[i].b;
-      return p.extra[i][b - kBufA1];
-    };
-    d.a = buf(r.a);
-    d.b = buf(r.b);
-    d.sq_r = buf(r.r);
-    out.push_back(d);
+  for (const Part &pt : p.tables[t - 1]) {
+    for (int32_t i : p.groups[pt.group]) {
+      MatDev d = p.mats[i];
+      auto buf = [&](int32_t b) -> void * {
+        if (b == kBufNone) return nullptr;
+        if (b == kBufA) return p.mats[i].a;
+        if (b == kBufB) return p.mats[i].b;
+        return p.extra[i][b - kBufA1];
+      };
+      d.a = buf(pt.a);
+      d.b = buf(pt.b);
+      d.sq_r = buf(pt.r);
+      if (pt.cur) std::swap(d.xt[0], d.xt[1]);
+      d.ca = pt.ca;
+      d.cb = pt.cb;
+      d.cc = pt.cc;
+      d.cdiag = pt.cdiag;
+      d.first_it = pt.first;
+      out.push_back(d);
+    }
   }
   return out;
 }
@@ -685,6 +761,7 @@ static int muon_step_impl(const dmuon_matrix *mats, int32_t n, const dmuon_step_
   // ---- validated: plan with real addresses, upload tables, launch ----
   char *ws = static_cast<char *>(workspace);
   build_plan(mats, n, *cfg, ws, p);
+  if (!plan_consistent(p)) return fail(DMUON_ERR_INVALID_ARG, "internal error: inconsistent launch plan");
   if (packed)
     for (int32_t i = 0; i < n; ++i)
       p.mats[i].packed = static_cast<char *>(packed) + mats[i].packed_offset * elem_size(packed_dtype);
@@ -704,7 +781,7 @@ static int muon_step_impl(const dmuon_matrix *mats, int32_t n, const dmuon_step_
   auto dtab = [&](int32_t t) { return reinterpret_cast<const MatDev *>(ws + p.off_table[t]); };
   const MatDev *dm = dtab(0);
   const StepScalars sc{cfg->a, cfg->b, cfg->c, cfg->lr, cfg->momentum, cfg->eps,
-                       (cfg->flags & DMUON_FLAG_NESTEROV) ? 1 : 0, 0.f};
+                       (cfg->flags & DMUON_FLAG_NESTEROV) ? 1 : 0, 0};
   const bool fp32 = cfg->flags & DMUON_FLAG_NS_FP32;
 
   // events[0] before the first launch, events[j] after launch j
@@ -743,8 +820,7 @@ static int muon_step_impl(const dmuon_matrix *mats, int32_t n, const dmuon_step_
                               : l.kind == kLkApply  ? kModeApply
                                                     : kModeFinal;
         const TileEntry *tl = reinterpret_cast<const TileEntry *>(ws + p.off_list[l.list]);
-        rc = launched(launch_ns_stage(mode, fp32, dtab(l.table), tl, p.list_xcd[l.list], l.cur, l.first,
-                                      l.sc, s),
+        rc = launched(launch_ns_stage(mode, fp32, dtab(l.table), tl, p.list_xcd[l.list], sc, s),
                       "Newton-Schulz stage launch");
       }
     }
@@ -770,6 +846,7 @@ int dmuon_step_launches(const dmuon_matrix *mats, int32_t n, const dmuon_step_co
   }
   Plan p;
   build_plan(mats, n, *cfg, nullptr, p);
+  if (!plan_consistent(p)) return fail(DMUON_ERR_INVALID_ARG, "internal error: inconsistent launch plan");
   *count = static_cast<int32_t>(p.prog.size());
   for (int32_t j = 0; j < cap && j < *count; ++j) {
     out[j].kind = p.prog[j].kind;

@@ -32,7 +32,9 @@ struct MatDev {
   void *orth;
   void *packed;     // nullable: this matrix's slot of the packed param buffer
   // workspace memory (element type bf16, or fp32 in the fp32 mode)
-  void *xt[2];      // X^T, n_p x m_p, row-major: the iterate, ping-pong
+  void *xt[2];      // X^T, n_p x m_p, row-major: the iterate, ping-pong; in
+                    // a GEMM launch's table xt[0] is the iterate read and
+                    // xt[1] the one Apply writes
   void *a;          // m_p x m_p: A = X X^T (Gram output, Square's L operand)
   void *b;          // m_p x m_p: B = b A + c A A (Square output, Apply's L operand)
   const void *sq_r; // Square's R operand; nullptr: R = a (the product A A)
@@ -50,6 +52,13 @@ struct MatDev {
   int32_t transposed;   // rows > cols
   float scale;
   int32_t tm, tn;       // mp / kGemmTile, np / kGemmTile
+  // Per-launch values of the GEMM stages, set in each launch's table (the
+  // parts of one grouped launch may come from different chains):
+  float ca;             // Apply / Final: weight of the a X term
+  float cb, cc;         // Square: C = cb A + cc L R^T
+  float cdiag;          // Square: added on the diagonal (rows < m)
+  int32_t first_it;     // X holds U unnormalised: Gram scales by inv_norm^2,
+                        // Apply / Final by inv_norm
 };
 
 // One 256 x 256 output tile of a grouped GEMM stage.
@@ -71,14 +80,14 @@ struct StepScalars {
   float a, b, c;
   float lr, mu, eps;
   int32_t nesterov;
-  float diag;  // Square only: added to the diagonal (rows < m) of its output
+  int32_t pad_;
 };
 
 enum GemmMode : int32_t {
   kModeGram = 0,    // C = X X^T (upper tiles, mirrored)        -> A
-  kModeSquare = 1,  // C = b A + c A R^T + diag I (upper tiles, mirrored) -> B;
-                    // R = A unless sq_r is set (then b = 0: a product of two
-                    // commuting symmetric matrices, itself symmetric)
+  kModeSquare = 1,  // C = cb A + cc A R^T + cdiag I (upper tiles, mirrored)
+                    // -> B; R = A unless sq_r is set (then cb = 0: a product
+                    // of two commuting symmetric matrices, itself symmetric)
   kModeApply = 2,   // C = a X + B X                             -> X', X'^T
   kModeFinal = 3    // last apply: P -= lr*scale*C, orth <- C
 };
@@ -135,10 +144,9 @@ struct AdamScalars {
 hipError_t launch_adamw_batch(const AdamBatch &b, AdamScalars s, hipStream_t st);
 
 // ---- launchers (gemm.hip) ----
-// first: the first iteration, whose X holds U unnormalised: Gram scales by
-// inv_norm^2 and Apply / Final by inv_norm.
+// mats: the launch's table (per-matrix operands and coefficients).
 hipError_t launch_ns_stage(GemmMode mode, bool fp32, const MatDev *mats,
                            const TileEntry *tiles, const StageXcd &xcd,
-                           int32_t cur, bool first, StepScalars s, hipStream_t st);
+                           StepScalars s, hipStream_t st);
 
 }  // namespace dmuon

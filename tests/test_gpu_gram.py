@@ -51,7 +51,7 @@ def test_gram_single_matrix_bf16(nsd, shape):
     say(f"gram bf16 step {shape}")
     opts = nsd.StepOptions(gram_ns=True)
     kinds = _kinds(nsd, [shape], opts)
-    assert kinds.count("gram") == 2 and kinds.count("square") == 14   # phases 3 + 2
+    assert kinds.count("gram") == 2 and kinds.count("square") == 13   # phases 3 + 2
     case = Case([shape], "bf16", "bf16", seed=31, m_std=1e-3)
     err = check_step(case, opts, case.run_gpu(opts), case.run_oracle(opts))
     say(f"  O rel err {err:.3e}")
@@ -85,7 +85,7 @@ def test_gram_mixed_with_direct_chain(nsd):
               (1024, 256), (64, 64), (129, 900)]
     opts = nsd.StepOptions(gram_ns=True)
     kinds = _kinds(nsd, shapes, opts)
-    assert kinds.count("final") == 2   # one per chain
+    assert kinds.count("final") == 1   # the two chains' last applies share a launch
     case = Case(shapes, "bf16", "bf16", seed=33, m_std=1e-3)
     a = case.run_gpu(opts)
     err = check_step(case, opts, a, case.run_oracle(opts))
