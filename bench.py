@@ -72,13 +72,16 @@ def measured_traffic(workload_name: str, fp32: bool, kind: str, gram_ns: bool):
     taken."""
     import hashlib
     path = os.path.join(ROOT, "profiles", "dominant_kernel_traffic_llama31_8b_owner0.json")
-    src = os.path.join(ROOT, "newton_schulz_dmuon_amd", "csrc", "gemm.hip")
+    csrc = os.path.join(ROOT, "newton_schulz_dmuon_amd", "csrc")
     try:
         rec = json.load(open(path))
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        # the kernel source, and the host planner that decides each launch's tiles
+        sha = {k: hashlib.sha256(open(os.path.join(csrc, f), "rb").read()).hexdigest()
+               for k, f in (("gemm", "gemm.hip"), ("host", "host_api.cpp"))}
     except OSError:
         return None
-    if fp32 or rec.get("workload") != workload_name or rec.get("gemm_source_sha256") != sha \
+    if fp32 or rec.get("workload") != workload_name or rec.get("gemm_source_sha256") != sha["gemm"] \
+            or rec.get("host_source_sha256") != sha["host"] \
             or rec.get("kind") != kind or rec.get("gram_ns") != gram_ns:
         return None
     return rec["traffic_bytes_per_launch"]
