@@ -31,6 +31,33 @@ def ns_bf16_storage(X0, a, b, c, steps):
     return X
 
 
+def ns_gram_bf16_storage(X0, a, b, c, steps, phases):
+    """The Gram-space chain with the GPU's storage points: X, A, P, P^2,
+    A P^2 and Q stored as bf16 (products in fp32), each stored m x m matrix
+    made exactly symmetric from its upper triangle, X <- Q X at the end of
+    every phase (the lengths in ``phases``, summing to ``steps``) in bf16,
+    the last one kept in fp32."""
+    assert sum(phases) == steps
+
+    def sym(M):
+        return np.triu(M) + np.triu(M, 1).T
+
+    X = rne_bf16(X0)
+    for ph, L in enumerate(phases):
+        A = rne_bf16(sym(to_f32(X @ X.T)))
+        m = A.shape[0]
+        Q = None
+        for i in range(L):
+            P = rne_bf16(sym(to_f32(a * np.eye(m) + b * A + c * to_f32(A @ A.T))))
+            if i + 1 < L:
+                T = rne_bf16(sym(to_f32(P @ P.T)))
+                A = rne_bf16(sym(to_f32(A @ T.T)))
+            Q = P if Q is None else rne_bf16(sym(to_f32(Q @ P.T)))
+        Xn = to_f32(Q @ X)
+        X = Xn if ph + 1 == len(phases) else rne_bf16(Xn)
+    return X
+
+
 def tol_o_bf16(steps: int) -> float:
     """Relative-Frobenius bar for the bf16 chain's output O.  2e-2 up to the
     default 5 iterations; above that the default quintic keeps amplifying

@@ -30,3 +30,70 @@ def test_quintic_expands_errors_inside_its_band():
     s = np.linspace(0.6818, 1.2024, 10001)
     dp = a + 3 * b * s ** 2 + 5 * c * s ** 4
     assert np.max(np.abs(dp)) > 1.0          # some band points amplify errors
+
+
+# ---- the Gram-space chain (DMUON_FLAG_GRAM_NS) ----
+
+def _gram_fp64(X0, a, b, c, phases):
+    """The Gram-space algebra in float64: per phase A = X X^T, then per
+    iteration P = aI + bA + cA^2, A <- A P^2, Q <- Q P; X <- Q X."""
+    X = np.asarray(X0, np.float64)
+    for L in phases:
+        A = X @ X.T
+        Q = np.eye(A.shape[0])
+        for _ in range(L):
+            P = a * np.eye(A.shape[0]) + b * A + c * (A @ A)
+            A = A @ P @ P
+            Q = Q @ P
+        X = Q @ X
+    return X
+
+
+def _rank1_plus_noise(m, n, seed):
+    rng = np.random.default_rng(seed)
+    U, _ = np.linalg.qr(rng.standard_normal((m, m)))
+    V, _ = np.linalg.qr(rng.standard_normal((n, m)))
+    s = np.r_[[30.0], np.abs(rng.standard_normal(m - 1)) * 0.05]
+    X = (U * s) @ V.T
+    return X / np.linalg.norm(X)
+
+
+@pytest.mark.parametrize("phases", [[5], [3, 2], [2, 2], [3, 3, 2], [1]])
+def test_gram_space_algebra_equals_direct_iteration(phases):
+    """Exact arithmetic (float64): the Gram-space chain and its restarts give
+    the direct iteration's X_K, also on an ill-conditioned input."""
+    rng = np.random.default_rng(11)
+    for X0 in (rng.standard_normal((24, 80)), _rank1_plus_noise(24, 80, 3)):
+        X0 = X0 / np.linalg.norm(X0)
+        ref = muon.newton_schulz(X0, *muon.QUINTIC, sum(phases))
+        got = _gram_fp64(X0, *muon.QUINTIC, phases)
+        assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 1e-11
+
+
+def test_gram_space_bf16_error_gaussian():
+    """bf16 storage on a Gaussian 128 x 512: within the 2e-2 bar with room,
+    and near the direct chain's own bf16 error."""
+    from _bf16_model import ns_gram_bf16_storage
+    rng = np.random.default_rng(5)
+    G = rng.standard_normal((128, 512))
+    X0 = G / np.linalg.norm(G)
+    ref = muon.newton_schulz(X0, *muon.QUINTIC, 5)
+    err = lambda Y: np.linalg.norm(Y - ref) / np.linalg.norm(ref)
+    e_gram = err(ns_gram_bf16_storage(X0, *muon.QUINTIC, 5, [3, 2]))
+    e_direct = err(ns_bf16_storage(X0, *muon.QUINTIC, 5))
+    assert e_gram < tol_o_bf16(5) / 1.3
+    assert e_gram < 1.5 * e_direct
+
+
+def test_gram_space_needs_restarts_on_ill_conditioned_input():
+    """Why phases are at most 3 iterations: on a rank-1-plus-noise input,
+    bf16 storage of Q over 5 iterations (eigenvalues up to a^5 ~ 485 on the
+    noise directions) ruins the result, while restarting after 3 keeps it
+    within 2x of the direct chain's bf16 error."""
+    from _bf16_model import ns_gram_bf16_storage
+    X0 = _rank1_plus_noise(64, 256, 7)
+    ref = muon.newton_schulz(X0, *muon.QUINTIC, 5)
+    err = lambda Y: np.linalg.norm(Y - ref) / np.linalg.norm(ref)
+    e_direct = err(ns_bf16_storage(X0, *muon.QUINTIC, 5))
+    assert err(ns_gram_bf16_storage(X0, *muon.QUINTIC, 5, [5])) > 100 * e_direct
+    assert err(ns_gram_bf16_storage(X0, *muon.QUINTIC, 5, [3, 2])) < 2 * e_direct

@@ -134,3 +134,28 @@ def test_gram_packed_step_matches_step_plus_pack(nsd):
     for o, (r, c) in zip(offs, shapes):
         assert torch.equal(outs[0][1][o:o + r * c].view(torch.int16),
                            outs[1][1][o:o + r * c].view(torch.int16))
+
+
+def test_gram_ill_conditioned_input_stays_near_direct_chain(nsd):
+    """A rank-1-plus-noise gradient (singular values 30 and ~0.05): the bf16
+    chains are both far from fp64 here (the small singular directions are
+    noise-dominated), and the Gram-space chain with its restarts stays
+    within 2x of the direct chain's error (without restarts it would lose
+    all accuracy)."""
+    from _gpu_util import rel_fro, rne_bf16
+    m, n = 128, 512
+    rng = np.random.default_rng(12)
+    U, _ = np.linalg.qr(rng.standard_normal((m, m)))
+    V, _ = np.linalg.qr(rng.standard_normal((n, m)))
+    s = np.r_[[30.0], np.abs(rng.standard_normal(m - 1)) * 0.05]
+    G = rne_bf16(1e-3 * (U * s) @ V.T).astype(np.float32)
+    errs = {}
+    for gram in (False, True):
+        case = Case([(m, n)], "bf16", "bf16", seed=36)
+        case.G = [G]
+        opts = nsd.StepOptions(gram_ns=gram)
+        _, _, O = case.run_gpu(opts)
+        _, _, Ow = case.run_oracle(opts)
+        errs[gram] = rel_fro(O[0], Ow[0])
+    say(f"  rank-1 + noise: direct {errs[False]:.3e}, gram-space {errs[True]:.3e}")
+    assert errs[True] < 2 * errs[False] and errs[True] < 0.5
