@@ -479,7 +479,9 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   auto capture_ax = [&](const lds_char *st, int kt) {
     if constexpr (!cap_ax) return;
     const int c = kt - cap_kt0;  // uniform in the wave
-    if (c < 0 || c >= kCapSteps) return;
+    // a zero weight (the plain products of the Gram-space chain and its
+    // X <- QX) adds nothing: skip the reads
+    if (c < 0 || c >= kCapSteps || cap_w == 0.f) return;
 #pragma unroll
     for (int i = 0; i < kFragM; ++i) {
       const float w = (i / kCapFrags == c) ? cap_w : 0.f;
