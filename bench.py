@@ -206,7 +206,7 @@ def main(argv=None) -> int:
     ap.add_argument("--ns-steps", type=int, default=None)
     ap.add_argument("--fp32-ns", action="store_true", help="fp32 checking mode")
     ap.add_argument("--direct-ns", action="store_true",
-                    help="direct chain for every matrix (default: Gram-space chain where n >= 2m)")
+                    help="direct chain for every matrix (default: Gram-space chain where n >= 2m, ns_steps >= 5)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
     args = ap.parse_args(argv)

@@ -74,13 +74,15 @@ enum {
   DMUON_FLAG_NESTEROV = 1u << 1,
   /* Gram-space Newton-Schulz (the pages credit a "Gram Newton-Schulz"
    * kernel: landing page, "VLA and VLM" and the credits) for every matrix
-   * with max(r,c) >= 2 min(r,c) when ns_steps >= 2; the others keep the
-   * direct chain.  All iterates are polynomials in A = X X^T, so the chain
-   * runs on m x m matrices: per iteration P = aI + bA + cA^2, A <- A P^2,
-   * Q <- Q P, and X <- Q X once at the end.  Same result in exact
-   * arithmetic; about 1.6x fewer flops at n = 3.5m.  It restarts from an
-   * explicit X every 3 iterations at most (5 -> 3 + 2), which keeps bf16
-   * rounding of the accumulated Q from growing on ill-conditioned inputs. */
+   * with max(r,c) >= 2 min(r,c) when ns_steps >= 5; the others, and every
+   * matrix at fewer iterations, keep the direct chain.  All iterates are
+   * polynomials in A = X X^T, so the chain runs on m x m matrices: per
+   * iteration P = aI + bA + cA^2, A <- A P^2, Q <- Q P, and X <- Q X once
+   * per phase.  Same result in exact arithmetic; about 1.35x fewer flops at
+   * n = 3.5m and ns_steps = 5.  Phases are two iterations (5 -> 2 + 2 + 1),
+   * each restarting from an explicit X, which keeps bf16 rounding of the
+   * accumulated Q at or below the direct chain's error on ill-conditioned
+   * inputs. */
   DMUON_FLAG_GRAM_NS = 1u << 2
 };
 

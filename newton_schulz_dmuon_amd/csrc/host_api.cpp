@@ -232,23 +232,28 @@ void build_stage_tiles(const std::vector<MatDev> &mats, int st, std::vector<Tile
 // runs, otherwise 64 x 128 blocks of X.  One sum-of-squares partial each.
 int64_t orient_groups(const MatDev &d) { return (d.mp / kTrTile) * (d.np / kTrTile) / 2; }
 
-// A matrix takes the Gram-space chain when asked for, with at least two
-// iterations (one is the same product either way) and n >= 2m: the m x m
-// chain then costs fewer flops than K direct iterations, and the iterate's
-// singular values stay within a factor (sqrt(n)+sqrt(m))/(sqrt(n)-sqrt(m))
-// < 6 of each other for Gaussian-like inputs, which keeps bf16 storage of
-// the accumulated polynomial Q accurate.
+// A matrix takes the Gram-space chain when asked for, with at least five
+// iterations and n >= 2m: the m x m chain then costs fewer flops than the
+// direct iterations, and the iterate's singular values stay within a factor
+// (sqrt(n)+sqrt(m))/(sqrt(n)-sqrt(m)) < 6 of each other for Gaussian-like
+// inputs.  Below five iterations the rounding of the first phase's Q is not
+// damped by later iterations: on ill-conditioned inputs (rank one plus
+// noise) two iterations come out about 18x, three to four 2-4x less
+// accurate than the direct chain in a bf16 emulation, so those keep it.
 bool uses_gram(const MatDev &d, const dmuon_step_config &cfg) {
-  return (cfg.flags & DMUON_FLAG_GRAM_NS) && cfg.ns_steps >= 2 && d.n >= 2 * d.m;
+  return (cfg.flags & DMUON_FLAG_GRAM_NS) && cfg.ns_steps >= 5 && d.n >= 2 * d.m;
 }
 
-// Phases of the Gram-space chain: at most 3 iterations each, as even as
-// possible, longer ones first (5 -> 3 + 2, 8 -> 3 + 3 + 2).  Each phase
-// starts from an explicit X (a fresh A = X X^T) and ends with X <- Q X.
+// Phases of the Gram-space chain: two iterations each, the last one a
+// single iteration when K is odd (5 -> 2 + 2 + 1, 8 -> 2 + 2 + 2 + 2).  Each
+// phase starts from an explicit X (a fresh A = X X^T) and ends with
+// X <- Q X.  Over a phase Q's eigenvalues reach a^L on the directions of
+// small singular values, and its bf16 rounding is relative to that: phases
+// of three lose accuracy on ill-conditioned inputs (rank one plus noise:
+// 4-5x the direct chain's error), phases of two stay at 0.5-1.05x of it.
 std::vector<int> gram_phases(int K) {
-  const int np = (K + 2) / 3, base = K / np, extra = K % np;
-  std::vector<int> L(np, base);
-  for (int i = 0; i < extra; ++i) ++L[i];
+  std::vector<int> L(K / 2, 2);
+  if (K % 2) L.push_back(1);
   return L;
 }
 

@@ -21,8 +21,11 @@ def to_f32(x):
     return np.asarray(x, np.float32).astype(np.float64)
 
 
-def ns_bf16_storage(X0, a, b, c, steps):
-    X = rne_bf16(X0)
+def ns_bf16_storage(X0, a, b, c, steps, round_x0=True):
+    """``round_x0=False``: the first X is taken as exact, as on the GPU when
+    U is already a bf16 value (the GPU stores U unnormalised and scales by
+    1/||U|| in fp32)."""
+    X = rne_bf16(X0) if round_x0 else to_f32(X0)
     for k in range(steps):
         A = rne_bf16(to_f32(X @ X.T))
         B = rne_bf16(to_f32(b * A + c * to_f32(A @ A)))
@@ -31,7 +34,7 @@ def ns_bf16_storage(X0, a, b, c, steps):
     return X
 
 
-def ns_gram_bf16_storage(X0, a, b, c, steps, phases):
+def ns_gram_bf16_storage(X0, a, b, c, steps, phases, round_x0=True):
     """The Gram-space chain with the GPU's storage points: X, A, P, P^2,
     A P^2 and Q stored as bf16 (products in fp32), each stored m x m matrix
     made exactly symmetric from its upper triangle, X <- Q X at the end of
@@ -42,7 +45,7 @@ def ns_gram_bf16_storage(X0, a, b, c, steps, phases):
     def sym(M):
         return np.triu(M) + np.triu(M, 1).T
 
-    X = rne_bf16(X0)
+    X = rne_bf16(X0) if round_x0 else to_f32(X0)
     for ph, L in enumerate(phases):
         A = rne_bf16(sym(to_f32(X @ X.T)))
         m = A.shape[0]

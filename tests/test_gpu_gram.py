@@ -5,8 +5,8 @@ The Gram-space chain computes the same X_K in exact arithmetic (every
 iterate is a polynomial in the first A = X X^T); the bars are the direct
 chain's: <= 2e-2 relative Frobenius for the bf16 chain up to 5 iterations,
 the 6-8 iteration bar above that, <= 1e-4 in the fp32 checking mode.
-Matrices with max(r, c) >= 2 min(r, c) take it; the others of the same call
-keep the direct chain.
+Matrices with max(r, c) >= 2 min(r, c) take it at ns_steps >= 5; the others
+of the same call keep the direct chain.
 """
 
 import numpy as np
@@ -51,15 +51,16 @@ def test_gram_single_matrix_bf16(nsd, shape):
     say(f"gram bf16 step {shape}")
     opts = nsd.StepOptions(gram_ns=True)
     kinds = _kinds(nsd, [shape], opts)
-    assert kinds.count("gram") == 2 and kinds.count("square") == 13   # phases 3 + 2
+    assert kinds.count("gram") == 3 and kinds.count("square") == 11   # phases 2 + 2 + 1
     case = Case([shape], "bf16", "bf16", seed=31, m_std=1e-3)
     err = check_step(case, opts, case.run_gpu(opts), case.run_oracle(opts))
     say(f"  O rel err {err:.3e}")
 
 
-@pytest.mark.parametrize("k", [2, 3, 4, 5, 6, 8])
+@pytest.mark.parametrize("k", [3, 5, 6, 7, 8])
 def test_gram_ns_steps(nsd, k):
-    """Every phase split: 2, 3 (one phase), 2+2, 3+2, 3+3, 3+3+2."""
+    """Phase splits 2+2+1, 2+2+2, 2+2+2+1, 2+2+2+2; at 3 the flag leaves the
+    direct chain in place."""
     say(f"gram ns_steps {k}")
     shapes = [(300, 700), (1000, 257), (17, 100)]
     case = Case(shapes, "bf16", "bf16", seed=40 + k, m_std=1e-3)
@@ -99,7 +100,7 @@ def test_gram_mixed_with_direct_chain(nsd):
 def test_gram_cubic_and_custom_coefficients(nsd):
     """c = 0 (the cubic): the P = aI + bA + cA^2 epilogue reads A instead
     of the captured R tile.  Also fp32 params with bf16 grads."""
-    for coef, k in (((1.5, -0.5, 0.0), 8), ((3.0, -3.2, 1.2), 5)):
+    for coef, k in (((1.5, -0.5, 0.0), 8), ((3.0, -3.2, 1.2), 5), ((3.4445, -4.7750, 2.0315), 7)):
         say(f"gram coefficients {coef}, ns_steps {k}")
         case = Case([(300, 700), (700, 300)], "f32", "bf16", seed=34, m_std=1e-3)
         opts = nsd.StepOptions(a=coef[0], b=coef[1], c=coef[2], ns_steps=k, gram_ns=True)
@@ -140,8 +141,9 @@ def test_gram_ill_conditioned_input_stays_near_direct_chain(nsd):
     """A rank-1-plus-noise gradient (singular values 30 and ~0.05): the bf16
     chains are both far from fp64 here (the small singular directions are
     noise-dominated), and the Gram-space chain with its restarts stays
-    within 2x of the direct chain's error (without restarts it would lose
-    all accuracy)."""
+    about at the direct chain's error (0.75x in a bf16 emulation; phases of
+    three iterations would give 4.6x, one phase of five would lose all
+    accuracy)."""
     from _gpu_util import rel_fro, rne_bf16
     m, n = 128, 512
     rng = np.random.default_rng(12)
@@ -158,4 +160,4 @@ def test_gram_ill_conditioned_input_stays_near_direct_chain(nsd):
         _, _, Ow = case.run_oracle(opts)
         errs[gram] = rel_fro(O[0], Ow[0])
     say(f"  rank-1 + noise: direct {errs[False]:.3e}, gram-space {errs[True]:.3e}")
-    assert errs[True] < 2 * errs[False] and errs[True] < 0.5
+    assert errs[True] < 1.2 * errs[False]
