@@ -83,7 +83,13 @@ enum {
    * each restarting from an explicit X, which keeps bf16 rounding of the
    * accumulated Q at or below the direct chain's error on ill-conditioned
    * inputs. */
-  DMUON_FLAG_GRAM_NS = 1u << 2
+  DMUON_FLAG_GRAM_NS = 1u << 2,
+  /* Record, per matrix, whether the Newton-Schulz input U (M after the
+   * momentum update, or the Nesterov look-ahead) holds a NaN or an Inf:
+   * one int32 per matrix (1 or 0) in the workspace, at the offset
+   * dmuon_nonfinite_flags_offset() gives.  It only reports: non-finite
+   * values still propagate through that matrix's step, as without it. */
+  DMUON_FLAG_CHECK_FINITE = 1u << 3
 };
 
 /* Launch kinds reported by dmuon_step_launches. */
@@ -180,6 +186,15 @@ int dmuon_pack_offsets(const int64_t *numel, int32_t n, int64_t align,
 int dmuon_step_launches(const dmuon_matrix *mats, int32_t n,
                         const dmuon_step_config *cfg, dmuon_launch_info *out,
                         int32_t cap, int32_t *count);
+
+/* Byte offset in the workspace of the int32[n] non-finite flags that a step
+ * with DMUON_FLAG_CHECK_FINITE writes (flag i for mats[i]; valid once the
+ * step has completed on its stream, until the workspace is used again).
+ * Host-only.
+ * Errors: INVALID_ARG (offset_out NULL, the flag not set in cfg) and those
+ * of dmuon_workspace_bytes. */
+int dmuon_nonfinite_flags_offset(const dmuon_matrix *mats, int32_t n,
+                                 const dmuon_step_config *cfg, size_t *offset_out);
 
 /* Bytes of device workspace dmuon_muon_step needs for these matrices and
  * flags.  Host-only; validates like dmuon_muon_step except for pointers. */

@@ -28,6 +28,7 @@ FIELD_GRAD = 1
 FLAG_NS_FP32 = 1 << 0
 FLAG_NESTEROV = 1 << 1
 FLAG_GRAM_NS = 1 << 2
+FLAG_CHECK_FINITE = 1 << 3
 
 # dmuon_launch_info.kind
 LAUNCH_KINDS = ("momentum_sumsq", "momentum_orient", "norm", "update_direct", "gram", "square",
@@ -36,7 +37,8 @@ LAUNCH_KINDS = ("momentum_sumsq", "momentum_orient", "norm", "update_direct", "g
 EXPORTED = ("dmuon_abi_version", "dmuon_error_string", "dmuon_last_error",
             "dmuon_partition_lpt", "dmuon_pack_offsets", "dmuon_workspace_bytes",
             "dmuon_pack", "dmuon_unpack", "dmuon_muon_step", "dmuon_muon_step_traced",
-            "dmuon_muon_step_packed", "dmuon_adamw_step", "dmuon_step_launches")
+            "dmuon_muon_step_packed", "dmuon_adamw_step", "dmuon_step_launches",
+            "dmuon_nonfinite_flags_offset")
 
 
 class Matrix(ctypes.Structure):
@@ -135,9 +137,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dmuon_adamw_step.argtypes = [P(Tensor), c_i32, P(AdamWConfig), vp]
     lib.dmuon_step_launches.argtypes = [P(Matrix), c_i32, P(StepConfig), P(LaunchInfo), c_i32,
                                         P(c_i32)]
+    lib.dmuon_nonfinite_flags_offset.argtypes = [P(Matrix), c_i32, P(StepConfig), P(ctypes.c_size_t)]
     for name in ("dmuon_partition_lpt", "dmuon_pack_offsets", "dmuon_workspace_bytes",
                  "dmuon_pack", "dmuon_unpack", "dmuon_muon_step", "dmuon_muon_step_traced",
-                 "dmuon_muon_step_packed", "dmuon_adamw_step", "dmuon_step_launches"):
+                 "dmuon_muon_step_packed", "dmuon_adamw_step", "dmuon_step_launches",
+                 "dmuon_nonfinite_flags_offset"):
         getattr(lib, name).restype = ctypes.c_int
     if lib.dmuon_abi_version() != ABI_VERSION:
         raise ImportError(f"libdmuon ABI {lib.dmuon_abi_version()} != {ABI_VERSION}")

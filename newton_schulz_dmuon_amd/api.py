@@ -59,11 +59,14 @@ class StepOptions:
     # Gram-space chain for matrices with max(r,c) >= 2 min(r,c) (see
     # DMUON_FLAG_GRAM_NS); the others keep the direct chain
     gram_ns: bool = False
+    # record per matrix whether U holds a NaN or an Inf (nonfinite_flags)
+    check_finite: bool = False
 
     def to_c(self) -> StepConfig:
         flags = (_lib.FLAG_NESTEROV if self.nesterov else 0) | \
                 (_lib.FLAG_NS_FP32 if self.ns_fp32 else 0) | \
-                (_lib.FLAG_GRAM_NS if self.gram_ns else 0)
+                (_lib.FLAG_GRAM_NS if self.gram_ns else 0) | \
+                (_lib.FLAG_CHECK_FINITE if self.check_finite else 0)
         return StepConfig(self.a, self.b, self.c, int(self.ns_steps), self.lr,
                           self.momentum, self.eps, flags)
 
@@ -103,6 +106,19 @@ def step_launches(shapes: Sequence, opts: StepOptions):
     out = (LaunchInfo * max(count.value, 1))()
     check(lib.dmuon_step_launches(arr, n, ctypes.byref(cfg), out, count.value, ctypes.byref(count)))
     return [(_lib.LAUNCH_KINDS[out[j].kind], out[j].flops) for j in range(count.value)]
+
+
+def nonfinite_flags(params, opts: StepOptions, workspace: Workspace):
+    """The per-matrix flags a step with ``opts.check_finite`` wrote into
+    ``workspace``: a device int32 tensor, 1 where that matrix's U held a NaN
+    or an Inf.  A view of the workspace; read it after the step's stream has
+    synchronised and before the workspace is used again."""
+    import torch
+    arr, n = matrices(params)
+    off = ctypes.c_size_t(0)
+    cfg = opts.to_c()
+    check(load().dmuon_nonfinite_flags_offset(arr, n, ctypes.byref(cfg), ctypes.byref(off)))
+    return workspace.buf[off.value:off.value + 4 * n].view(torch.int32)
 
 
 def workspace_bytes(params, opts: StepOptions) -> int:

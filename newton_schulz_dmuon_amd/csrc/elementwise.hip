@@ -113,7 +113,12 @@ __global__ __launch_bounds__(256) void finalize_norm_kernel(const MatDev *__rest
   double acc = 0.0;
   for (int32_t i = threadIdx.x; i < d.part_count; i += 256) acc += d.partials[i];
   const double tot = block_sum_f64(acc, red);
-  if (threadIdx.x == 0) *d.inv_norm = static_cast<float>(1.0 / (sqrt(tot) + (double)eps));
+  if (threadIdx.x == 0) {
+    *d.inv_norm = static_cast<float>(1.0 / (sqrt(tot) + (double)eps));
+    // the squares are summed in fp64, where no finite fp32 U overflows: a
+    // non-finite sum means a NaN or an Inf in U
+    if (d.nonfinite) *d.nonfinite = __builtin_isfinite(tot) ? 0 : 1;
+  }
 }
 
 // Fused momentum + sum of squares + wide orientation:

@@ -90,7 +90,7 @@ int validate_config(const dmuon_step_config *cfg) {
   for (float v : vals)
     if (!std::isfinite(v)) return fail(DMUON_ERR_INVALID_ARG, "non-finite step coefficient");
   if (cfg->eps < 0.f) return fail(DMUON_ERR_INVALID_ARG, "eps < 0");
-  const uint32_t known = DMUON_FLAG_NS_FP32 | DMUON_FLAG_NESTEROV | DMUON_FLAG_GRAM_NS;
+  const uint32_t known = DMUON_FLAG_NS_FP32 | DMUON_FLAG_NESTEROV | DMUON_FLAG_GRAM_NS | DMUON_FLAG_CHECK_FINITE;
   if (cfg->flags & ~known) return fail(DMUON_ERR_INVALID_ARG, "unknown flag bits 0x%x", cfg->flags & ~known);
   return DMUON_OK;
 }
@@ -169,7 +169,7 @@ struct Plan {
   int64_t ew_total = 0, tr_total = 0;
   // workspace layout (byte offsets)
   std::vector<int64_t> off_table, off_list;
-  int64_t off_partials = 0, off_inv = 0;
+  int64_t off_partials = 0, off_inv = 0, off_flags = -1;
   int64_t table_bytes = 0;  // [0, table_bytes) is uploaded
   int64_t total_bytes = 0;
 };
@@ -453,6 +453,11 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
   off = round_up(off + 8 * (K > 0 ? tr : ew), 256);
   p.off_inv = off;
   off = round_up(off + 256 * int64_t(n), 256);  // one 256-byte slot per matrix
+  p.off_flags = -1;
+  if (cfg.flags & DMUON_FLAG_CHECK_FINITE) {  // one int32 per matrix
+    p.off_flags = off;
+    off = round_up(off + 4 * int64_t(n), 256);
+  }
   for (int32_t i = 0; i < n; ++i) {
     MatDev &d = p.mats[i];
     // sum-of-squares partials: one per orientation tile, or per flat chunk
@@ -462,6 +467,7 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
                     : nullptr;
     d.part_count = K > 0 ? static_cast<int32_t>(orient_groups(d)) : d.ew_count;
     d.inv_norm = ws ? reinterpret_cast<float *>(ws + p.off_inv + 256 * int64_t(i)) : nullptr;
+    d.nonfinite = ws && p.off_flags >= 0 ? reinterpret_cast<int32_t *>(ws + p.off_flags) + i : nullptr;
     if (K == 0) continue;
     const int64_t xb = d.mp * d.np * es, ab = d.mp * d.mp * es;
     const int nbuf = K >= 2 ? 2 : 1;
@@ -673,6 +679,24 @@ int dmuon_pack_offsets(const int64_t *numel, int32_t n, int64_t align, int64_t *
     end = start + numel[i];
   }
   *total_out = round_up(end, align);
+  return DMUON_OK;
+}
+
+int dmuon_nonfinite_flags_offset(const dmuon_matrix *mats, int32_t n, const dmuon_step_config *cfg,
+                                 size_t *offset_out) {
+  g_last_error.clear();
+  if (!offset_out) return fail(DMUON_ERR_INVALID_ARG, "offset_out is NULL");
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (!(cfg->flags & DMUON_FLAG_CHECK_FINITE))
+    return fail(DMUON_ERR_INVALID_ARG, "DMUON_FLAG_CHECK_FINITE is not set");
+  rc = validate_shapes(mats, n);
+  if (rc) return rc;
+  rc = validate_step_shapes(mats, n);
+  if (rc) return rc;
+  Plan p;
+  build_plan(mats, n, *cfg, nullptr, p);
+  *offset_out = static_cast<size_t>(p.off_flags);
   return DMUON_OK;
 }
 

@@ -41,6 +41,7 @@ struct MatDev {
   double *partials; // sum of U^2 per flat chunk (ns_steps = 0) or per
                     // 8192-element momentum-pass group (ns_steps >= 1)
   float *inv_norm;  // one float: 1 / (||U||_F + eps)
+  int32_t *nonfinite; // nullable: set to 1 when U holds a NaN or an Inf, else 0
   int64_t rows, cols;   // caller shape r x c
   int64_t m, n;         // wide orientation m = min(r, c), n = max(r, c)
   int64_t mp, np;       // m, n rounded up to kPad

@@ -204,3 +204,36 @@ def test_grads_read_from_packed_buffer(nsd):
     torch.cuda.synchronize()
     check_step(case, opts, ([to_host(p) for p in P], [to_host(m) for m in M],
                             [to_host(o) for o in O]), case.run_oracle(opts))
+
+
+@pytest.mark.parametrize("gram", [False, True])
+def test_check_finite_flags(nsd, gram):
+    """DMUON_FLAG_CHECK_FINITE reports, per matrix, a NaN or an Inf in U: a
+    NaN gradient element, an Inf momentum element, and a clean matrix.  The
+    flags are rewritten by every step (a clean second step reads 0), and the
+    outputs are those of a step without the flag, bit for bit."""
+    shapes = [(300, 700), (257, 1000), (700, 300)]
+    case = Case(shapes, "bf16", "bf16", seed=22, m_std=1e-3)
+    g0 = case.G[0].copy()
+    g0[3, 5] = np.nan
+    m1 = case.M[1].copy()
+    m1[7, 9] = np.inf
+    ws = nsd.Workspace()
+    opts = nsd.StepOptions(check_finite=True, gram_ns=gram)
+    plain = nsd.StepOptions(gram_ns=gram)
+    outs = {}
+    for name, o in (("checked", opts), ("plain", plain)):
+        bad = Case(shapes, "bf16", "bf16", seed=22, m_std=1e-3)
+        bad.G[0], bad.M[1] = g0, m1
+        outs[name] = bad.run_gpu(o, workspace=ws)
+        if name == "checked":
+            flags = nsd.nonfinite_flags([to_dev(p, "bf16") for p in bad.P], opts, ws).cpu().tolist()
+    say(f"  flags {flags}")
+    assert flags == [1, 1, 0]
+    for x, y in zip(outs["checked"], outs["plain"]):
+        for u, v in zip(x, y):
+            assert np.array_equal(u, v, equal_nan=True)
+    clean = Case(shapes, "bf16", "bf16", seed=23, m_std=1e-3)
+    clean.run_gpu(opts, workspace=ws)
+    flags = nsd.nonfinite_flags([to_dev(p, "bf16") for p in clean.P], opts, ws).cpu().tolist()
+    assert flags == [0, 0, 0]

@@ -133,3 +133,31 @@ def test_random_plans_are_consistent(seed):
             assert sum(f for _, f in L) == want
             if k > 0:
                 assert [x for x, _ in L].count("final") == 1
+
+
+def test_nonfinite_flags_offset():
+    """DMUON_FLAG_CHECK_FINITE: the int32[n] flags sit 256-byte aligned inside
+    the workspace, which grows by their slot; without the flag the offset
+    call is an error."""
+    lib = _lib.load()
+    shapes = [(300, 700), (17, 33), (513, 513)]
+    arr = (_lib.Matrix * 3)(*[_lib.Matrix(None, 0, 0, None, None, None, r, c, 1.0, 0, 0)
+                              for r, c in shapes])
+    off = ctypes.c_size_t(0)
+    plain = nsd.StepOptions().to_c()
+    assert lib.dmuon_nonfinite_flags_offset(arr, 3, ctypes.byref(plain), ctypes.byref(off)) == \
+        _lib.ERR_INVALID_ARG
+    for gram in (False, True):
+        for k in (0, 5):
+            opts = nsd.StepOptions(check_finite=True, gram_ns=gram, ns_steps=k)
+            cfg = opts.to_c()
+            assert lib.dmuon_nonfinite_flags_offset(arr, 3, ctypes.byref(cfg), None) == \
+                _lib.ERR_INVALID_ARG
+            assert lib.dmuon_nonfinite_flags_offset(arr, 3, ctypes.byref(cfg), ctypes.byref(off)) == \
+                _lib.OK
+            total, base = ctypes.c_size_t(0), ctypes.c_size_t(0)
+            _lib.check(lib.dmuon_workspace_bytes(arr, 3, ctypes.byref(cfg), ctypes.byref(total)))
+            cfg0 = nsd.StepOptions(gram_ns=gram, ns_steps=k).to_c()
+            _lib.check(lib.dmuon_workspace_bytes(arr, 3, ctypes.byref(cfg0), ctypes.byref(base)))
+            assert off.value % 256 == 0 and off.value + 12 <= total.value
+            assert total.value == base.value + 256
