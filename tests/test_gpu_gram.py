@@ -161,3 +161,23 @@ def test_gram_ill_conditioned_input_stays_near_direct_chain(nsd):
         errs[gram] = rel_fro(O[0], Ow[0])
     say(f"  rank-1 + noise: direct {errs[False]:.3e}, gram-space {errs[True]:.3e}")
     assert errs[True] < 1.2 * errs[False]
+
+
+def test_gram_nesterov(nsd):
+    """The look-ahead input G + mu*M through the Gram-space chain."""
+    case = Case([(300, 700), (1000, 257)], "bf16", "bf16", seed=37, m_std=1e-3)
+    opts = nsd.StepOptions(nesterov=True, gram_ns=True)
+    err = check_step(case, opts, case.run_gpu(opts), case.run_oracle(opts))
+    say(f"  worst O rel err {err:.3e}")
+
+
+def test_gram_zero_gradient_and_momentum(nsd):
+    """U = 0: A = 0, P = aI, Q = a^L I on every phase, and X stays 0, so O = 0
+    and the parameters are unchanged."""
+    case = Case([(300, 700), (700, 300)], "bf16", "bf16", seed=38)
+    case.G = [np.zeros_like(g) for g in case.G]
+    opts = nsd.StepOptions(gram_ns=True)
+    P, M, O = case.run_gpu(opts)
+    for i in range(2):
+        assert np.all(O[i] == 0) and np.all(M[i] == 0)
+        assert np.array_equal(P[i], case.P[i].astype(np.float64))
