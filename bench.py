@@ -374,7 +374,10 @@ def main(argv=None) -> int:
                    "ns_steps": K, "gram_ns": opts.gram_ns,
                    "param_dtype": w.param_dtype, "grad_dtype": w.grad_dtype,
                    "parallelism": "one owner's share on 1 GPU"},
+        # value over the peak (direct-chain flop count), and the executed
+        # flops' own fraction of the peak
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "executed_pct_bf16_peak": round(100 * executed / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "matrices_per_s": round(len(shapes) / (ms * 1e-3), 2),
         "steps_per_s": round(1e3 / ms, 3),
         "ns_chain": "gram-space where max(r,c) >= 2 min(r,c), direct otherwise" if opts.gram_ns
