@@ -161,3 +161,8 @@ def test_nonfinite_flags_offset():
             _lib.check(lib.dmuon_workspace_bytes(arr, 3, ctypes.byref(cfg0), ctypes.byref(base)))
             assert off.value % 256 == 0 and off.value + 12 <= total.value
             assert total.value == base.value + 256
+
+
+def test_launch_info_layout_matches_header():
+    assert ctypes.sizeof(_lib.LaunchInfo) == 16
+    assert _lib.LaunchInfo.kind.offset == 0 and _lib.LaunchInfo.flops.offset == 8
