@@ -227,6 +227,39 @@ void build_stage_tiles(const std::vector<MatDev> &mats, int st, std::vector<Tile
   }
 }
 
+// The tile lists depend only on the stage and the matrices' padded shapes
+// and dimensions, and a training run calls the step with the same shapes
+// every time: keep the last lists built (a small cache, cleared when full).
+std::mutex g_tiles_mu;
+std::map<std::vector<int64_t>, std::pair<std::vector<TileEntry>, StageXcd>> g_tiles_cache;
+constexpr size_t kTilesCacheMax = 64;
+
+void cached_stage_tiles(const std::vector<MatDev> &mats, int st, std::vector<TileEntry> &out,
+                        StageXcd &xcd) {
+  std::vector<int64_t> key;
+  key.reserve(1 + 4 * mats.size());
+  key.push_back(st);
+  for (const MatDev &d : mats) {
+    key.push_back(d.mp);
+    key.push_back(d.np);
+    key.push_back(d.tm);
+    key.push_back(d.tn);
+  }
+  {
+    std::lock_guard<std::mutex> lock(g_tiles_mu);
+    auto it = g_tiles_cache.find(key);
+    if (it != g_tiles_cache.end()) {
+      out = it->second.first;
+      xcd = it->second.second;
+      return;
+    }
+  }
+  build_stage_tiles(mats, st, out, xcd);
+  std::lock_guard<std::mutex> lock(g_tiles_mu);
+  if (g_tiles_cache.size() >= kTilesCacheMax) g_tiles_cache.clear();
+  g_tiles_cache.emplace(std::move(key), std::make_pair(out, xcd));
+}
+
 // Work-groups of the momentum / orientation pass for one matrix, 8192
 // elements each: a tall matrix (its own X^T) in contiguous 8192-element
 // runs, otherwise 64 x 128 blocks of X.  One sum-of-squares partial each.
@@ -425,7 +458,7 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
         for (int32_t i : p.groups[g]) shapes.push_back(p.mats[i]);
       p.lists.emplace_back();
       p.list_xcd.emplace_back();
-      build_stage_tiles(shapes, st, p.lists.back(), p.list_xcd.back());
+      cached_stage_tiles(shapes, st, p.lists.back(), p.list_xcd.back());
       li = list_of.emplace(key, static_cast<int32_t>(p.lists.size()) - 1).first;
     }
     l.list = li->second;
