@@ -181,3 +181,22 @@ def test_gram_zero_gradient_and_momentum(nsd):
     for i in range(2):
         assert np.all(O[i] == 0) and np.all(M[i] == 0)
         assert np.array_equal(P[i], case.P[i].astype(np.float64))
+
+
+def test_gram_fp32_mode_eight_steps(nsd):
+    """The fp32 checking mode through phases 2 + 2 + 2 + 2 (a CPU emulation
+    of fp32 storage gives about 5e-7)."""
+    case = Case([(300, 700), (700, 300), (100, 1000)], "f32", "f32", seed=39, g_std=1.0, m_std=0.5)
+    opts = nsd.StepOptions(ns_fp32=True, gram_ns=True, ns_steps=8)
+    err = check_step(case, opts, case.run_gpu(opts), case.run_oracle(opts))
+    say(f"  worst O rel err {err:.3e}")
+
+
+def test_gram_workspace_and_plan_reuse_across_shapes(nsd):
+    """One workspace, calls with different shape sets and back: the cached
+    tile lists are keyed by shape, and every call matches the oracle."""
+    ws = nsd.Workspace()
+    for shapes in ([(700, 1500), (513, 513)], [(300, 700), (17, 100)], [(700, 1500), (513, 513)]):
+        case = Case(shapes, "bf16", "bf16", seed=40, m_std=1e-3)
+        opts = nsd.StepOptions(gram_ns=True)
+        check_step(case, opts, case.run_gpu(opts, workspace=ws), case.run_oracle(opts))
