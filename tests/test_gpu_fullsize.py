@@ -126,3 +126,43 @@ def test_full_model_sets(nsd, wid, k_values, gram_ns):
         case, gpu = run_set(nsd, w, shapes, sample, opts)
         err = check_step(case, opts, gpu, case.run_oracle(opts))
         say(f"  worst O rel err {err:.3e}")
+
+
+@pytest.mark.parametrize("wid", [3, 4])
+def test_gram_and_direct_chains_agree_on_every_matrix(nsd, wid):
+    """Every matrix of the set, not a sample: the Gram-space step (merged
+    launches of both chains) and the direct-chain step, on the same device
+    inputs, give O within 3e-2 of each other per matrix (each is within
+    about 1.5e-2 of fp64 on these inputs).  A tile or table of a merged
+    launch that named the wrong matrix or buffer would show as a gross
+    mismatch on the matrices it touched."""
+    from synth import update_scale, workload
+    w = workload(wid)
+    shapes = [(r, c) for _, r, c in w.shapes]
+    if w.n_owners > 1:
+        owners, _ = nsd.partition_lpt([r * c for r, c in shapes], w.n_owners)
+        shapes = [s for s, o in zip(shapes, owners) if o == w.owner]
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    G = [(torch.randn(r, c, generator=gen, device=dev) * w.grad_std).to(torch.bfloat16)
+         for r, c in shapes]
+    P0 = [(torch.randn(r, c, generator=gen, device=dev) * w.param_std).to(torch.bfloat16)
+          for r, c in shapes]
+    scales = [update_scale(r, c) for r, c in shapes]
+    out = {}
+    for gram in (False, True):
+        P = [p.clone() for p in P0]
+        M = [torch.zeros(r, c, dtype=torch.float32, device=dev) for r, c in shapes]
+        O = [torch.empty_like(p) for p in P]
+        nsd.muon_step(P, G, M, scales, nsd.StepOptions(gram_ns=gram), orth_out=O)
+        torch.cuda.synchronize()
+        out[gram] = O
+        del P, M
+    worst = 0.0
+    for i, (r, c) in enumerate(shapes):
+        a, b = out[False][i].float(), out[True][i].float()
+        d = float(torch.linalg.norm(a - b) / torch.linalg.norm(a))
+        worst = max(worst, d)
+        assert d <= 3e-2, (i, (r, c), d)
+    say(f"{w.name}: {len(shapes)} matrices, worst direct/gram O difference {worst:.3e}")
