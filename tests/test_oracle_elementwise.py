@@ -78,11 +78,52 @@ def test_whole_step_closed_form(shape, nesterov):
     assert np.allclose(P1, P - lr * scale * O_want, rtol=0, atol=1e-15)
 
 
-def test_update_sign_and_scale():
-    P = random_case(26, 3, 4).astype(np.float64)
-    O = random_case(27, 3, 4).astype(np.float64)
-    P1 = muon.scaled_update(P, O, 0.5, 2.0)
-    assert np.allclose(P - P1, 1.0 * O, rtol=0, atol=1e-15)
+@pytest.mark.parametrize("shape", [(6, 10), (10, 6), (7, 7)])
+@pytest.mark.parametrize("nesterov", [False, True])
+def test_step_from_nonzero_momentum_closed_form(shape, nesterov):
+    """G = alpha Q and M0 = beta Q (Q with orthonormal rows or columns):
+    M1 = (mu beta + alpha) Q; the Newton-Schulz input is M1, or with
+    Nesterov the look-ahead G + mu M1 = (alpha + mu (mu beta + alpha)) Q.
+    eps is of the order of ||U||, so X0's singular value
+    u / (u sqrt(m) + eps) depends on the input's scale u and O tells the
+    inputs apart: a swapped look-ahead mu G + M1 (equal to the right one
+    only when M0 = 0) misses the closed form by far more than the tolerance.
+    """
+    r, c = shape
+    m = min(r, c)
+    Q = orthonormal(5, r, c)
+    alpha, beta, mu, lr, eps, scale = 0.37, -0.81, 0.9, 0.02, 0.6, 1.3
+    P = random_case(28, r, c, std=0.02).astype(np.float64)
+    cfg = muon.StepConfig(ns_steps=5, lr=lr, momentum=mu, eps=eps, nesterov=nesterov)
+    P1, M1, O = muon.muon_step_matrix(P, alpha * Q, beta * Q, scale, cfg)
+    assert np.allclose(M1, (mu * beta + alpha) * Q, rtol=0, atol=1e-15)
+
+    def o_for(u):
+        s0 = abs(u) / (abs(u) * math.sqrt(m) + eps)
+        return math.copysign(p_iter(s0, 5), u) * Q
+    u = alpha + mu * (mu * beta + alpha) if nesterov else mu * beta + alpha
+    assert np.allclose(O, o_for(u), rtol=0, atol=1e-13)
+    assert np.allclose(P1, P - lr * scale * o_for(u), rtol=0, atol=1e-15)
+    if nesterov:
+        swapped = mu * alpha + (mu * beta + alpha)
+        assert np.max(np.abs(o_for(swapped) - o_for(u))) > 1e-2
+
+
+def test_momentum_and_update_match_scalar_loops():
+    """Element-by-element Python float loops of M <- mu M + G and
+    P <- P - lr s O give the oracle's arrays bit for bit (both are one
+    correctly rounded fp64 multiply-add sequence per element)."""
+    G = random_case(26, 3, 4).astype(np.float64)
+    M0 = random_case(27, 3, 4).astype(np.float64)
+    P = random_case(29, 3, 4).astype(np.float64)
+    O = random_case(31, 3, 4).astype(np.float64)
+    mu, lr, s = 0.95, 0.02, 1.7
+    M1 = muon.momentum_accumulate(M0, G, mu)
+    P1 = muon.scaled_update(P, O, lr, s)
+    for i in range(3):
+        for j in range(4):
+            assert M1[i, j] == float(mu) * float(M0[i, j]) + float(G[i, j])
+            assert P1[i, j] == float(P[i, j]) - (lr * s) * float(O[i, j])
 
 
 def test_muon_step_list_is_per_matrix():
