@@ -67,7 +67,12 @@ enum { DMUON_FIELD_PARAM = 0, DMUON_FIELD_GRAD = 1 };
 /* dmuon_step_config.flags */
 enum {
   /* Keep X, A, B in fp32 through the Newton-Schulz chain (fp32 MFMA) instead
-   * of bf16.  A checking mode: slower, closer to exact arithmetic. */
+   * of bf16.  A checking mode: slower, closer to exact arithmetic.
+   * Without it (the bf16 chain), from ns_steps = 6 on, B = bA + cA^2 (and
+   * every P of the Gram-space chain) is stored as a pair of bf16 values,
+   * hi = RNE(v) and lo = RNE(v - hi), and each product that reads it runs
+   * one more pass over lo: the default quintic amplifies rounding errors on
+   * part of its band, and B's rounding is the largest contributor. */
   DMUON_FLAG_NS_FP32 = 1u << 0,
   /* Orthogonalise the look-ahead G + mu*M (after the momentum update)
    * instead of M. */
@@ -80,9 +85,9 @@ enum {
    * iteration P = aI + bA + cA^2, A <- A P^2, Q <- Q P, and X <- Q X once
    * per phase.  Same result in exact arithmetic; about 1.35x fewer flops at
    * n = 3.5m and ns_steps = 5.  Phases are two iterations (5 -> 2 + 2 + 1),
-   * each restarting from an explicit X, which keeps bf16 rounding of the
-   * accumulated Q at or below the direct chain's error on ill-conditioned
-   * inputs. */
+   * each restarting from an explicit X, which bounds the bf16 rounding of the
+   * accumulated Q: on a rank-one-plus-noise input (GPU test) the error stays
+   * within 1.2x of the direct chain's. */
   DMUON_FLAG_GRAM_NS = 1u << 2,
   /* Record, per matrix, whether the Newton-Schulz input U (M after the
    * momentum update, or the Nesterov look-ahead) holds a NaN or an Inf:
@@ -108,11 +113,12 @@ enum {
 typedef struct {
   int32_t kind;         /* DMUON_LAUNCH_*                                    */
   int32_t reserved;     /* 0                                                 */
-  double flops;         /* algorithmic flops of the GEMM launches (symmetric
+  double flops;         /* flops the GEMM launches execute (symmetric
                            products as their upper triangle: m(m+1)n for
                            A = X X^T, m^2(m+1) for an m x m product, 2m^2 n
-                           for an apply, summed over the launch's matrices);
-                           0 for the element-wise launches                   */
+                           for an apply, times the passes over bf16 hi + lo
+                           pairs, summed over the launch's matrices); 0 for
+                           the element-wise launches                         */
 } dmuon_launch_info;
 
 /* One matrix of the owner's share. */
@@ -129,7 +135,8 @@ typedef struct {
   float scale;          /* per-matrix update scale (finite)                  */
   int32_t reserved;     /* must be 0                                         */
   int64_t packed_offset;/* element offset of this matrix in the packed
-                           buffer (dmuon_pack / dmuon_unpack only)           */
+                           buffer (read by dmuon_pack, dmuon_unpack and
+                           dmuon_muon_step_packed only)                      */
 } dmuon_matrix;
 
 /* Step hyper-parameters.  The landing page's optimizer call uses lr = 0.02
@@ -296,9 +303,12 @@ int dmuon_muon_step_packed(const dmuon_matrix *mats, int32_t n,
  * first launch and events[j] right after the j-th launch.  Launch order:
  * with ns_steps = 0: momentum + sum of squares, norm, direct update; with
  * ns_steps >= 1: momentum + sum of squares + wide orientation, norm, then
- * Gram, Square, Apply for each iteration (the last Apply carries the
- * parameter update) over the direct-chain matrices, then the Gram-space
- * chain's launches (DMUON_FLAG_GRAM_NS); dmuon_step_launches lists them.
+ * the Newton-Schulz launches.  The direct chain runs Gram, Square, Apply
+ * per iteration (the last Apply carries the parameter update); with
+ * DMUON_FLAG_GRAM_NS the Gram-space chain's launches are merged into that
+ * sequence, each chain keeping its order and a launch of each chain of the
+ * same kind becoming one grouped launch (along a longest common subsequence
+ * of the two kind sequences); dmuon_step_launches lists the result.
  * Only the first
  * n_events are recorded; n_events = 0 makes this dmuon_muon_step.
  * Errors: those of dmuon_muon_step; INVALID_ARG for n_events < 0 or a NULL

@@ -25,6 +25,12 @@
 //           also stored to the packed slot when the step has one, and X'
 //           to orth_out; no workspace write
 //
+// From six iterations on, B (and every P of the Gram-space chain) is kept
+// as a bf16 hi + lo pair, hi = RNE(v), lo = RNE(v - hi): Square stores both
+// halves, and a product that reads a pair runs its K loop over one more
+// pass, (L, R) then (L, R_lo) and/or (L_lo, R), accumulating into the same
+// tile.
+//
 // Every product is C[i][j] = sum_k L[i][k] R[j][k].  Square and Apply read
 // both operands k-contiguous (row-major L and R), the layout the MFMA
 // instructions take; Gram's operands have k down the rows and are turned
@@ -192,6 +198,15 @@ __device__ __forceinline__ int tile_swz(int row, int chunk) {
   return SW == kSwzRows ? chunk ^ (((row >> 2) & 3) << 1) : chunk ^ ((row & 7) << 1);
 }
 
+// The low half of a bf16 hi + lo pair: v - RNE(v), exact in fp32 (it is
+// rounded to bf16 when stored).
+__device__ __forceinline__ f32x4 bf16_low_part(const f32x4 &v) {
+  f32x4 r;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) r[k] = v[k] - bf16_bits_to_f32(f32_to_bf16_bits(v[k]));
+  return r;
+}
+
 // Puts rows r0 .. r0+3 of column c (one lane's four values) as bf16.
 __device__ __forceinline__ void stage_tile_put(lds_char *lds, int r0, int c, const f32x4 &v) {
   typedef __attribute__((address_space(3))) uint16_t lds_u16;
@@ -237,6 +252,9 @@ __device__ __forceinline__ void stage_tile_put_t(lds_char *lds, int r, int c0, c
 template <int SW>
 __device__ __forceinline__ void stage_tile_flush(lds_char *lds, uint16_t *dst, int64_t ld, int tid) {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // opaque: each flush rebuilds its addresses instead of keeping them live
+  // across the epilogue's other flushes
+  asm volatile("" : "+v"(tid));
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int f = q * 512 + tid;
@@ -267,6 +285,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   constexpr bool kMN = MODE == kModeGram;
   constexpr int kKStep = kRowBytes / static_cast<int>(sizeof(T));  // K elements per step
   const T *L, *R;
+  const T *Llo = nullptr, *Rlo = nullptr;  // low halves of hi + lo operand pairs
   int64_t ld;  // elements; both operands have the same leading dimension
   if (MODE == kModeGram) {
     L = R = static_cast<const T *>(d.xt[0]);
@@ -274,18 +293,36 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   } else if (MODE == kModeSquare) {
     L = static_cast<const T *>(d.a);
     R = d.sq_r ? static_cast<const T *>(d.sq_r) : L;
+    if constexpr (sizeof(T) == 2) {
+      Llo = static_cast<const T *>(d.l_lo);
+      Rlo = static_cast<const T *>(d.sq_r ? d.r_lo : d.l_lo);
+    }
     ld = d.mp;
   } else {
     L = static_cast<const T *>(d.b);
     R = static_cast<const T *>(d.xt[0]);
+    if constexpr (sizeof(T) == 2) Llo = static_cast<const T *>(d.l_lo);
     ld = d.mp;
   }
   const int64_t ld_bytes = ld * static_cast<int64_t>(sizeof(T));
   const int nkt = kMN ? static_cast<int>(d.np / kKStep) : static_cast<int>(ld_bytes / kRowBytes);
   // K-contiguous: the tile's 256 rows; MN-major: the tile's 256 columns
   const int64_t tile_stride = kMN ? kTile * static_cast<int64_t>(sizeof(T)) : kTile * ld_bytes;
-  const char *gl = reinterpret_cast<const char *>(L) + static_cast<int64_t>(ti) * tile_stride;
-  const char *gr = reinterpret_cast<const char *>(R) + static_cast<int64_t>(tj) * tile_stride;
+  auto panel = [&](const T *base, int32_t t) {
+    return reinterpret_cast<const char *>(base) + static_cast<int64_t>(t) * tile_stride;
+  };
+  // The K loop runs over one to three passes of the operand panels: (L, R),
+  // then (L, R_lo) when R is a hi + lo pair, then (L_lo, R) when L is; all
+  // accumulate into the same tile.  Pass s covers steps [s*nkt, (s+1)*nkt).
+  const bool r_pair = Rlo != nullptr, l_pair = Llo != nullptr;
+  const char *const gl = panel(L, ti), *const gr = panel(R, tj);
+  const char *const gl_lo = l_pair ? panel(Llo, ti) : gl;
+  const char *const gl1 = r_pair ? gl : gl_lo;
+  const char *const gr1 = r_pair ? panel(Rlo, tj) : gr;
+  // pass s reads L at gl + s1*dl1 + s2*dl2 (s1 = s >= 1, s2 = s >= 2), and
+  // R likewise: byte distances, so that picking a pass is arithmetic
+  const int64_t dl1 = gl1 - gl, dl2 = gl_lo - gl1, dr1 = gr1 - gr, dr2 = gr - gr1;
+  const int ntot = (1 + r_pair + l_pair) * nkt;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -317,8 +354,11 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   const uint32_t goff_step = static_cast<uint32_t>(4 * kRowsPerKB) * static_cast<uint32_t>(ld_bytes);
   auto issue = [&](int slot, int kt) {
     lds_char *st = lds + slot * kStageBytes;
-    const int64_t kofs = kMN ? static_cast<int64_t>(kt) * kKStep * ld_bytes : static_cast<int64_t>(kt) * kRowBytes;
-    const char *const bl = gl + kofs, *const br = gr + kofs;  // uniform
+    const int s1 = kt >= nkt, s2 = kt >= 2 * nkt;  // pass of step kt (uniform)
+    const int kk = kt - (s1 + s2) * nkt;
+    const int64_t kofs = kMN ? static_cast<int64_t>(kk) * kKStep * ld_bytes : static_cast<int64_t>(kk) * kRowBytes;
+    const char *const bl = gl + (kofs + s1 * dl1 + s2 * dl2);  // uniform
+    const char *const br = gr + (kofs + s1 * dr1 + s2 * dr2);
     // opaque copy: the per-instruction offsets are rebuilt at every issue
     // instead of being kept live across the mainloop
     uint32_t g0 = goff0;
@@ -472,6 +512,9 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   const bool sq_cap = MODE == kModeSquare && d.cc != 0.f && __builtin_isfinite(sq_w);
   const float cap_w = MODE == kModeSquare ? (sq_cap ? sq_w : 0.f) : d.ca;
   const int cap_kt0 = ti * (kTile / kKStep) + wm * kCapSteps;
+  // Only the first pass of the K loop captures: its R is R itself (later
+  // passes read R_lo or run past kt = nkt, where c >= kCapSteps); the host
+  // gives a capturing Square no hi + lo operand.
   // Step c of the wave's kCapSteps holds fragment rows [c*kCapFrags,
   // (c+1)*kCapFrags).  Every fragment row reads and adds at every capture
   // step, with weight a on its own step and 0 on the others (at an address
@@ -524,9 +567,9 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   issue(0, 0);
   stage_barrier();
   if (wm == 1) plain_barrier();
-  for (int kt = 0; kt < nkt; ++kt) {
+  for (int kt = 0; kt < ntot; ++kt) {
     const lds_char *st = lds + (kt & 1) * kStageBytes;
-    issue((kt + 1) & 1, min(kt + 1, nkt - 1));
+    issue((kt + 1) & 1, min(kt + 1, ntot - 1));
     capture_ax(st, kt);
     read_frag(st, 0, fa);
     read_frag(st, 1, fb);
@@ -623,18 +666,52 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
       }
     }
     if constexpr (kStage) {
+      const int64_t tile_ij = static_cast<int64_t>(ti) * kTile * mp + static_cast<int64_t>(tj) * kTile;
+      const int64_t tile_ji = static_cast<int64_t>(tj) * kTile * mp + static_cast<int64_t>(ti) * kTile;
+      // hi half (the output itself), then, for a hi + lo pair, the low half
+      // lo = RNE(v - RNE(v)); each as the tile and, off the diagonal, its
+      // mirror tile (tj, ti) staged the transposed way
       uint16_t *const o16 = reinterpret_cast<uint16_t *>(out);
-      stage_tile_flush<kSwzRows>(lds, o16 + static_cast<int64_t>(ti) * kTile * mp + static_cast<int64_t>(tj) * kTile,
-                                 mp, tid);
-      if (ti != tj) {  // the mirror tile (tj, ti), staged the transposed way
+      uint16_t *const lo16 = MODE == kModeSquare ? reinterpret_cast<uint16_t *>(d.out_lo) : nullptr;
+      stage_tile_flush<kSwzRows>(lds, o16 + tile_ij, mp, tid);
+      if (ti != tj) {
         lds_barrier();
 #pragma unroll
         for (int i = 0; i < kFragM; ++i)
 #pragma unroll
           for (int j = 0; j < kFragN; ++j)
             stage_tile_put_t(lds, wn * kWaveN + j * 16 + r16, wm * kWaveM + i * 16 + 4 * g4, acc[i][j]);
-        stage_tile_flush<kSwzCols>(lds, o16 + static_cast<int64_t>(tj) * kTile * mp + static_cast<int64_t>(ti) * kTile,
-                                   mp, tid);
+        stage_tile_flush<kSwzCols>(lds, o16 + tile_ji, mp, tid);
+      }
+      if (lo16) {
+        // The low halves go to the same LDS slots as the high ones: opaque
+        // lane coordinates make the compiler rebuild those addresses here
+        // rather than keep them live through the flushes above.
+        int lo_lane = lane;
+        asm volatile("" : "+v"(lo_lane));
+        const int lr16 = lo_lane & 15, lg4 = lo_lane >> 4;
+        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < kFragM; ++i)
+#pragma unroll
+          for (int j = 0; j < kFragN; ++j) {
+            const f32x4 lo = bf16_low_part(acc[i][j]);
+            if (ti != tj)
+              stage_tile_put(lds, wm * kWaveM + i * 16 + 4 * lg4, wn * kWaveN + j * 16 + lr16, lo);
+            else
+              stage_tile_put_sym(lds, wm * kWaveM + i * 16 + 4 * lg4, wn * kWaveN + j * 16 + lr16, lo);
+          }
+        stage_tile_flush<kSwzRows>(lds, lo16 + tile_ij, mp, tid);
+        if (ti != tj) {
+          lds_barrier();
+#pragma unroll
+          for (int i = 0; i < kFragM; ++i)
+#pragma unroll
+            for (int j = 0; j < kFragN; ++j)
+              stage_tile_put_t(lds, wn * kWaveN + j * 16 + lr16, wm * kWaveM + i * 16 + 4 * lg4,
+                               bf16_low_part(acc[i][j]));
+          stage_tile_flush<kSwzCols>(lds, lo16 + tile_ji, mp, tid);
+        }
       }
     }
   } else if (MODE == kModeApply) {
@@ -663,7 +740,8 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
     // wm == h hold half h): row-major when P = O (m x n), transposed when
     // P = O^T (n x m).  Then all threads update P in four-element pieces
     // along its rows: P -= lr*scale*O, and orth_out = O.  The aX term is
-    // read here (X^T[col][row .. row+3], one vector per fragment).
+    // already in the accumulators: it was captured from the X^T tile in LDS
+    // during the mainloop, as in Apply.
     const float step = s.lr * d.scale;
     const bool tp = d.transposed != 0;
     const bool vec_ok = (d.cols & 3) == 0;  // rows of P start 4-element aligned

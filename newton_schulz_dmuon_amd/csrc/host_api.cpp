@@ -4,6 +4,7 @@
 // rejected call has no effect on any buffer.
 
 #include <algorithm>
+#include <array>
 #include <cstdarg>
 #include <cmath>
 #include <cstdio>
@@ -135,19 +136,33 @@ enum LaunchKind : int32_t {
 };
 
 // Workspace buffers a GEMM launch can name per matrix: the direct chain uses
-// A and B; the Gram-space chain also A', T, Q0, Q1 (m_p x m_p each).
-enum Buf : int32_t { kBufNone = -1, kBufA = 0, kBufB, kBufA1, kBufT, kBufQ0, kBufQ1, kBufCount };
+// A and B; the Gram-space chain also A', T, Q0, Q1 (m_p x m_p each).  With
+// hi + lo pairs (split_pairs), B_lo holds the low half of B (direct chain)
+// or of a later iteration's P (Gram-space chain), Q0_lo that of the first P.
+enum Buf : int32_t {
+  kBufNone = -1, kBufA = 0, kBufB, kBufA1, kBufT, kBufQ0, kBufQ1, kBufBlo, kBufQ0lo, kBufCount
+};
 
 // One part of a grouped GEMM launch: a group of matrices (0 direct chain, 1
 // Gram-space chain) and, for every matrix of it, which buffer each MatDev
 // pointer names (a: Gram output, Square L; b: Square output, Apply L; r:
-// Square R), which X^T buffer is read (cur; the other one is written), and
+// Square R; l_lo, r_lo: low halves of L and R; o_lo: low half of a Square
+// output), which X^T buffer is read (cur; the other one is written), and
 // the stage's coefficients.
 struct Part {
   int32_t group, a, b, r, cur, first;
   float ca, cb, cc, cdiag;
-  auto key() const { return std::make_tuple(group, a, b, r, cur, first, ca, cb, cc, cdiag); }
+  int32_t l_lo = kBufNone, r_lo = kBufNone, o_lo = kBufNone;
+  auto key() const {
+    return std::make_tuple(group, a, b, r, cur, first, ca, cb, cc, cdiag, l_lo, r_lo, o_lo);
+  }
   bool operator<(const Part &o) const { return key() < o.key(); }
+  // passes of the K loop (each a full product): 1 + one per low half read;
+  // a Square without its own R reads L twice
+  int32_t passes(int32_t kind) const {
+    const bool r_split = r_lo != kBufNone || (kind == DMUON_LAUNCH_SQUARE && r == kBufNone && l_lo != kBufNone);
+    return 1 + (l_lo != kBufNone) + (kind == DMUON_LAUNCH_SQUARE && r_split);
+  }
 };
 
 struct Launch {
@@ -160,7 +175,10 @@ struct Launch {
 
 struct Plan {
   std::vector<MatDev> mats;                   // every matrix: table 0
-  std::vector<std::vector<void *>> extra;     // Gram-space buffers A', T, Q0, Q1 per matrix
+  // per matrix, the buffers beyond A and B (index buf - kBufA1; nullptr in
+  // the sizing pass) and a bit mask of the ones it has
+  std::vector<std::array<void *, kBufCount - kBufA1>> extra;
+  std::vector<uint32_t> have;
   std::vector<int32_t> groups[2];             // matrix indices: direct chain, Gram-space chain
   std::vector<std::vector<Part>> tables;      // tables 1..: the parts of a launch
   std::vector<std::vector<TileEntry>> lists;
@@ -182,8 +200,8 @@ struct Plan {
 // to the XCD with the least work so far; each XCD's list keeps that order, so
 // its 32 CUs work through long-K tiles first and the tiles running together
 // on one XCD read few distinct panels through its L2.
-void build_stage_tiles(const std::vector<MatDev> &mats, int st, std::vector<TileEntry> &out,
-                       StageXcd &xcd) {
+void build_stage_tiles(const std::vector<MatDev> &mats, const std::vector<int32_t> &passes, int st,
+                       std::vector<TileEntry> &out, StageXcd &xcd) {
   struct Block {
     int64_t cost;
     int32_t mat, ti0, tj0;
@@ -193,7 +211,7 @@ void build_stage_tiles(const std::vector<MatDev> &mats, int st, std::vector<Tile
   std::vector<Block> blocks;
   for (int32_t i = 0; i < static_cast<int32_t>(mats.size()); ++i) {
     const MatDev &d = mats[i];
-    const int64_t depth = st == 0 ? d.np : d.mp;
+    const int64_t depth = (st == 0 ? d.np : d.mp) * passes[i];
     const int32_t rows = d.tm, cols = sym ? d.tm : d.tn;
     for (int32_t bi = 0; bi < rows; bi += bm)
       for (int32_t bj = sym ? bi : 0; bj < cols; bj += bn) {
@@ -234,16 +252,18 @@ std::mutex g_tiles_mu;
 std::map<std::vector<int64_t>, std::pair<std::vector<TileEntry>, StageXcd>> g_tiles_cache;
 constexpr size_t kTilesCacheMax = 64;
 
-void cached_stage_tiles(const std::vector<MatDev> &mats, int st, std::vector<TileEntry> &out,
-                        StageXcd &xcd) {
+void cached_stage_tiles(const std::vector<MatDev> &mats, const std::vector<int32_t> &passes, int st,
+                        std::vector<TileEntry> &out, StageXcd &xcd) {
   std::vector<int64_t> key;
-  key.reserve(1 + 4 * mats.size());
+  key.reserve(1 + 5 * mats.size());
   key.push_back(st);
-  for (const MatDev &d : mats) {
+  for (size_t i = 0; i < mats.size(); ++i) {
+    const MatDev &d = mats[i];
     key.push_back(d.mp);
     key.push_back(d.np);
     key.push_back(d.tm);
     key.push_back(d.tn);
+    key.push_back(passes[i]);
   }
   {
     std::lock_guard<std::mutex> lock(g_tiles_mu);
@@ -254,7 +274,7 @@ void cached_stage_tiles(const std::vector<MatDev> &mats, int st, std::vector<Til
       return;
     }
   }
-  build_stage_tiles(mats, st, out, xcd);
+  build_stage_tiles(mats, passes, st, out, xcd);
   std::lock_guard<std::mutex> lock(g_tiles_mu);
   if (g_tiles_cache.size() >= kTilesCacheMax) g_tiles_cache.clear();
   g_tiles_cache.emplace(std::move(key), std::make_pair(out, xcd));
@@ -277,6 +297,19 @@ bool uses_gram(const MatDev &d, const dmuon_step_config &cfg) {
   return (cfg.flags & DMUON_FLAG_GRAM_NS) && cfg.ns_steps >= 5 && d.n >= 2 * d.m;
 }
 
+// From six iterations on, the bf16 chain keeps B (direct chain) and every P
+// (Gram-space chain) as hi + lo pairs.  The default quintic amplifies
+// rounding errors on part of its band, and the rounding of B (or P) is the
+// largest contributor: in a bf16 emulation on Gaussian inputs of the
+// Qwen2.5-7B and Qwen2.5-1.5B shapes, pairs take the error at 8 iterations
+// from 1.5-2.7e-2 to 0.7-1.4e-2, where keeping X or A in fp32 instead
+// changes it by 1-10%.  Up to five iterations bf16 storage stays below
+// about 1.4e-2 on those inputs, so the pairs' extra passes are not paid.
+constexpr int kSplitFromSteps = 6;
+bool split_pairs(const dmuon_step_config &cfg) {
+  return !(cfg.flags & DMUON_FLAG_NS_FP32) && cfg.ns_steps >= kSplitFromSteps;
+}
+
 // Phases of the Gram-space chain: two iterations each, the last one a
 // single iteration when K is odd (5 -> 2 + 2 + 1, 8 -> 2 + 2 + 2 + 2).  Each
 // phase starts from an explicit X (a fresh A = X X^T) and ends with
@@ -296,8 +329,10 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
   const bool fp32 = cfg.flags & DMUON_FLAG_NS_FP32;
   const int64_t es = fp32 ? 4 : 2;
   const int K = cfg.ns_steps;
+  const bool split = split_pairs(cfg);
   p.mats.resize(n);
   p.extra.assign(n, {});
+  p.have.assign(n, 0);
   p.groups[0].clear();
   p.groups[1].clear();
   int64_t ew = 0, tr = 0;
@@ -349,18 +384,25 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
     Launch l;
     l.kind = kind;
     l.parts = std::move(parts);
-    for (const Part &pt : l.parts) l.flops += flops(pt.group, kind);
+    // executed flops: every pass of the K loop is a full product
+    for (const Part &pt : l.parts) l.flops += flops(pt.group, kind) * pt.passes(kind);
     chain.push_back(std::move(l));
   };
   std::vector<Launch> chain[2];
   if (K > 0 && !p.groups[0].empty()) {
-    // direct chain: K x (A = X X^T; B = b A + c A A; X <- a X + B X)
+    // direct chain: K x (A = X X^T; B = b A + c A A; X <- a X + B X); with
+    // pairs, Square also stores B's low half and Apply reads it
     for (int k = 0; k < K; ++k) {
       const int32_t cur = k & 1, first = k == 0;
       const Part pt{0, kBufA, kBufB, kBufNone, cur, first, cfg.a, cfg.b, cfg.c, 0.f};
+      Part sq = pt, ap = pt;
+      if (split) {
+        sq.o_lo = kBufBlo;
+        ap.l_lo = kBufBlo;
+      }
       gemm(chain[0], kLkGram, {pt});
-      gemm(chain[0], kLkSquare, {pt});
-      gemm(chain[0], k + 1 == K ? kLkFinal : kLkApply, {pt});
+      gemm(chain[0], kLkSquare, {sq});
+      gemm(chain[0], k + 1 == K ? kLkFinal : kLkApply, {ap});
     }
   }
   if (K > 0 && !p.groups[1].empty()) {
@@ -372,7 +414,11 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
     // commuting symmetric matrices: upper tiles + mirror.  P of the first
     // iteration is written to Q0 and is Q.  T = P P and Q P both read only
     // P: one launch.
+    // With pairs, every P is stored as hi + lo (the first in Q0 / Q0_lo,
+    // later ones in B / B_lo) and read as such by P P, Q P and, when Q is
+    // still the first P (a phase of one iteration), by X <- Q X.
     const std::vector<int> phases = gram_phases(K);
+    auto lo_of = [&](int32_t buf) { return !split ? kBufNone : buf == kBufQ0 ? kBufQ0lo : kBufBlo; };
     int32_t cur = 0;
     for (size_t ph = 0; ph < phases.size(); ++ph) {
       const int32_t first = ph == 0, last_phase = ph + 1 == phases.size();
@@ -381,15 +427,26 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
       };
       gemm(chain[1], kLkGram, {Part{1, kBufA, kBufB, kBufNone, cur, first, 0.f, 0.f, 0.f, 0.f}});
       int32_t acur = kBufA, anext = kBufA1, qcur = kBufQ0;
+      bool q_is_p0 = true;  // Q still holds the phase's first P (a pair)
       for (int i = 0; i < phases[ph]; ++i) {
         const int32_t pbuf = i == 0 ? kBufQ0 : kBufB;
-        gemm(chain[1], kLkSquare, {part(acur, pbuf, kBufNone, cfg.b, cfg.c, cfg.a)});  // P
+        Part pp = part(acur, pbuf, kBufNone, cfg.b, cfg.c, cfg.a);  // P
+        pp.o_lo = lo_of(pbuf);
+        gemm(chain[1], kLkSquare, {pp});
         std::vector<Part> next;
-        if (i + 1 < phases[ph]) next.push_back(part(pbuf, kBufT, kBufNone, 0.f, 1.f, 0.f));  // T = P P
+        if (i + 1 < phases[ph]) {
+          Part t = part(pbuf, kBufT, kBufNone, 0.f, 1.f, 0.f);  // T = P P
+          t.l_lo = lo_of(pbuf);
+          next.push_back(t);
+        }
         if (i > 0) {
           const int32_t qnext = qcur == kBufQ0 ? kBufQ1 : kBufQ0;
-          next.push_back(part(qcur, qnext, pbuf, 0.f, 1.f, 0.f));  // Q P
+          Part qp = part(qcur, qnext, pbuf, 0.f, 1.f, 0.f);  // Q P
+          qp.l_lo = q_is_p0 ? lo_of(qcur) : kBufNone;
+          qp.r_lo = lo_of(pbuf);
+          next.push_back(qp);
           qcur = qnext;
+          q_is_p0 = false;
         }
         if (!next.empty()) gemm(chain[1], kLkSquare, next);
         if (i + 1 < phases[ph]) {
@@ -397,8 +454,9 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
           std::swap(acur, anext);
         }
       }
-      gemm(chain[1], last_phase ? kLkFinal : kLkApply,
-           {Part{1, kBufA, qcur, kBufNone, cur, first, 0.f, 0.f, 0.f, 0.f}});
+      Part ap{1, kBufA, qcur, kBufNone, cur, first, 0.f, 0.f, 0.f, 0.f};
+      ap.l_lo = q_is_p0 ? lo_of(qcur) : kBufNone;
+      gemm(chain[1], last_phase ? kLkFinal : kLkApply, {ap});
       cur ^= 1;
     }
   }
@@ -448,17 +506,24 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
     }
     l.table = t->second;
     const int32_t st = l.kind == kLkGram ? 0 : l.kind == kLkSquare ? 1 : 2;
-    std::vector<int32_t> gs;
-    for (const Part &pt : l.parts) gs.push_back(pt.group);
+    std::vector<int32_t> gs;  // (group, passes) of every part
+    for (const Part &pt : l.parts) {
+      gs.push_back(pt.group);
+      gs.push_back(pt.passes(l.kind));
+    }
     auto key = std::make_pair(st, gs);
     auto li = list_of.find(key);
     if (li == list_of.end()) {
       std::vector<MatDev> shapes;
-      for (int32_t g : gs)
-        for (int32_t i : p.groups[g]) shapes.push_back(p.mats[i]);
+      std::vector<int32_t> passes;
+      for (size_t q = 0; q < gs.size(); q += 2)
+        for (int32_t i : p.groups[gs[q]]) {
+          shapes.push_back(p.mats[i]);
+          passes.push_back(gs[q + 1]);
+        }
       p.lists.emplace_back();
       p.list_xcd.emplace_back();
-      cached_stage_tiles(shapes, st, p.lists.back(), p.list_xcd.back());
+      cached_stage_tiles(shapes, passes, st, p.lists.back(), p.list_xcd.back());
       li = list_of.emplace(key, static_cast<int32_t>(p.lists.size()) - 1).first;
     }
     l.list = li->second;
@@ -512,12 +577,17 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
     off = round_up(off + ab, 256);
     d.b = ws ? ws + off : nullptr;
     off = round_up(off + ab, 256);
-    if (uses_gram(d, cfg)) {
-      p.extra[i].resize(4);
-      for (int b = 0; b < 4; ++b) {
-        p.extra[i][b] = ws ? ws + off : nullptr;
-        off = round_up(off + ab, 256);
-      }
+    auto add = [&](int32_t buf) {
+      p.extra[i][buf - kBufA1] = ws ? ws + off : nullptr;
+      p.have[i] |= 1u << buf;
+      off = round_up(off + ab, 256);
+    };
+    p.have[i] |= (1u << kBufA) | (1u << kBufB);
+    if (uses_gram(d, cfg))
+      for (int32_t b : {kBufA1, kBufT, kBufQ0, kBufQ1}) add(b);
+    if (split) {
+      add(kBufBlo);
+      if (uses_gram(d, cfg)) add(kBufQ0lo);
     }
   }
   p.total_bytes = off;
@@ -535,10 +605,15 @@ bool plan_consistent(const Plan &p) {
     std::vector<const MatDev *> rows;
     for (const Part &pt : p.tables[l.table - 1]) {
       if (pt.group < 0 || pt.group > 1) return false;
+      // a capturing Square (b A from its R tile) must not read a pair: the
+      // capture is taken in the first pass only
+      if (l.kind == kLkSquare && pt.cb != 0.f && (pt.l_lo != kBufNone || pt.r_lo != kBufNone)) return false;
+      if (l.kind != kLkSquare && (pt.r_lo != kBufNone || pt.o_lo != kBufNone)) return false;
+      if (l.kind == kLkGram && pt.l_lo != kBufNone) return false;
       for (int32_t i : p.groups[pt.group]) {
         rows.push_back(&p.mats[i]);
-        const bool gram_buf = pt.a >= kBufA1 || pt.b >= kBufA1 || pt.r >= kBufA1;
-        if (gram_buf && p.extra[i].size() != 4) return false;
+        for (int32_t b : {pt.a, pt.b, pt.r, pt.l_lo, pt.r_lo, pt.o_lo})
+          if (b != kBufNone && !(p.have[i] >> b & 1u)) return false;
         // the second X^T buffer is read (cur = 1) or written (Apply); the
         // sizing pass has no addresses yet
         const bool needs_xt1 = pt.cur || l.kind == kLkApply;
@@ -574,6 +649,9 @@ std::vector<MatDev> table_contents(const Plan &p, size_t t) {
       d.a = buf(pt.a);
       d.b = buf(pt.b);
       d.sq_r = buf(pt.r);
+      d.l_lo = buf(pt.l_lo);
+      d.r_lo = buf(pt.r_lo);
+      d.out_lo = buf(pt.o_lo);
       if (pt.cur) std::swap(d.xt[0], d.xt[1]);
       d.ca = pt.ca;
       d.cb = pt.cb;

@@ -38,6 +38,15 @@ struct MatDev {
   void *a;          // m_p x m_p: A = X X^T (Gram output, Square's L operand)
   void *b;          // m_p x m_p: B = b A + c A A (Square output, Apply's L operand)
   const void *sq_r; // Square's R operand; nullptr: R = a (the product A A)
+  // Low halves of bf16 hi + lo pairs (nullable; bf16 chain only).  A pair
+  // holds v as hi = RNE(v) and lo = RNE(v - hi), about 16 significant bits.
+  // An operand with a low half adds a pass over it to the K loop:
+  // L R^T = L R^T + L R_lo^T + L_lo R^T (the lo x lo term is below fp32
+  // accumulation noise).  When sq_r is nullptr, R = L and R's low half is
+  // l_lo.
+  const void *l_lo;  // low half of Square's L (a) or Apply's L (b)
+  const void *r_lo;  // low half of Square's sq_r
+  void *out_lo;      // Square: also store the low half of the output here
   double *partials; // sum of U^2 per flat chunk (ns_steps = 0) or per
                     // 8192-element momentum-pass group (ns_steps >= 1)
   float *inv_norm;  // one float: 1 / (||U||_F + eps)

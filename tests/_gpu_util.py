@@ -102,8 +102,10 @@ def check_step(case: Case, opts, gpu, want, tol_o=None):
         if Og is not None:
             eo = rel_fro(Og[i], Ow[i])
             worst = max(worst, eo)
-            # orth_out is rounded to the param dtype: allow that rounding too
-            extra = 2.0 ** -8 if case.pdt == "bf16" else 0.0
+            # orth_out is rounded to the param dtype: RNE to bf16 moves each
+            # element by at most 2^-9 of itself, so the relative Frobenius
+            # error grows by at most 2^-9
+            extra = 2.0 ** -9 if case.pdt == "bf16" else 0.0
             assert eo <= tol_o + extra, (i, (r, c), "O", eo)
         P0 = case.P[i].astype(np.float64)
         step = opts.lr * case.scales[i]

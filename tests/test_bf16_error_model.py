@@ -18,11 +18,50 @@ def qwen7b_k():
 
 @pytest.mark.parametrize("k,lo,hi", [(3, 1e-3, 6e-3), (5, 8e-3, 2e-2), (8, 2e-2, 3e-2)])
 def test_bf16_storage_error_grows_with_iterations(qwen7b_k, k, lo, hi):
+    """bf16 storage of every intermediate (no pairs): the error grows with
+    the iteration count and passes the 2e-2 bar at 8 iterations."""
     ref = muon.newton_schulz(qwen7b_k, *muon.QUINTIC, k)
-    emu = ns_bf16_storage(qwen7b_k, *muon.QUINTIC, k)
+    emu = ns_bf16_storage(qwen7b_k, *muon.QUINTIC, k, pairs=False)
     err = np.linalg.norm(emu - ref) / np.linalg.norm(ref)
     assert lo < err < hi, err
-    assert err < tol_o_bf16(k) / 1.4
+    assert (err < tol_o_bf16(k) / 1.4) == (k <= 5)
+
+
+@pytest.mark.parametrize("k", [6, 7, 8])
+def test_pairs_bring_long_chains_within_the_bar(qwen7b_k, k):
+    """With B stored as a hi + lo pair (the library, from six iterations on)
+    the same input stays within the bar with room, at every iteration count
+    up to 8, with the first X rounded (as here) or exact (as on the GPU)."""
+    ref = muon.newton_schulz(qwen7b_k, *muon.QUINTIC, k)
+    for round_x0 in (True, False):
+        emu = ns_bf16_storage(qwen7b_k, *muon.QUINTIC, k, round_x0=round_x0)
+        err = np.linalg.norm(emu - ref) / np.linalg.norm(ref)
+        assert err < tol_o_bf16(k) / 1.3, (round_x0, err)
+
+
+@pytest.mark.parametrize("k,phases", [(6, [2, 2, 2]), (7, [2, 2, 2, 1]), (8, [2, 2, 2, 2])])
+def test_gram_space_pairs_within_the_bar(qwen7b_k, k, phases):
+    """The Gram-space chain with P stored as pairs: within the bar with
+    room; with P in bf16 alone it is not at 8 iterations."""
+    from _bf16_model import ns_gram_bf16_storage
+    ref = muon.newton_schulz(qwen7b_k, *muon.QUINTIC, k)
+    err = lambda Y: np.linalg.norm(Y - ref) / np.linalg.norm(ref)
+    e_pairs = err(ns_gram_bf16_storage(qwen7b_k, *muon.QUINTIC, k, phases, round_x0=False))
+    assert e_pairs < tol_o_bf16(k) / 1.3, e_pairs
+    if k == 8:
+        e_bf16 = err(ns_gram_bf16_storage(qwen7b_k, *muon.QUINTIC, k, phases, round_x0=False,
+                                          pairs=False))
+        assert e_bf16 > tol_o_bf16(k), e_bf16
+
+
+def test_b_rounding_dominates_at_eight_iterations(qwen7b_k):
+    """Why B: at 8 iterations, a pair for B halves the error, while keeping
+    the stored X exact changes it by a few per cent."""
+    ref = muon.newton_schulz(qwen7b_k, *muon.QUINTIC, 8)
+    err = lambda Y: np.linalg.norm(Y - ref) / np.linalg.norm(ref)
+    base = err(ns_bf16_storage(qwen7b_k, *muon.QUINTIC, 8, round_x0=False, pairs=False))
+    b_pair = err(ns_bf16_storage(qwen7b_k, *muon.QUINTIC, 8, round_x0=False, pairs=True))
+    assert b_pair < 0.6 * base, (b_pair, base)
 
 
 def test_quintic_expands_errors_inside_its_band():

@@ -14,17 +14,37 @@ LLAMA8B_OWNER0 = [(4096, 4096)] * 8 + [(1024, 4096)] * 8 + [(14336, 4096)] * 8 +
     [(4096, 14336)] * 4
 
 
-def direct_flops(m, n, k):
-    return k * (m * (m + 1) * n + m * m * (m + 1) + 2 * m * m * n)
+def pairs(k, fp32=False):
+    """From six iterations on, the bf16 chain stores B / P as hi + lo pairs."""
+    return k >= 6 and not fp32
+
+
+def direct_flops(m, n, k, fp32=False):
+    """Executed flops: with pairs, Apply runs a second pass over B's low half."""
+    apply_passes = 2 if pairs(k, fp32) else 1
+    return k * (m * (m + 1) * n + m * m * (m + 1) + apply_passes * 2 * m * m * n)
 
 
 def phases(k):
     return [2] * (k // 2) + ([1] if k % 2 else [])
 
 
-def gram_flops(m, n, k):
+def square_passes(L, split):
+    """Products of m_p x m_p matrices in a phase of L iterations, counted in
+    full passes: L of P, L - 1 of P P, L - 1 of A T, L - 1 of Q P.  With
+    pairs, P P reads a pair on both sides (3 passes), the first Q P too
+    (Q is the first P), later ones on one side (2)."""
+    if not split:
+        return 4 * L - 3
+    return L + 3 * (L - 1) + (L - 1) + (3 + 2 * (L - 2) if L >= 2 else 0)
+
+
+def gram_flops(m, n, k, fp32=False):
     ph = phases(k)
-    return len(ph) * (m * (m + 1) * n + 2 * m * m * n) + sum(4 * L - 3 for L in ph) * m * m * (m + 1)
+    split = pairs(k, fp32)
+    apply = sum(2 if split and L == 1 else 1 for L in ph) * 2 * m * m * n
+    return len(ph) * m * (m + 1) * n + apply + \
+        sum(square_passes(L, split) for L in ph) * m * m * (m + 1)
 
 
 @pytest.mark.parametrize("k", [1, 2, 3, 4, 5, 6, 7, 8, 10])
@@ -87,6 +107,36 @@ def test_gram_needs_more_workspace():
         # four more m_p x m_p buffers per Gram-space matrix, plus its launch tables
         d = ws(nsd.StepOptions(gram_ns=True), shapes) - ws(nsd.StepOptions(), shapes)
         assert extra <= d < extra + 65536 and (d == 0) == (extra == 0), (shapes, d)
+
+
+def test_pairs_add_workspace_not_launches():
+    """From six iterations on: one more m_p x m_p buffer per direct-chain
+    matrix (B's low half) and two per Gram-space matrix (the low halves of
+    the first and the later P); the launch sequence is the same, and the fp32
+    mode has no pairs."""
+    def ws(opts, shapes):
+        arr = (_lib.Matrix * len(shapes))()
+        for i, (r, c) in enumerate(shapes):
+            arr[i] = _lib.Matrix(None, 0, 0, None, None, None, r, c, 1.0, 0, 0)
+        out = ctypes.c_size_t(0)
+        cfg = opts.to_c()
+        _lib.check(_lib.load().dmuon_workspace_bytes(arr, len(shapes), ctypes.byref(cfg),
+                                                     ctypes.byref(out)))
+        return out.value
+    buf = 512 * 512 * 2
+    for gram, shapes, extra in ((False, [(300, 700)], buf), (True, [(300, 700)], 2 * buf),
+                                (True, [(700, 300)], 2 * buf), (True, [(513, 300)], buf)):
+        o5 = nsd.StepOptions(ns_steps=5, gram_ns=gram)
+        o6 = nsd.StepOptions(ns_steps=6, gram_ns=gram)
+        k5 = [kd for kd, _ in nsd.step_launches(shapes, o5)]
+        k6 = [kd for kd, _ in nsd.step_launches(shapes, o6)]
+        d = ws(o6, shapes) - ws(o5, shapes)
+        assert extra <= d < extra + 65536, (gram, shapes, d)
+        if not gram or shapes == [(513, 300)]:   # the direct chain: one more iteration
+            assert k6 == k5[:2] + ["gram", "square", "apply"] + k5[2:]
+        f6 = nsd.StepOptions(ns_steps=6, gram_ns=gram, ns_fp32=True)
+        f5 = nsd.StepOptions(ns_steps=5, gram_ns=gram, ns_fp32=True)
+        assert ws(f6, shapes) == ws(f5, shapes)
 
 
 def test_step_launches_errors():
