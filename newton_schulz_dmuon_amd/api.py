@@ -42,6 +42,18 @@ def _stream_handle(device, stream) -> Optional[int]:
     return stream.cuda_stream
 
 
+def _keep_for_stream(t, device, stream) -> None:
+    """PyTorch's caching allocator ties a block to the stream that allocated
+    it and may hand it out again as soon as the tensor is freed.  A buffer
+    allocated on the current stream but used by kernels on another one is
+    marked as in use by that stream too, so that neither its release (a
+    temporary workspace) nor its replacement (a growing Workspace) lets a
+    new tensor take the memory before those kernels are done."""
+    import torch
+    if stream is not None and stream != torch.cuda.current_stream(device):
+        t.record_stream(stream)
+
+
 @dataclass
 class StepOptions:
     """``dmuon_step_config``.  ``lr`` and ``ns_steps`` defaults are the ones in
@@ -165,6 +177,7 @@ def muon_step(params: Sequence, grads: Sequence, momenta: Sequence, scales: Sequ
     need = ctypes.c_size_t(0)
     check(lib.dmuon_workspace_bytes(arr, n, ctypes.byref(cfg), ctypes.byref(need)))
     ws = (workspace or Workspace()).get(need.value, device)
+    _keep_for_stream(ws, device, stream)
     if packed is None:
         check(lib.dmuon_muon_step(arr, n, ctypes.byref(cfg), ws.data_ptr(), ws.numel(),
                                   _stream_handle(device, stream)))

@@ -147,9 +147,12 @@ def test_nonfinite_input_propagates_within_its_matrix(nsd):
     say(f"  clean matrix O rel err {err:.3e}")
 
 
-def test_qwen25_1p5b_layer(nsd):
+@pytest.mark.parametrize("gram_ns", [False, True])
+def test_qwen25_1p5b_layer(nsd, gram_ns):
     """One Qwen2.5-1.5B layer's projections: q/o 1536^2, k/v 256x1536,
-    gate/up 8960x1536, down 1536x8960, bf16."""
+    gate/up 8960x1536, down 1536x8960, bf16; the direct chain for every
+    matrix, and the Gram-space chain (k, v, gate, up, down take it, q and o
+    keep the direct one), as bench.py runs this workload."""
     from synth import matrix_inputs, workload
     w = workload(2)
     case = Case([(r, c) for _, r, c in w.shapes], "bf16", "bf16")
@@ -157,8 +160,8 @@ def test_qwen25_1p5b_layer(nsd):
     for i in range(len(w.shapes)):
         P, G, M = matrix_inputs(w, i)
         case.P.append(P); case.G.append(G); case.M.append(M)
-    opts = nsd.StepOptions()
-    say("qwen layer: gpu")
+    opts = nsd.StepOptions(gram_ns=gram_ns)
+    say(f"qwen layer: gpu, gram_ns {gram_ns}")
     gpu = case.run_gpu(opts)
     say("qwen layer: oracle")
     err = check_step(case, opts, gpu, case.run_oracle(opts))
@@ -237,3 +240,30 @@ def test_check_finite_flags(nsd, gram):
     clean.run_gpu(opts, workspace=ws)
     flags = nsd.nonfinite_flags([to_dev(p, "bf16") for p in clean.P], opts, ws).cpu().tolist()
     assert flags == [0, 0, 0]
+
+
+def test_side_stream_with_temporary_workspace(nsd):
+    """A step enqueued on a side stream with no persisted workspace: the
+    binding's temporary workspace is freed when the call returns, while the
+    step's kernels still run on the side stream.  A buffer of the same size
+    allocated on the current stream right after, and filled there, must not
+    receive that memory (the binding marks it as in use by the side
+    stream); the step's results match the oracle."""
+    shapes = [(1024, 3072), (2048, 1024)]
+    case = Case(shapes, "bf16", "bf16", seed=12, m_std=1e-3)
+    opts = nsd.StepOptions(gram_ns=True)
+    P = [to_dev(p, "bf16") for p in case.P]
+    G = [to_dev(g, "bf16") for g in case.G]
+    M = [to_dev(m, "f32") for m in case.M]
+    O = [torch.empty_like(p) for p in P]
+    need = nsd.workspace_bytes(P, opts)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    say(f"side-stream step, workspace {need} bytes")
+    nsd.muon_step(P, G, M, case.scales, opts, orth_out=O, stream=side)
+    junk = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    junk.fill_(0xFF)
+    torch.cuda.synchronize()
+    gpu = ([to_host(p) for p in P], [to_host(m) for m in M], [to_host(o) for o in O])
+    err = check_step(case, opts, gpu, case.run_oracle(opts))
+    say(f"  O rel err {err:.3e}")
