@@ -318,6 +318,31 @@ int dmuon_muon_step_traced(const dmuon_matrix *mats, int32_t n,
                            size_t workspace_bytes, void *stream,
                            void *const *events, int32_t n_events);
 
+/* Bytes of the static device scratch dmuon_muon_step_noalloc works in. */
+#define DMUON_NOALLOC_SCRATCH_BYTES (64ull << 20)
+
+/* dmuon_muon_step for callers that cannot allocate device memory (tight
+ * serving loops, harnesses that forbid hipMalloc): no workspace argument,
+ * and no device or pinned allocation in the call.  Its workspace is a
+ * file-scope device array of DMUON_NOALLOC_SCRATCH_BYTES that every GPU the
+ * library runs on holds from the library's module load until the process
+ * ends; its address is looked up once per device on the first call there.
+ * The launch tables go through a static host buffer of 4 MiB, reused after
+ * the previous call's copy from it has completed (the call may wait for
+ * that).  Results are bitwise those of dmuon_muon_step with a workspace.
+ * Limits: the matrices' dmuon_workspace_bytes() must not exceed
+ * DMUON_NOALLOC_SCRATCH_BYTES, else WORKSPACE_TOO_SMALL and nothing is
+ * enqueued.  Every call on one GPU shares that GPU's scratch, which keeps the
+ * last call's contents (nothing in it needs clearing: each step writes every
+ * workspace byte it reads, the zero padding included).  Calls in stream order
+ * are safe; calls that overlap on one GPU (other streams, other host
+ * threads whose work is in flight together) race on the scratch.  Not meant
+ * for stream capture: the table upload is a copy from pageable host memory.
+ * Errors: those of dmuon_muon_step, WORKSPACE_TOO_SMALL as above, HIP if
+ * the scratch cannot be looked up. */
+int dmuon_muon_step_noalloc(const dmuon_matrix *mats, int32_t n,
+                            const dmuon_step_config *cfg, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

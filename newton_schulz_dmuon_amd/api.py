@@ -187,6 +187,22 @@ def muon_step(params: Sequence, grads: Sequence, momenta: Sequence, scales: Sequ
                                          _stream_handle(device, stream), None, 0))
 
 
+def muon_step_noalloc(params: Sequence, grads: Sequence, momenta: Sequence,
+                      scales: Sequence[float], opts: StepOptions = StepOptions(),
+                      orth_out: Optional[Sequence] = None, stream=None) -> None:
+    """``muon_step`` without a workspace: ``dmuon_muon_step_noalloc`` works
+    in the library's static per-device scratch (``_lib.NOALLOC_SCRATCH_BYTES``)
+    and allocates nothing.  Calls overlapping on one GPU race on that
+    scratch; calls in stream order are safe."""
+    n = len(params)
+    if n == 0:
+        return
+    arr, n = matrices(params, grads, momenta, scales, orth_out)
+    cfg = opts.to_c()
+    check(load().dmuon_muon_step_noalloc(arr, n, ctypes.byref(cfg),
+                                         _stream_handle(params[0].device, stream)))
+
+
 def pack(tensors: Sequence, offsets: Sequence[int], packed, stream=None) -> None:
     """``packed[offsets[i] + r*cols + c] = tensors[i][r, c]`` (bit copy)."""
     arr, n = matrices(tensors, packed_offsets=offsets)

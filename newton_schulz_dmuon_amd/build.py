@@ -18,7 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdmuon.so")
-SOURCES = ["host_api.cpp", "elementwise.hip", "gemm.hip"]
+SOURCES = ["host_api.cpp", "elementwise.hip", "gemm.hip", "scratch.hip"]
 ARCH = "gfx950"
 
 COMMON = [

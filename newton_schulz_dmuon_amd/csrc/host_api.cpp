@@ -715,6 +715,42 @@ int upload(void *dst, const std::vector<char> &src, hipStream_t st) {
   return DMUON_OK;
 }
 
+// The no-allocation path's table upload: a static (pageable) host buffer,
+// reused only after the copy from it has completed (an event per device,
+// created on first use; events are not memory allocations).
+constexpr size_t kNoAllocTableBytes = size_t(4) << 20;
+std::mutex g_static_mu;
+char g_static_host[kNoAllocTableBytes];
+hipEvent_t g_static_ev[64] = {};
+hipEvent_t g_static_last = nullptr;
+
+int upload_static(void *dst, const std::vector<char> &src, hipStream_t st) {
+  if (src.size() > kNoAllocTableBytes)
+    return fail(DMUON_ERR_WORKSPACE_TOO_SMALL, "launch tables need %zu bytes, the static staging holds %zu",
+                src.size(), kNoAllocTableBytes);
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(DMUON_ERR_INVALID_ARG, "device %d beyond the static path's 64", dev);
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (g_static_last) {
+    e = hipEventSynchronize(g_static_last);
+    if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize");
+    g_static_last = nullptr;
+  }
+  if (!g_static_ev[dev]) {
+    e = hipEventCreateWithFlags(&g_static_ev[dev], hipEventDisableTiming);
+    if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+  }
+  std::memcpy(g_static_host, src.data(), src.size());
+  e = hipMemcpyAsync(dst, g_static_host, src.size(), hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync");
+  e = hipEventRecord(g_static_ev[dev], st);
+  if (e != hipSuccess) return hip_fail(e, "hipEventRecord");
+  g_static_last = g_static_ev[dev];
+  return DMUON_OK;
+}
+
 int check_launch(hipError_t e, const char *what) {
   return e == hipSuccess ? DMUON_OK : hip_fail(e, what);
 }
@@ -827,11 +863,14 @@ int dmuon_workspace_bytes(const dmuon_matrix *mats, int32_t n, const dmuon_step_
   return DMUON_OK;
 }
 
-// packed == nullptr: no packed copy of the updated params.
+// packed == nullptr: no packed copy of the updated params.  noalloc: the
+// workspace is this device's static scratch (workspace / workspace_bytes
+// are ignored) and the tables go through the static host buffer.
 static int muon_step_impl(const dmuon_matrix *mats, int32_t n, const dmuon_step_config *cfg,
                           void *workspace, size_t workspace_bytes, void *stream,
                           void *const *events, int32_t n_events, void *packed = nullptr,
-                          int32_t packed_dtype = DMUON_BF16, int64_t packed_numel = 0) {
+                          int32_t packed_dtype = DMUON_BF16, int64_t packed_numel = 0,
+                          bool noalloc = false) {
   g_last_error.clear();
   if (n_events < 0 || (n_events > 0 && !events))
     return fail(DMUON_ERR_INVALID_ARG, "bad event list");
@@ -885,6 +924,18 @@ static int muon_step_impl(const dmuon_matrix *mats, int32_t n, const dmuon_step_
   if (rc) return rc;
   Plan p;
   build_plan(mats, n, *cfg, nullptr, p);
+  if (noalloc) {
+    if (static_cast<size_t>(p.total_bytes) > kNoAllocScratchBytes)
+      return fail(DMUON_ERR_WORKSPACE_TOO_SMALL,
+                  "these matrices need %lld bytes of workspace; the static scratch holds %zu",
+                  (long long)p.total_bytes, kNoAllocScratchBytes);
+    if (static_cast<size_t>(p.table_bytes) > kNoAllocTableBytes)
+      return fail(DMUON_ERR_WORKSPACE_TOO_SMALL, "launch tables need %lld bytes; the static staging holds %zu",
+                  (long long)p.table_bytes, kNoAllocTableBytes);
+    const hipError_t e = noalloc_scratch(&workspace);
+    if (e != hipSuccess) return hip_fail(e, "static scratch lookup");
+    workspace_bytes = kNoAllocScratchBytes;
+  }
   if (workspace_bytes < static_cast<size_t>(p.total_bytes))
     return fail(DMUON_ERR_WORKSPACE_TOO_SMALL, "workspace needs %lld bytes, got %zu",
                 (long long)p.total_bytes, workspace_bytes);
@@ -915,7 +966,7 @@ static int muon_step_impl(const dmuon_matrix *mats, int32_t n, const dmuon_step_
       std::memcpy(tables.data() + p.off_list[l], p.lists[l].data(), sizeof(TileEntry) * p.lists[l].size());
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  rc = upload(ws, tables, s);
+  rc = noalloc ? upload_static(ws, tables, s) : upload(ws, tables, s);
   if (rc) return rc;
 
   auto dtab = [&](int32_t t) { return reinterpret_cast<const MatDev *>(ws + p.off_table[t]); };
@@ -1017,6 +1068,11 @@ int dmuon_muon_step_packed(const dmuon_matrix *mats, int32_t n, const dmuon_step
   }
   return muon_step_impl(mats, n, cfg, workspace, workspace_bytes, stream, events, n_events, packed,
                         packed_dtype, packed_numel);
+}
+
+int dmuon_muon_step_noalloc(const dmuon_matrix *mats, int32_t n, const dmuon_step_config *cfg,
+                            void *stream) {
+  return muon_step_impl(mats, n, cfg, nullptr, 0, stream, nullptr, 0, nullptr, DMUON_BF16, 0, true);
 }
 
 // ------------------------------------------------------------------ AdamW --

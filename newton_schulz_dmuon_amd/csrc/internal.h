@@ -153,6 +153,14 @@ struct AdamScalars {
 };
 hipError_t launch_adamw_batch(const AdamBatch &b, AdamScalars s, hipStream_t st);
 
+// ---- static scratch (scratch.hip) ----
+// Size of the file-scope device array that dmuon_muon_step_noalloc uses as
+// its workspace (DMUON_NOALLOC_SCRATCH_BYTES of the C ABI).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+// This device's address of that array (looked up once per device, with the
+// device current, then kept).
+hipError_t noalloc_scratch(void **ptr);
+
 // ---- launchers (gemm.hip) ----
 // mats: the launch's table (per-matrix operands and coefficients).
 hipError_t launch_ns_stage(GemmMode mode, bool fp32, const MatDev *mats,
