@@ -68,19 +68,23 @@ enum { DMUON_FIELD_PARAM = 0, DMUON_FIELD_GRAD = 1 };
 enum {
   /* Keep X, A, B in fp32 through the Newton-Schulz chain (fp32 MFMA) instead
    * of bf16.  A checking mode: slower, closer to exact arithmetic.
-   * Without it (the bf16 chain), from ns_steps = 6 on, B = bA + cA^2 (and
-   * every P of the Gram-space chain) is stored as a pair of bf16 values,
-   * hi = RNE(v) and lo = RNE(v - hi), and each product that reads it runs
-   * one more pass over lo: the default quintic amplifies rounding errors on
-   * part of its band, and B's rounding is the largest contributor. */
+   * Without it (the bf16 chain): from ns_steps = 6 on, B = bA + cA^2 (from
+   * the third iteration on), and every P and T = P^2 of the Gram-space
+   * chain, are stored as a pair of bf16 values, hi = RNE(v) and
+   * lo = RNE(v - hi), and each product that reads one runs one more pass
+   * over lo, because the default quintic amplifies rounding errors on part
+   * of its band and B's rounding is the largest contributor; and a matrix
+   * with min(rows, cols) < 128 runs its whole chain in fp32 (its own
+   * launches), because its singular values stay in that band for most
+   * iterations, where bf16 storage alone cannot keep it within 2e-2. */
   DMUON_FLAG_NS_FP32 = 1u << 0,
   /* Orthogonalise the look-ahead G + mu*M (after the momentum update)
    * instead of M. */
   DMUON_FLAG_NESTEROV = 1u << 1,
   /* Gram-space Newton-Schulz (the pages credit a "Gram Newton-Schulz"
    * kernel: landing page, "VLA and VLM" and the credits) for every matrix
-   * with max(r,c) >= 2 min(r,c) when ns_steps >= 5; the others, and every
-   * matrix at fewer iterations, keep the direct chain.  All iterates are
+   * with max(r,c) >= 2 min(r,c) and min(r,c) >= 128 when ns_steps >= 5; the
+   * others, and every matrix at fewer iterations, keep the direct chain.  All iterates are
    * polynomials in A = X X^T, so the chain runs on m x m matrices: per
    * iteration P = aI + bA + cA^2, A <- A P^2, Q <- Q P, and X <- Q X once
    * per phase.  Same result in exact arithmetic; about 1.35x fewer flops at

@@ -131,7 +131,6 @@ __global__ __launch_bounds__(256) void finalize_norm_kernel(const MatDev *__rest
 // so that M is read in 512-byte and X^T written in 128-byte row segments.
 // The 1/(||U||_F + eps) scale is applied by the first iteration's Gram and
 // Apply epilogues, so M is read once.
-template <typename T>
 __device__ __forceinline__ void momentum4(const MatDev &d, int64_t ur, int64_t uc, float mu, bool nesterov,
                                           bool vec, float (&u)[4]) {
   u[0] = u[1] = u[2] = u[3] = 0.f;
@@ -159,7 +158,15 @@ __device__ __forceinline__ void momentum4(const MatDev &d, int64_t ur, int64_t u
   }
 }
 
-template <typename T>
+// Four consecutive elements of X^T in the matrix's workspace type: bf16, or
+// fp32 (the fp32 mode, and small matrices in a bf16 step).
+__device__ __forceinline__ void store_xt4(const MatDev &d, int64_t idx, const float (&u)[4]) {
+  if (d.ws_f32)
+    Vec4St<float>::st(static_cast<float *>(d.xt[0]) + idx, u);
+  else
+    Vec4St<uint16_t>::st(static_cast<uint16_t *>(d.xt[0]) + idx, u);
+}
+
 __global__ __launch_bounds__(kOrientThreads) void momentum_orient_kernel(
     const MatDev *__restrict__ mats, int32_t nmat, StepScalars s) {
   constexpr int TT = static_cast<int>(kTrTile);
@@ -173,7 +180,6 @@ __global__ __launch_bounds__(kOrientThreads) void momentum_orient_kernel(
   const float mu = s.mu;
   const int tid = threadIdx.x;
   const bool vec = (d.cols & 3) == 0;  // rows of M start 16-byte aligned
-  T *XT = static_cast<T *>(d.xt[0]);
   double acc = 0.0;
   if (d.transposed) {
     // 8192 contiguous elements of X^T per group: two runs of 4096, four
@@ -183,10 +189,10 @@ __global__ __launch_bounds__(kOrientThreads) void momentum_orient_kernel(
     for (int h = 0; h < 2; ++h) {
       const int64_t e0 = t * (2 * TT * TT) + h * (TT * TT) + 4 * tid;
       float u[4];
-      momentum4<T>(d, e0 / d.mp, e0 % d.mp, mu, s.nesterov, vec, u);
+      momentum4(d, e0 / d.mp, e0 % d.mp, mu, s.nesterov, vec, u);
 #pragma unroll
       for (int k = 0; k < 4; ++k) acc += (double)u[k] * u[k];
-      Vec4St<T>::st(XT + e0, u);  // X^T[ur][uc .. uc+3], zeros in the padding
+      store_xt4(d, e0, u);  // X^T[ur][uc .. uc+3], zeros in the padding
     }
   } else {
     // block rows i0 .. i0+63 (m), columns j0 .. j0+127 (n); thread: row p,
@@ -197,7 +203,7 @@ __global__ __launch_bounds__(kOrientThreads) void momentum_orient_kernel(
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       float u[4];
-      momentum4<T>(d, i0 + p, j0 + h * TT + q, mu, s.nesterov, vec, u);
+      momentum4(d, i0 + p, j0 + h * TT + q, mu, s.nesterov, vec, u);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         tile[p][h * TT + q + k] = u[k];
@@ -212,7 +218,7 @@ __global__ __launch_bounds__(kOrientThreads) void momentum_orient_kernel(
       float vt[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) vt[k] = tile[b + k][a];
-      Vec4St<T>::st(XT + (j0 + a) * d.mp + i0 + b, vt);
+      store_xt4(d, (j0 + a) * d.mp + i0 + b, vt);
     }
   }
   const double tot = block_sum_f64(acc, red);
@@ -329,13 +335,9 @@ hipError_t launch_finalize_norm(const MatDev *mats, int32_t nmat, float eps, hip
 }
 
 hipError_t launch_momentum_orient(const MatDev *mats, int32_t nmat, int64_t total_tiles,
-                                  StepScalars s, bool fp32, hipStream_t st) {
-  if (fp32)
-    hipLaunchKernelGGL(momentum_orient_kernel<float>, dim3((uint32_t)total_tiles), dim3(kOrientThreads), 0,
-                       st, mats, nmat, s);
-  else
-    hipLaunchKernelGGL(momentum_orient_kernel<uint16_t>, dim3((uint32_t)total_tiles), dim3(kOrientThreads),
-                       0, st, mats, nmat, s);
+                                  StepScalars s, hipStream_t st) {
+  hipLaunchKernelGGL(momentum_orient_kernel, dim3((uint32_t)total_tiles), dim3(kOrientThreads), 0,
+                     st, mats, nmat, s);
   return hipGetLastError();
 }
 

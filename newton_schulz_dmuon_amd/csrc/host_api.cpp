@@ -138,13 +138,15 @@ enum LaunchKind : int32_t {
 // Workspace buffers a GEMM launch can name per matrix: the direct chain uses
 // A and B; the Gram-space chain also A', T, Q0, Q1 (m_p x m_p each).  With
 // hi + lo pairs (split_pairs), B_lo holds the low half of B (direct chain)
-// or of a later iteration's P (Gram-space chain), Q0_lo that of the first P.
+// or of a later iteration's P (Gram-space chain), Q0_lo that of the first P,
+// T_lo that of T = P P.
 enum Buf : int32_t {
-  kBufNone = -1, kBufA = 0, kBufB, kBufA1, kBufT, kBufQ0, kBufQ1, kBufBlo, kBufQ0lo, kBufCount
+  kBufNone = -1, kBufA = 0, kBufB, kBufA1, kBufT, kBufQ0, kBufQ1, kBufBlo, kBufQ0lo, kBufTlo, kBufCount
 };
 
 // One part of a grouped GEMM launch: a group of matrices (0 direct chain, 1
-// Gram-space chain) and, for every matrix of it, which buffer each MatDev
+// Gram-space chain, 2 direct chain in fp32 for small matrices of a bf16
+// step) and, for every matrix of it, which buffer each MatDev
 // pointer names (a: Gram output, Square L; b: Square output, Apply L; r:
 // Square R; l_lo, r_lo: low halves of L and R; o_lo: low half of a Square
 // output), which X^T buffer is read (cur; the other one is written), and
@@ -167,6 +169,7 @@ struct Part {
 
 struct Launch {
   int32_t kind;
+  bool fp32 = false;        // fp32 operands (kernel instance); parts share it
   std::vector<Part> parts;  // GEMM launches; all of one kind
   int32_t table = 0;        // MatDev table: the parts' matrices, in order
   int32_t list = 0;         // tile list over that table
@@ -179,7 +182,9 @@ struct Plan {
   // the sizing pass) and a bit mask of the ones it has
   std::vector<std::array<void *, kBufCount - kBufA1>> extra;
   std::vector<uint32_t> have;
-  std::vector<int32_t> groups[2];             // matrix indices: direct chain, Gram-space chain
+  // matrix indices: direct chain, Gram-space chain, fp32 direct chain of
+  // the small matrices of a bf16 step
+  std::vector<int32_t> groups[3];
   std::vector<std::vector<Part>> tables;      // tables 1..: the parts of a launch
   std::vector<std::vector<TileEntry>> lists;
   std::vector<StageXcd> list_xcd;
@@ -286,7 +291,8 @@ void cached_stage_tiles(const std::vector<MatDev> &mats, const std::vector<int32
 int64_t orient_groups(const MatDev &d) { return (d.mp / kTrTile) * (d.np / kTrTile) / 2; }
 
 // A matrix takes the Gram-space chain when asked for, with at least five
-// iterations and n >= 2m: the m x m chain then costs fewer flops than the
+// iterations, n >= 2m and m >= kFp32BelowM (below that a bf16 step runs the
+// matrix's chain in fp32): the m x m chain then costs fewer flops than the
 // direct iterations, and the iterate's singular values stay within a factor
 // (sqrt(n)+sqrt(m))/(sqrt(n)-sqrt(m)) < 6 of each other for Gaussian-like
 // inputs.  Below five iterations the rounding of the first phase's Q is not
@@ -294,17 +300,19 @@ int64_t orient_groups(const MatDev &d) { return (d.mp / kTrTile) * (d.np / kTrTi
 // noise) two iterations come out about 18x, three to four 2-4x less
 // accurate than the direct chain in a bf16 emulation, so those keep it.
 bool uses_gram(const MatDev &d, const dmuon_step_config &cfg) {
-  return (cfg.flags & DMUON_FLAG_GRAM_NS) && cfg.ns_steps >= 5 && d.n >= 2 * d.m;
+  return (cfg.flags & DMUON_FLAG_GRAM_NS) && cfg.ns_steps >= 5 && d.n >= 2 * d.m && d.m >= kFp32BelowM;
 }
 
-// From six iterations on, the bf16 chain keeps B (direct chain) and every P
-// (Gram-space chain) as hi + lo pairs.  The default quintic amplifies
-// rounding errors on part of its band, and the rounding of B (or P) is the
-// largest contributor: in a bf16 emulation on Gaussian inputs of the
-// Qwen2.5-7B and Qwen2.5-1.5B shapes, pairs take the error at 8 iterations
-// from 1.5-2.7e-2 to 0.7-1.4e-2, where keeping X or A in fp32 instead
-// changes it by 1-10%.  Up to five iterations bf16 storage stays below
-// about 1.4e-2 on those inputs, so the pairs' extra passes are not paid.
+// From six iterations on, the bf16 chain keeps B (direct chain), and every
+// P and T = P P (Gram-space chain), as hi + lo pairs.  The default quintic
+// amplifies rounding errors on part of its band, and the rounding of B (or
+// P) is the largest contributor: in a bf16 emulation on Gaussian inputs of
+// the Qwen2.5-7B and Qwen2.5-1.5B shapes, pairs take the error at 8
+// iterations from 1.5-2.7e-2 to 0.7-1.4e-2, where keeping X or A in fp32
+// instead changes it by 1-10%.  In the Gram-space chain T comes next (P
+// alone leaves 1.9e-2 on a 17 x 100 input at 6 iterations, P and T 1.0e-2).
+// Up to five iterations bf16 storage stays below about 1.4e-2 on those
+// inputs, so the pairs' extra passes are not paid.
 constexpr int kSplitFromSteps = 6;
 bool split_pairs(const dmuon_step_config &cfg) {
   return !(cfg.flags & DMUON_FLAG_NS_FP32) && cfg.ns_steps >= kSplitFromSteps;
@@ -324,17 +332,27 @@ std::vector<int> gram_phases(int K) {
 }
 
 // Builds the plan; with ws == nullptr only sizes are computed.
+// In a bf16 step, a matrix with m = min(r, c) < kFp32BelowM runs its chain
+// in fp32 (its own launches, group 2).  Such a matrix's singular values
+// start near 1/sqrt(m), reach the quintic's band within one or two
+// iterations and stay there, where rounding errors grow: in a bf16
+// emulation on Gaussian inputs, bf16 storage gives up to 2.0-2.3e-2 at five
+// iterations for m = 17-32 and 2.1-2.8e-2 at eight even with B as a pair,
+// against at most 1.2e-2 at m >= 128.  Its products are at most one
+// 256-tile wide, so fp32 costs next to nothing.
+bool small_fp32(const MatDev &d, const dmuon_step_config &cfg) {
+  return !(cfg.flags & DMUON_FLAG_NS_FP32) && d.m < kFp32BelowM;
+}
+
 void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg, char *ws,
                 Plan &p) {
   const bool fp32 = cfg.flags & DMUON_FLAG_NS_FP32;
-  const int64_t es = fp32 ? 4 : 2;
   const int K = cfg.ns_steps;
   const bool split = split_pairs(cfg);
   p.mats.resize(n);
   p.extra.assign(n, {});
   p.have.assign(n, 0);
-  p.groups[0].clear();
-  p.groups[1].clear();
+  for (auto &g : p.groups) g.clear();
   int64_t ew = 0, tr = 0;
   for (int32_t i = 0; i < n; ++i) {
     const dmuon_matrix &s = in[i];
@@ -361,7 +379,8 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
     ew += d.ew_count;
     d.tr_first = tr;
     tr += orient_groups(d);
-    if (K > 0) p.groups[uses_gram(d, cfg) ? 1 : 0].push_back(i);
+    d.ws_f32 = fp32 || small_fp32(d, cfg);
+    if (K > 0) p.groups[uses_gram(d, cfg) ? 1 : small_fp32(d, cfg) ? 2 : 0].push_back(i);
   }
   p.ew_total = ew;
   p.tr_total = K > 0 ? tr : 0;
@@ -388,23 +407,29 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
     for (const Part &pt : l.parts) l.flops += flops(pt.group, kind) * pt.passes(kind);
     chain.push_back(std::move(l));
   };
-  std::vector<Launch> chain[2];
-  if (K > 0 && !p.groups[0].empty()) {
-    // direct chain: K x (A = X X^T; B = b A + c A A; X <- a X + B X); with
-    // pairs, Square also stores B's low half and Apply reads it
+  std::vector<Launch> chain[3];
+  // direct chain: K x (A = X X^T; B = b A + c A A; X <- a X + B X); with
+  // pairs (bf16 only), Square also stores B's low half and Apply reads it,
+  // from the third iteration on: the first two iterations' rounding of B
+  // does not show in the result (bf16 emulation: the same error as pairs
+  // in every iteration, m >= 128, 6 and 8 iterations)
+  auto direct_chain = [&](int32_t g, bool pairs, bool chain_fp32) {
     for (int k = 0; k < K; ++k) {
       const int32_t cur = k & 1, first = k == 0;
-      const Part pt{0, kBufA, kBufB, kBufNone, cur, first, cfg.a, cfg.b, cfg.c, 0.f};
+      const Part pt{g, kBufA, kBufB, kBufNone, cur, first, cfg.a, cfg.b, cfg.c, 0.f};
       Part sq = pt, ap = pt;
-      if (split) {
+      if (pairs && k >= 2) {
         sq.o_lo = kBufBlo;
         ap.l_lo = kBufBlo;
       }
-      gemm(chain[0], kLkGram, {pt});
-      gemm(chain[0], kLkSquare, {sq});
-      gemm(chain[0], k + 1 == K ? kLkFinal : kLkApply, {ap});
+      gemm(chain[g], kLkGram, {pt});
+      gemm(chain[g], kLkSquare, {sq});
+      gemm(chain[g], k + 1 == K ? kLkFinal : kLkApply, {ap});
     }
-  }
+    for (Launch &l : chain[g]) l.fp32 = chain_fp32;
+  };
+  if (K > 0 && !p.groups[0].empty()) direct_chain(0, split, fp32);
+  if (K > 0 && !p.groups[2].empty()) direct_chain(2, false, true);
   if (K > 0 && !p.groups[1].empty()) {
     // Gram-space chain, per phase of L iterations from X:
     //   A = X X^T; Q = I
@@ -416,7 +441,8 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
     // P: one launch.
     // With pairs, every P is stored as hi + lo (the first in Q0 / Q0_lo,
     // later ones in B / B_lo) and read as such by P P, Q P and, when Q is
-    // still the first P (a phase of one iteration), by X <- Q X.
+    // still the first P (a phase of one iteration), by X <- Q X; T = P P is
+    // stored as T / T_lo and read as such by A T.
     const std::vector<int> phases = gram_phases(K);
     auto lo_of = [&](int32_t buf) { return !split ? kBufNone : buf == kBufQ0 ? kBufQ0lo : kBufBlo; };
     int32_t cur = 0;
@@ -437,6 +463,7 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
         if (i + 1 < phases[ph]) {
           Part t = part(pbuf, kBufT, kBufNone, 0.f, 1.f, 0.f);  // T = P P
           t.l_lo = lo_of(pbuf);
+          t.o_lo = split ? kBufTlo : kBufNone;
           next.push_back(t);
         }
         if (i > 0) {
@@ -450,7 +477,9 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
         }
         if (!next.empty()) gemm(chain[1], kLkSquare, next);
         if (i + 1 < phases[ph]) {
-          gemm(chain[1], kLkSquare, {part(acur, anext, kBufT, 0.f, 1.f, 0.f)});  // A T
+          Part at = part(acur, anext, kBufT, 0.f, 1.f, 0.f);  // A T
+          at.r_lo = split ? kBufTlo : kBufNone;
+          gemm(chain[1], kLkSquare, {at});
           std::swap(acur, anext);
         }
       }
@@ -459,6 +488,7 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
       gemm(chain[1], last_phase ? kLkFinal : kLkApply, {ap});
       cur ^= 1;
     }
+    for (Launch &l : chain[1]) l.fp32 = fp32;
   }
   // The two chains touch disjoint matrices: merge them into one sequence
   // that keeps each chain's order and runs a launch of each chain of the
@@ -487,6 +517,9 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
       }
     }
   }
+  // the small matrices' fp32 launches share no launch with the bf16 ones
+  // (another kernel instance): they run after them
+  merged.insert(merged.end(), chain[2].begin(), chain[2].end());
   if (K == 0) {
     p.prog.push_back(Launch{kLkMomentumSumsq});
     p.prog.push_back(Launch{kLkNorm});
@@ -567,6 +600,7 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
     d.inv_norm = ws ? reinterpret_cast<float *>(ws + p.off_inv + 256 * int64_t(i)) : nullptr;
     d.nonfinite = ws && p.off_flags >= 0 ? reinterpret_cast<int32_t *>(ws + p.off_flags) + i : nullptr;
     if (K == 0) continue;
+    const int64_t es = d.ws_f32 ? 4 : 2;
     const int64_t xb = d.mp * d.np * es, ab = d.mp * d.mp * es;
     const int nbuf = K >= 2 ? 2 : 1;
     for (int b = 0; b < nbuf; ++b) {
@@ -585,9 +619,12 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
     p.have[i] |= (1u << kBufA) | (1u << kBufB);
     if (uses_gram(d, cfg))
       for (int32_t b : {kBufA1, kBufT, kBufQ0, kBufQ1}) add(b);
-    if (split) {
+    if (split && !d.ws_f32) {
       add(kBufBlo);
-      if (uses_gram(d, cfg)) add(kBufQ0lo);
+      if (uses_gram(d, cfg)) {
+        add(kBufQ0lo);
+        add(kBufTlo);
+      }
     }
   }
   p.total_bytes = off;
@@ -604,7 +641,7 @@ bool plan_consistent(const Plan &p) {
     if (l.list < 0 || l.list >= static_cast<int32_t>(p.lists.size())) return false;
     std::vector<const MatDev *> rows;
     for (const Part &pt : p.tables[l.table - 1]) {
-      if (pt.group < 0 || pt.group > 1) return false;
+      if (pt.group < 0 || pt.group > 2) return false;
       // a capturing Square (b A from its R tile) must not read a pair: the
       // capture is taken in the first pass only
       if (l.kind == kLkSquare && pt.cb != 0.f && (pt.l_lo != kBufNone || pt.r_lo != kBufNone)) return false;
@@ -973,7 +1010,6 @@ static int muon_step_impl(const dmuon_matrix *mats, int32_t n, const dmuon_step_
   const MatDev *dm = dtab(0);
   const StepScalars sc{cfg->a, cfg->b, cfg->c, cfg->lr, cfg->momentum, cfg->eps,
                        (cfg->flags & DMUON_FLAG_NESTEROV) ? 1 : 0, 0};
-  const bool fp32 = cfg->flags & DMUON_FLAG_NS_FP32;
 
   // events[0] before the first launch, events[j] after launch j
   int32_t ev = 0;
@@ -997,7 +1033,7 @@ static int muon_step_impl(const dmuon_matrix *mats, int32_t n, const dmuon_step_
         rc = launched(launch_momentum_sumsq(dm, n, p.ew_total, sc, s), "momentum_sumsq launch");
         break;
       case kLkMomentumOrient:
-        rc = launched(launch_momentum_orient(dm, n, p.tr_total, sc, fp32, s), "momentum_orient launch");
+        rc = launched(launch_momentum_orient(dm, n, p.tr_total, sc, s), "momentum_orient launch");
         break;
       case kLkNorm:
         rc = launched(launch_finalize_norm(dm, n, cfg->eps, s), "finalize_norm launch");
@@ -1011,7 +1047,7 @@ static int muon_step_impl(const dmuon_matrix *mats, int32_t n, const dmuon_step_
                               : l.kind == kLkApply  ? kModeApply
                                                     : kModeFinal;
         const TileEntry *tl = reinterpret_cast<const TileEntry *>(ws + p.off_list[l.list]);
-        rc = launched(launch_ns_stage(mode, fp32, dtab(l.table), tl, p.list_xcd[l.list], sc, s),
+        rc = launched(launch_ns_stage(mode, l.fp32, dtab(l.table), tl, p.list_xcd[l.list], sc, s),
                       "Newton-Schulz stage launch");
       }
     }

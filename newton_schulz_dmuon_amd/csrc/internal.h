@@ -20,6 +20,9 @@ constexpr int64_t kEwChunk = 8192;
 constexpr int64_t kTrTile = 64;
 // Square output tile of the Newton-Schulz GEMM kernels.
 constexpr int64_t kGemmTile = 256;
+// In a bf16 step, matrices with min(rows, cols) below this run their
+// Newton-Schulz chain in fp32 (see build_plan).
+constexpr int64_t kFp32BelowM = 128;
 
 enum Dtype : int32_t { kBF16 = 0, kF32 = 1 };
 
@@ -69,6 +72,9 @@ struct MatDev {
   float cdiag;          // Square: added on the diagonal (rows < m)
   int32_t first_it;     // X holds U unnormalised: Gram scales by inv_norm^2,
                         // Apply / Final by inv_norm
+  int32_t ws_f32;       // X^T, A, B of this matrix are fp32 (the fp32 mode, or
+                        // a matrix with min(r, c) < kFp32BelowM in a bf16
+                        // step), else bf16
 };
 
 // One 256 x 256 output tile of a grouped GEMM stage.
@@ -109,7 +115,7 @@ hipError_t launch_momentum_sumsq(const MatDev *mats, int32_t nmat,
 hipError_t launch_finalize_norm(const MatDev *mats, int32_t nmat, float eps,
                                 hipStream_t st);
 hipError_t launch_momentum_orient(const MatDev *mats, int32_t nmat,
-                                  int64_t total_tiles, StepScalars s, bool fp32,
+                                  int64_t total_tiles, StepScalars s,
                                   hipStream_t st);
 hipError_t launch_update_direct(const MatDev *mats, int32_t nmat,
                                 int64_t total_chunks, StepScalars s,

@@ -30,8 +30,8 @@ def bf16_pair(x):
 
 
 def uses_pairs(steps: int) -> bool:
-    """The library stores B (direct chain) and P (Gram-space chain) as pairs
-    from six iterations on."""
+    """The library stores B (direct chain), P and T (Gram-space chain) as
+    pairs from six iterations on."""
     return steps >= 6
 
 
@@ -56,8 +56,9 @@ def ns_gram_bf16_storage(X0, a, b, c, steps, phases, round_x0=True, pairs=None):
     A P^2 and Q stored as bf16 (products in fp32), each stored m x m matrix
     made exactly symmetric from its upper triangle, X <- Q X at the end of
     every phase (the lengths in ``phases``, summing to ``steps``) in bf16,
-    the last one kept in fp32.  ``pairs``: every P stored as a hi + lo pair
-    (default: as the library does for this many iterations)."""
+    the last one kept in fp32.  ``pairs``: every P and every T = P P stored
+    as a hi + lo pair (default: as the library does for this many
+    iterations)."""
     assert sum(phases) == steps
     pairs = uses_pairs(steps) if pairs is None else pairs
     store_p = bf16_pair if pairs else rne_bf16
@@ -73,7 +74,7 @@ def ns_gram_bf16_storage(X0, a, b, c, steps, phases, round_x0=True, pairs=None):
         for i in range(L):
             P = store_p(sym(to_f32(a * np.eye(m) + b * A + c * to_f32(A @ A.T))))
             if i + 1 < L:
-                T = rne_bf16(sym(to_f32(P @ P.T)))
+                T = store_p(sym(to_f32(P @ P.T)))
                 A = rne_bf16(sym(to_f32(A @ T.T)))
             Q = P if Q is None else rne_bf16(sym(to_f32(Q @ P.T)))
         Xn = to_f32(Q @ X)

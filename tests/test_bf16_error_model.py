@@ -156,3 +156,68 @@ def test_gram_space_longer_phases_or_fewer_iterations_lose_accuracy():
     assert ratio(5, [5]) > 100
     assert ratio(5, [3, 2]) > 2.5
     assert ratio(2, [2]) > 5
+
+
+def test_gram_space_t_pairs_on_a_small_matrix():
+    """Why T = P P is a pair too: on the 17 x 100 input of the GPU phase-split
+    test at 6 iterations, pairs for P alone leave about 1.9e-2, P and T
+    about 1.0e-2 (the GPU gave 1.98e-2 with P alone)."""
+    import torch
+    from _bf16_model import bf16_pair, rne_bf16, to_f32
+    from synth import random_case
+    k = 6
+    base = 10_000 * (40 + k) + 10 * 2            # Case(..., seed=46), third matrix
+    G = random_case(base + 2, 17, 100, 1e-3, "bf16")
+    M0 = random_case(base + 3, 17, 100, 1e-3, "f32")
+    M1 = muon.momentum_accumulate(M0, G, 0.95)
+    X0r, _ = muon.normalise_and_orient(M1, 1e-7)
+    U = torch.from_numpy(M1.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    X0, _ = muon.normalise_and_orient(U, 1e-7)
+    a, b, c = muon.QUINTIC
+
+    def sym(M):
+        return np.triu(M) + np.triu(M, 1).T
+
+    def chain(pair_t):
+        X = to_f32(X0)
+        for ph in range(3):
+            A = rne_bf16(sym(to_f32(X @ X.T)))
+            P0 = bf16_pair(sym(to_f32(a * np.eye(17) + b * A + c * to_f32(A @ A))))
+            T = (bf16_pair if pair_t else rne_bf16)(sym(to_f32(P0 @ P0)))
+            A1 = rne_bf16(sym(to_f32(A @ T)))
+            P1 = bf16_pair(sym(to_f32(a * np.eye(17) + b * A1 + c * to_f32(A1 @ A1))))
+            Q = rne_bf16(sym(to_f32(P0 @ P1)))
+            X = to_f32(Q @ X) if ph == 2 else rne_bf16(to_f32(Q @ X))
+        return X
+    ref = muon.newton_schulz(X0r, a, b, c, k)
+    err = lambda Y: np.linalg.norm(Y - ref) / np.linalg.norm(ref)
+    e_p, e_pt = err(chain(False)), err(chain(True))
+    assert 1.7e-2 < e_p < 2.2e-2, e_p
+    assert e_pt < 1.2e-2, e_pt
+    from _bf16_model import ns_gram_bf16_storage
+    assert abs(err(ns_gram_bf16_storage(X0, a, b, c, k, [2, 2, 2], round_x0=False)) - e_pt) < 1e-6 * e_pt + 1e-12
+
+
+def test_small_matrices_exceed_the_bar_in_bf16():
+    """Why matrices with m < 128 run in fp32: Gaussian inputs shaped like the
+    momentum-plus-gradient of the GPU tests; at m = 32 bf16 storage passes
+    about 1.9e-2 at five iterations on some seeds and 2.4e-2 at eight even
+    with B as a pair, while at m = 128 it stays below 1.3e-2 and 1e-2."""
+    from _bf16_model import rne_bf16
+
+    def worst(m, n, k, pairs):
+        w = 0.0
+        for seed in range(8):
+            rng = np.random.default_rng(2000 + seed)
+            G = rne_bf16(rng.standard_normal((m, n)) * 1e-3)
+            M1 = 0.95 * rng.standard_normal((m, n)).astype(np.float32) * 1e-3 + G
+            X0, _ = muon.normalise_and_orient(rne_bf16(M1), 1e-7)
+            X0r, _ = muon.normalise_and_orient(M1, 1e-7)
+            ref = muon.newton_schulz(X0r, *muon.QUINTIC, k)
+            emu = ns_bf16_storage(X0, *muon.QUINTIC, k, round_x0=False, pairs=pairs)
+            w = max(w, np.linalg.norm(emu - ref) / np.linalg.norm(ref))
+        return w
+    assert worst(32, 200, 5, False) > 1.8e-2
+    assert worst(17, 33, 8, True) > tol_o_bf16(8)
+    assert worst(128, 512, 5, False) < 1.3e-2
+    assert worst(128, 512, 8, True) < 1e-2

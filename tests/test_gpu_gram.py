@@ -3,10 +3,10 @@ against the fp64 oracle of the direct iteration.
 
 The Gram-space chain computes the same X_K in exact arithmetic (every
 iterate is a polynomial in the first A = X X^T); the bars are the direct
-chain's: <= 2e-2 relative Frobenius for the bf16 chain up to 5 iterations,
-the 6-8 iteration bar above that, <= 1e-4 in the fp32 checking mode.
-Matrices with max(r, c) >= 2 min(r, c) take it at ns_steps >= 5; the others
-of the same call keep the direct chain.
+chain's: <= 2e-2 relative Frobenius for the bf16 chain at every ns_steps up
+to 8, <= 1e-4 in the fp32 checking mode.  Matrices with max(r, c) >=
+2 min(r, c) and min(r, c) >= 128 take it at ns_steps >= 5; the others of the
+same call keep the direct chain (in fp32 below m = 128 in a bf16 step).
 """
 
 import numpy as np
@@ -29,15 +29,15 @@ def nsd():
 
 
 WIDE = [
-    (128, 256),     # aspect exactly 2: one tile each way
+    (128, 256),     # aspect exactly 2, m at the chain's threshold: one tile each way
     (300, 700),     # ragged both ways, 2 x 3 tiles
     (700, 300),     # tall: transposed
     (257, 1000),    # one row past a tile boundary
     (1000, 257),
-    (100, 1000),    # aspect 10
-    (17, 100),
-    (1, 300),       # m = 1: A is 1 x 1
-    (300, 1),
+    (130, 1300),    # aspect 10
+    (129, 4000),    # aspect 31
+    (140, 42000),   # aspect 300
+    (42000, 140),
     (520, 1100),    # 3 x 5 tiles
 ]
 
@@ -62,7 +62,7 @@ def test_gram_ns_steps(nsd, k):
     """Phase splits 2+2+1, 2+2+2, 2+2+2+1, 2+2+2+2; at 3 the flag leaves the
     direct chain in place."""
     say(f"gram ns_steps {k}")
-    shapes = [(300, 700), (1000, 257), (17, 100)]
+    shapes = [(300, 700), (1000, 257), (130, 700)]
     case = Case(shapes, "bf16", "bf16", seed=40 + k, m_std=1e-3)
     opts = nsd.StepOptions(ns_steps=k, gram_ns=True)
     err = check_step(case, opts, case.run_gpu(opts), case.run_oracle(opts))
@@ -80,13 +80,15 @@ def test_gram_fp32_mode(nsd, shape):
 
 def test_gram_mixed_with_direct_chain(nsd):
     """One call whose square and near-square matrices keep the direct chain
-    while the wide and tall ones take the Gram-space chain; twice, bitwise
-    equal (deterministic)."""
+    while the wide and tall ones take the Gram-space chain, and the small
+    ones (m < 128) run the direct chain in fp32; twice, bitwise equal
+    (deterministic)."""
     shapes = [(513, 513), (300, 700), (300, 500), (700, 300), (17, 33), (1, 1), (256, 1024),
               (1024, 256), (64, 64), (129, 900)]
     opts = nsd.StepOptions(gram_ns=True)
     kinds = _kinds(nsd, shapes, opts)
-    assert kinds.count("final") == 1   # the two chains' last applies share a launch
+    # the two bf16 chains' last applies share a launch; the fp32 chain has its own
+    assert kinds.count("final") == 2
     case = Case(shapes, "bf16", "bf16", seed=33, m_std=1e-3)
     a = case.run_gpu(opts)
     err = check_step(case, opts, a, case.run_oracle(opts))

@@ -267,3 +267,25 @@ def test_side_stream_with_temporary_workspace(nsd):
     gpu = ([to_host(p) for p in P], [to_host(m) for m in M], [to_host(o) for o in O])
     err = check_step(case, opts, gpu, case.run_oracle(opts))
     say(f"  O rel err {err:.3e}")
+
+
+SMALL = [(1, 300), (300, 1), (8, 50), (17, 33), (17, 100), (32, 200), (200, 32), (64, 400),
+         (100, 100), (127, 500)]
+
+
+@pytest.mark.parametrize("k", [5, 8])
+def test_small_matrices_run_in_fp32(nsd, k):
+    """In a bf16 step, matrices with min(r, c) < 128 run their chain in fp32
+    (their singular values sit in the quintic's band for most iterations,
+    where bf16 storage reaches about 2e-2 at five iterations and 3e-2 at
+    eight): O within 1e-4 of fp64, plus the rounding of orth_out to bf16;
+    a 128-wide matrix of the same call keeps the bf16 chain."""
+    from _gpu_util import TOL_O_FP32
+    shapes = SMALL + [(128, 512)]
+    kinds = [kd for kd, _ in nsd.step_launches(shapes, nsd.StepOptions(ns_steps=k))]
+    assert kinds.count("final") == 2
+    say(f"small matrices, ns_steps {k}")
+    case = Case(SMALL, "bf16", "bf16", seed=60 + k, m_std=1e-3)
+    opts = nsd.StepOptions(ns_steps=k, gram_ns=True)
+    err = check_step(case, opts, case.run_gpu(opts), case.run_oracle(opts), tol_o=TOL_O_FP32)
+    say(f"  worst O rel err {err:.3e}")

@@ -19,10 +19,20 @@ def pairs(k, fp32=False):
     return k >= 6 and not fp32
 
 
+def small(m, fp32=False):
+    """In a bf16 step, matrices with m < 128 run their chain in fp32 (no pairs)."""
+    return m < 128 and not fp32
+
+
 def direct_flops(m, n, k, fp32=False):
-    """Executed flops: with pairs, Apply runs a second pass over B's low half."""
-    apply_passes = 2 if pairs(k, fp32) else 1
-    return k * (m * (m + 1) * n + m * m * (m + 1) + apply_passes * 2 * m * m * n)
+    """Executed flops: with pairs, Apply runs a second pass over B's low half
+    from the third iteration on."""
+    paired = max(k - 2, 0) if pairs(k, fp32) and not small(m, fp32) else 0
+    return k * (m * (m + 1) * n + m * m * (m + 1) + 2 * m * m * n) + paired * 2 * m * m * n
+
+
+def uses_gram(m, n, k, gram):
+    return gram and k >= 5 and n >= 2 * m and m >= 128
 
 
 def phases(k):
@@ -33,10 +43,11 @@ def square_passes(L, split):
     """Products of m_p x m_p matrices in a phase of L iterations, counted in
     full passes: L of P, L - 1 of P P, L - 1 of A T, L - 1 of Q P.  With
     pairs, P P reads a pair on both sides (3 passes), the first Q P too
-    (Q is the first P), later ones on one side (2)."""
+    (Q is the first P), later ones on one side (2), and A T reads T's pair
+    (2)."""
     if not split:
         return 4 * L - 3
-    return L + 3 * (L - 1) + (L - 1) + (3 + 2 * (L - 2) if L >= 2 else 0)
+    return L + 3 * (L - 1) + 2 * (L - 1) + (3 + 2 * (L - 2) if L >= 2 else 0)
 
 
 def gram_flops(m, n, k, fp32=False):
@@ -75,16 +86,22 @@ def test_direct_chain_sequence_and_flops():
 
 
 def test_gram_chain_selection_and_flops():
-    shapes = LLAMA8B_OWNER0 + [(300, 599), (300, 600), (601, 300), (1, 1)]
+    shapes = LLAMA8B_OWNER0 + [(300, 599), (300, 600), (601, 300), (128, 256), (127, 256)]
     L = nsd.step_launches(shapes, nsd.StepOptions(gram_ns=True))
     total = sum(f for _, f in L)
     want = 0
     for r, c in shapes:
         m, n = min(r, c), max(r, c)
-        want += gram_flops(m, n, 5) if n >= 2 * m else direct_flops(m, n, 5)
+        want += gram_flops(m, n, 5) if uses_gram(m, n, 5, True) else direct_flops(m, n, 5)
     assert total == want
-    # the two chains' launches of the same kind share grouped launches: one
-    # final, and fewer launches than the two chains run apart
+    # the two bf16 chains' launches of the same kind share grouped launches:
+    # one final for them, one for the small matrix's fp32 chain (127 x 256),
+    # and fewer launches than the two chains run apart
+    kinds = [k for k, _ in L]
+    assert kinds.count("final") == 2
+    assert kinds[-15:] == ["gram", "square", "apply"] * 4 + ["gram", "square", "final"]
+    shapes = shapes[:-1]
+    L = nsd.step_launches(shapes, nsd.StepOptions(gram_ns=True))
     kinds = [k for k, _ in L]
     assert kinds.count("final") == 1
     alone = len(nsd.step_launches(shapes[:8], nsd.StepOptions(gram_ns=True))) + \
@@ -111,9 +128,9 @@ def test_gram_needs_more_workspace():
 
 def test_pairs_add_workspace_not_launches():
     """From six iterations on: one more m_p x m_p buffer per direct-chain
-    matrix (B's low half) and two per Gram-space matrix (the low halves of
-    the first and the later P); the launch sequence is the same, and the fp32
-    mode has no pairs."""
+    matrix (B's low half) and three per Gram-space matrix (the low halves of
+    the first and the later P and of T); the launch sequence is the same,
+    and the fp32 mode has no pairs."""
     def ws(opts, shapes):
         arr = (_lib.Matrix * len(shapes))()
         for i, (r, c) in enumerate(shapes):
@@ -124,15 +141,16 @@ def test_pairs_add_workspace_not_launches():
                                                      ctypes.byref(out)))
         return out.value
     buf = 512 * 512 * 2
-    for gram, shapes, extra in ((False, [(300, 700)], buf), (True, [(300, 700)], 2 * buf),
-                                (True, [(700, 300)], 2 * buf), (True, [(513, 300)], buf)):
+    for gram, shapes, extra in ((False, [(300, 700)], buf), (True, [(300, 700)], 3 * buf),
+                                (True, [(700, 300)], 3 * buf), (True, [(513, 300)], buf),
+                                (True, [(100, 700)], 0)):
         o5 = nsd.StepOptions(ns_steps=5, gram_ns=gram)
         o6 = nsd.StepOptions(ns_steps=6, gram_ns=gram)
         k5 = [kd for kd, _ in nsd.step_launches(shapes, o5)]
         k6 = [kd for kd, _ in nsd.step_launches(shapes, o6)]
         d = ws(o6, shapes) - ws(o5, shapes)
         assert extra <= d < extra + 65536, (gram, shapes, d)
-        if not gram or shapes == [(513, 300)]:   # the direct chain: one more iteration
+        if not gram or shapes in ([(513, 300)], [(100, 700)]):   # the direct chain: one more iteration
             assert k6 == k5[:2] + ["gram", "square", "apply"] + k5[2:]
         f6 = nsd.StepOptions(ns_steps=6, gram_ns=gram, ns_fp32=True)
         f5 = nsd.StepOptions(ns_steps=5, gram_ns=gram, ns_fp32=True)
@@ -178,11 +196,12 @@ def test_random_plans_are_consistent(seed):
             want = 0
             for r, c in shapes:
                 m, nn = min(r, c), max(r, c)
-                use = gram and k >= 5 and nn >= 2 * m
-                want += gram_flops(m, nn, k) if use else direct_flops(m, nn, k)
+                want += gram_flops(m, nn, k) if uses_gram(m, nn, k, gram) else direct_flops(m, nn, k)
             assert sum(f for _, f in L) == want
             if k > 0:
-                assert [x for x, _ in L].count("final") == 1
+                n_small = any(small(min(r, c)) for r, c in shapes)
+                n_big = any(not small(min(r, c)) for r, c in shapes)
+                assert [x for x, _ in L].count("final") == n_small + n_big
 
 
 def test_nonfinite_flags_offset():
