@@ -264,10 +264,18 @@ __device__ __forceinline__ void stage_tile_flush(lds_char *lds, uint16_t *dst, i
   }
 }
 
-template <typename T, int MODE>
+// Role of a launch (a template argument, so that each kernel instance holds
+// only its own code): whole tiles; pieces of split tiles (the mainloop over
+// steps [k0, k1), fp32 accumulators to a partial slot); or the reduce
+// entries of split tiles (the sum of their pieces' slots, then the tile's
+// epilogue).
+constexpr int kRoleWhole = 0, kRolePiece = 1, kRoleReduce = 2;
+
+template <typename T, int MODE, int ROLE>
 __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restrict__ mats,
                                                            const TileEntry *__restrict__ tiles,
-                                                           StageXcd xcd, StepScalars s) {
+                                                           StageXcd xcd, StepScalars s,
+                                                           f32x4 *__restrict__ splitk) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * kOperandBytes];  // 128 KB
   // C cast: generic -> LDS address space.  [2 stages][L, R][256 rows][128 B]
   lds_char *const lds = (lds_char *)smem;
@@ -323,6 +331,11 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   // R likewise: byte distances, so that picking a pass is arithmetic
   const int64_t dl1 = gl1 - gl, dl2 = gl_lo - gl1, dr1 = gr1 - gr, dr2 = gr - gr1;
   const int ntot = (1 + r_pair + l_pair) * nkt;
+  // split K: a piece runs steps [k0, k1) and leaves its accumulators in a
+  // partial slot; a reduce entry runs no step and starts from the sum of
+  // its pieces' slots
+  constexpr bool kPiece = ROLE == kRolePiece, kReduce = ROLE == kRoleReduce;
+  const int kbeg = kPiece ? e.k0 : 0, kend = kPiece ? e.k1 : ntot;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -564,28 +577,55 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   // is in flight after the loop.  The last step re-loads its own K range
   // into the free stage, which keeps the loop body free of a branch
   // (measured faster than skipping that load).
-  issue(0, 0);
-  stage_barrier();
-  if (wm == 1) plain_barrier();
-  for (int kt = 0; kt < ntot; ++kt) {
-    const lds_char *st = lds + (kt & 1) * kStageBytes;
-    issue((kt + 1) & 1, min(kt + 1, ntot - 1));
-    capture_ax(st, kt);
-    read_frag(st, 0, fa);
-    read_frag(st, 1, fb);
-    tr_fence();
-    tr_wait(fa);
-    tr_wait(fb);
-    __builtin_amdgcn_sched_barrier(0);
-    lds_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_frag(fa);
-    mfma_frag(fb);
-    __builtin_amdgcn_sched_barrier(0);
-    dma_barrier();
-    __builtin_amdgcn_sched_barrier(0);
+  if constexpr (!kReduce) {
+    issue(kbeg & 1, kbeg);
+    stage_barrier();
+    if (wm == 1) plain_barrier();
+    for (int kt = kbeg; kt < kend; ++kt) {
+      const lds_char *st = lds + (kt & 1) * kStageBytes;
+      issue((kt + 1) & 1, min(kt + 1, kend - 1));
+      capture_ax(st, kt);
+      read_frag(st, 0, fa);
+      read_frag(st, 1, fb);
+      tr_fence();
+      tr_wait(fa);
+      tr_wait(fb);
+      __builtin_amdgcn_sched_barrier(0);
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_frag(fa);
+      mfma_frag(fb);
+      __builtin_amdgcn_sched_barrier(0);
+      dma_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (wm == 0) plain_barrier();
   }
-  if (wm == 0) plain_barrier();
+
+  // Partial slots: fragment (i, j) of thread t at vector (i * kFragN + j) *
+  // kThreads + t of the slot; the slot's base is uniform.
+  constexpr int64_t kSlotVecs = kPartialSlotFloats / 4;
+  if constexpr (kPiece) {
+    f32x4 *const base = splitk + static_cast<int64_t>(e.slot) * kSlotVecs;
+#pragma unroll
+    for (int i = 0; i < kFragM; ++i)
+#pragma unroll
+      for (int j = 0; j < kFragN; ++j) base[(i * kFragN + j) * kThreads + tid] = acc[i][j];
+    return;
+  }
+  if constexpr (kReduce) {
+    // each element sums its pieces in slot order; one fragment row at a
+    // time, so that few loads are in flight beside the accumulators
+    const f32x4 *const base = splitk + static_cast<int64_t>(e.slot) * kSlotVecs;
+#pragma unroll
+    for (int i = 0; i < kFragM; ++i) {
+#pragma unroll
+      for (int j = 0; j < kFragN; ++j) acc[i][j] = base[(i * kFragN + j) * kThreads + tid];
+      for (int32_t q = 1; q < e.k0; ++q)
+#pragma unroll
+        for (int j = 0; j < kFragN; ++j) acc[i][j] += base[q * kSlotVecs + (i * kFragN + j) * kThreads + tid];
+    }
+  }
 
   // ---- epilogue: lane holds C[row0 + 4*g4 + v][col0 + r16], v = 0..3 ----
   // The four values of a lane are four consecutive rows of one column, i.e.
@@ -857,36 +897,47 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   }
 }
 
-template <typename T>
-hipError_t launch_t(GemmMode mode, const MatDev *mats, const TileEntry *tiles, const StageXcd &xcd,
-                    StepScalars s, hipStream_t st) {
+template <typename T, int ROLE>
+hipError_t launch_role(GemmMode mode, const MatDev *mats, const TileEntry *tiles, const StageXcd &xcd,
+                       StepScalars s, f32x4 *splitk, hipStream_t st) {
   int32_t longest = 0;
   for (int x = 0; x < kXcds; ++x) longest = xcd.count[x] > longest ? xcd.count[x] : longest;
   if (longest == 0) return hipSuccess;
   const dim3 grid(static_cast<uint32_t>(longest) * kXcds), block(kThreads);
   switch (mode) {
     case kModeGram:
-      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeGram>), grid, block, 0, st, mats, tiles, xcd, s);
+      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeGram, ROLE>), grid, block, 0, st, mats, tiles, xcd, s, splitk);
       break;
     case kModeSquare:
-      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeSquare>), grid, block, 0, st, mats, tiles, xcd, s);
+      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeSquare, ROLE>), grid, block, 0, st, mats, tiles, xcd, s, splitk);
       break;
     case kModeApply:
-      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeApply>), grid, block, 0, st, mats, tiles, xcd, s);
+      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeApply, ROLE>), grid, block, 0, st, mats, tiles, xcd, s, splitk);
       break;
     default:
-      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeFinal>), grid, block, 0, st, mats, tiles, xcd, s);
+      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeFinal, ROLE>), grid, block, 0, st, mats, tiles, xcd, s, splitk);
       break;
   }
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_t(GemmMode mode, int role, const MatDev *mats, const TileEntry *tiles, const StageXcd &xcd,
+                    StepScalars s, float *splitk_f, hipStream_t st) {
+  f32x4 *splitk = reinterpret_cast<f32x4 *>(splitk_f);
+  switch (role) {
+    case kRolePiece: return launch_role<T, kRolePiece>(mode, mats, tiles, xcd, s, splitk, st);
+    case kRoleReduce: return launch_role<T, kRoleReduce>(mode, mats, tiles, xcd, s, splitk, st);
+    default: return launch_role<T, kRoleWhole>(mode, mats, tiles, xcd, s, splitk, st);
+  }
+}
+
 }  // namespace
 
-hipError_t launch_ns_stage(GemmMode mode, bool fp32, const MatDev *mats, const TileEntry *tiles,
-                           const StageXcd &xcd, StepScalars s, hipStream_t st) {
-  return fp32 ? launch_t<float>(mode, mats, tiles, xcd, s, st)
-              : launch_t<uint16_t>(mode, mats, tiles, xcd, s, st);
+hipError_t launch_ns_stage(GemmMode mode, bool fp32, int role, const MatDev *mats, const TileEntry *tiles,
+                           const StageXcd &xcd, StepScalars s, float *splitk, hipStream_t st) {
+  return fp32 ? launch_t<float>(mode, role, mats, tiles, xcd, s, splitk, st)
+              : launch_t<uint16_t>(mode, role, mats, tiles, xcd, s, splitk, st);
 }
 
 }  // namespace dmuon

@@ -173,6 +173,7 @@ struct Launch {
   std::vector<Part> parts;  // GEMM launches; all of one kind
   int32_t table = 0;        // MatDev table: the parts' matrices, in order
   int32_t list = 0;         // tile list over that table
+  int32_t role = 0;         // 0 whole tiles, 1 pieces of split tiles, 2 their reduce
   double flops = 0;         // algorithmic flops (symmetric products: upper triangle)
 };
 
@@ -193,6 +194,7 @@ struct Plan {
   // workspace layout (byte offsets)
   std::vector<int64_t> off_table, off_list;
   int64_t off_partials = 0, off_inv = 0, off_flags = -1;
+  int64_t off_splitk = -1, splitk_slots = 0;  // partial slots of split tiles
   int64_t table_bytes = 0;  // [0, table_bytes) is uploaded
   int64_t total_bytes = 0;
 };
@@ -332,6 +334,103 @@ std::vector<int> gram_phases(int K) {
 }
 
 // Builds the plan; with ws == nullptr only sizes are computed.
+// ---- split K for launches that leave CUs idle ----
+// A launch with fewer tiles than the chip has CUs runs as long as its
+// longest tile while most CUs idle (a single Qwen2.5-1.5B layer: about a
+// hundred Gram tiles of 140 K steps for 256 CUs).  Such a launch can run
+// its tiles in pieces over K instead: a launch of pieces, each writing its
+// fp32 accumulators to a partial slot, then a launch of reduce entries that
+// sum each tile's slots in a fixed order and run the tile's epilogue.  The
+// host picks the piece count per tile (at most kMaxPieces, pieces of at
+// least kMinPieceSteps steps) whose estimated time is least: the list
+// schedule of the pieces over the CUs, plus kSplitLaunchSteps for the reduce
+// launch, plus kSplitStepsPerPiece for each piece's partial slot (256 KB
+// written, then read back by the reduce, all pieces sharing the HBM: about
+// 0.07 of a K step each); no split when that does not beat the whole tiles.
+// Times are in K steps of one 256 x 256 tile (about 1.9 us).
+constexpr int kCUs = 256;
+constexpr int kMaxPieces = 16;
+constexpr int64_t kMinPieceSteps = 16;
+constexpr double kSplitLaunchSteps = 8.0;
+constexpr double kSplitStepsPerPiece = 0.07;
+
+// Greedy list schedule of item lengths (longest first) on `machines`
+// machines: the finishing time of the last one.
+int64_t list_makespan(std::vector<int64_t> len, int machines) {
+  std::sort(len.begin(), len.end(), std::greater<int64_t>());
+  std::vector<int64_t> heap(machines, 0);  // min-heap of machine loads
+  for (int64_t l : len) {
+    std::pop_heap(heap.begin(), heap.end(), std::greater<int64_t>());
+    heap.back() += l;
+    std::push_heap(heap.begin(), heap.end(), std::greater<int64_t>());
+  }
+  return *std::max_element(heap.begin(), heap.end());
+}
+
+// Pieces per tile for a launch whose tiles need steps[t] K steps; all ones
+// when splitting does not pay.
+std::vector<int32_t> choose_pieces(const std::vector<int64_t> &steps) {
+  std::vector<int32_t> best(steps.size(), 1);
+  if (steps.empty() || static_cast<int64_t>(steps.size()) >= kCUs) return best;
+  double best_t = static_cast<double>(list_makespan(steps, kCUs));
+  for (int smax = 2; smax <= kMaxPieces; ++smax) {
+    std::vector<int32_t> pieces(steps.size());
+    std::vector<int64_t> len;
+    bool any = false;
+    for (size_t t = 0; t < steps.size(); ++t) {
+      pieces[t] = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(smax, steps[t] / kMinPieceSteps)));
+      any |= pieces[t] > 1;
+      for (int32_t q = 0; q < pieces[t]; ++q)
+        len.push_back((steps[t] * (q + 1)) / pieces[t] - (steps[t] * q) / pieces[t]);
+    }
+    if (!any) break;
+    const double t_split = static_cast<double>(list_makespan(len, kCUs)) + kSplitLaunchSteps +
+                           kSplitStepsPerPiece * static_cast<double>(len.size());
+    if (t_split < best_t) {
+      best_t = t_split;
+      best = pieces;
+    }
+  }
+  return best;
+}
+
+// Per-XCD lists of entries with costs: costliest first, each to the XCD
+// with the least work so far (as build_stage_tiles does for blocks).
+void assign_xcds(const std::vector<std::pair<int64_t, TileEntry>> &items, std::vector<TileEntry> &out,
+                 StageXcd &xcd) {
+  std::vector<size_t> order(items.size());
+  std::iota(order.begin(), order.end(), 0);
+  std::stable_sort(order.begin(), order.end(),
+                   [&](size_t a, size_t b) { return items[a].first > items[b].first; });
+  std::vector<TileEntry> lists[kXcds];
+  int64_t load[kXcds] = {0};
+  for (size_t o : order) {
+    int x = 0;
+    for (int y = 1; y < kXcds; ++y)
+      if (load[y] < load[x]) x = y;
+    load[x] += items[o].first;
+    lists[x].push_back(items[o].second);
+  }
+  out.clear();
+  for (int x = 0; x < kXcds; ++x) {
+    xcd.first[x] = static_cast<int32_t>(out.size());
+    xcd.count[x] = static_cast<int32_t>(lists[x].size());
+    out.insert(out.end(), lists[x].begin(), lists[x].end());
+  }
+}
+
+// K-loop steps of every row of a launch's table (its parts' matrices).
+std::vector<int64_t> row_steps(const Plan &p, const Launch &l) {
+  std::vector<int64_t> out;
+  const int64_t kstep = l.fp32 ? 32 : 64;  // elements per 128-byte K step
+  for (const Part &pt : l.parts)
+    for (int32_t i : p.groups[pt.group]) {
+      const MatDev &d = p.mats[i];
+      out.push_back(pt.passes(l.kind) * ((l.kind == kLkGram ? d.np : d.mp) / kstep));
+    }
+  return out;
+}
+
 // In a bf16 step, a matrix with m = min(r, c) < kFp32BelowM runs its chain
 // in fp32 (its own launches, group 2).  Such a matrix's singular values
 // start near 1/sqrt(m), reach the quintic's band within one or two
@@ -390,6 +489,7 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
   p.lists.clear();
   p.list_xcd.clear();
   p.prog.clear();
+  p.splitk_slots = 0;
   // algorithmic flops of one stage over a group
   auto flops = [&](int g, int32_t kind) {
     double f = 0;
@@ -560,6 +660,46 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
       li = list_of.emplace(key, static_cast<int32_t>(p.lists.size()) - 1).first;
     }
     l.list = li->second;
+    // split K where the launch leaves CUs idle
+    const std::vector<TileEntry> &tl = p.lists[l.list];
+    const std::vector<int64_t> rs = row_steps(p, l);
+    std::vector<int64_t> steps;
+    for (const TileEntry &e : tl) steps.push_back(rs[e.mat]);
+    const std::vector<int32_t> pieces = choose_pieces(steps);
+    if (*std::max_element(pieces.begin(), pieces.end()) > 1) {
+      std::vector<std::pair<int64_t, TileEntry>> pc, rd;
+      int32_t slot = 0;
+      for (size_t t = 0; t < tl.size(); ++t) {
+        TileEntry r = tl[t];
+        r.k0 = pieces[t];
+        r.k1 = 0;
+        r.slot = slot;
+        rd.emplace_back(1, r);
+        for (int32_t q = 0; q < pieces[t]; ++q) {
+          TileEntry e = tl[t];
+          e.k0 = static_cast<int32_t>((steps[t] * q) / pieces[t]);
+          e.k1 = static_cast<int32_t>((steps[t] * (q + 1)) / pieces[t]);
+          e.slot = slot++;
+          pc.emplace_back(e.k1 - e.k0, e);
+        }
+      }
+      p.splitk_slots = std::max<int64_t>(p.splitk_slots, slot);
+      Launch lp = l, lr = l;
+      lp.role = 1;
+      lr.role = 2;
+      lr.flops = 0;
+      p.lists.emplace_back();
+      p.list_xcd.emplace_back();
+      assign_xcds(pc, p.lists.back(), p.list_xcd.back());
+      lp.list = static_cast<int32_t>(p.lists.size()) - 1;
+      p.lists.emplace_back();
+      p.list_xcd.emplace_back();
+      assign_xcds(rd, p.lists.back(), p.list_xcd.back());
+      lr.list = static_cast<int32_t>(p.lists.size()) - 1;
+      p.prog.push_back(std::move(lp));
+      p.prog.push_back(std::move(lr));
+      continue;
+    }
     p.prog.push_back(std::move(l));
   }
 
@@ -580,6 +720,11 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
     off = round_up(off + int64_t(sizeof(TileEntry)) * static_cast<int64_t>(p.lists[l].size()), 256);
   }
   p.table_bytes = off;
+  p.off_splitk = -1;
+  if (p.splitk_slots > 0) {
+    p.off_splitk = off;
+    off = round_up(off + 4 * kPartialSlotFloats * p.splitk_slots, 256);
+  }
   p.off_partials = off;
   off = round_up(off + 8 * (K > 0 ? tr : ew), 256);
   p.off_inv = off;
@@ -659,10 +804,16 @@ bool plan_consistent(const Plan &p) {
     }
     const bool sym = l.kind == kLkGram || l.kind == kLkSquare;
     const int32_t n = static_cast<int32_t>(rows.size());
+    const std::vector<int64_t> rs = row_steps(p, l);
     for (const TileEntry &e : p.lists[l.list]) {
       if (e.mat < 0 || e.mat >= n) return false;
       const MatDev &d = *rows[e.mat];
       if (e.ti >= d.tm || e.tj >= (sym ? d.tm : d.tn) || (sym && e.tj < e.ti)) return false;
+      // pieces: a step range inside the tile's K loop and a slot; reduce
+      // entries: at least one slot, all inside the partial region
+      if (l.role == 1 && (e.k0 < 0 || e.k1 <= e.k0 || e.k1 > rs[e.mat] || e.slot < 0 || e.slot >= p.splitk_slots))
+        return false;
+      if (l.role == 2 && (e.k1 != 0 || e.k0 < 1 || e.slot < 0 || e.slot + e.k0 > p.splitk_slots)) return false;
     }
   }
   return true;
@@ -1047,7 +1198,8 @@ static int muon_step_impl(const dmuon_matrix *mats, int32_t n, const dmuon_step_
                               : l.kind == kLkApply  ? kModeApply
                                                     : kModeFinal;
         const TileEntry *tl = reinterpret_cast<const TileEntry *>(ws + p.off_list[l.list]);
-        rc = launched(launch_ns_stage(mode, l.fp32, dtab(l.table), tl, p.list_xcd[l.list], sc, s),
+        float *splitk = p.off_splitk >= 0 ? reinterpret_cast<float *>(ws + p.off_splitk) : nullptr;
+        rc = launched(launch_ns_stage(mode, l.fp32, l.role, dtab(l.table), tl, p.list_xcd[l.list], sc, splitk, s),
                       "Newton-Schulz stage launch");
       }
     }

@@ -77,11 +77,23 @@ struct MatDev {
                         // step), else bf16
 };
 
-// One 256 x 256 output tile of a grouped GEMM stage.
+// One 256 x 256 output tile of a grouped GEMM stage, or a piece of one
+// (split K).  In a launch of whole tiles only mat, ti, tj count.  In a
+// launch of pieces: steps [k0, k1) of the tile's K loop (counted over all
+// of its passes), whose fp32 accumulators go to partial slot `slot`.  In a
+// reduce launch (after the pieces' launch): the sum of partial slots
+// slot .. slot + k0 - 1, in that order, then the tile's epilogue.
 struct TileEntry {
   int32_t mat;
   uint16_t ti, tj;
+  int32_t k0, k1;
+  int32_t slot;
+  int32_t reserved_;
 };
+// fp32 accumulators of one 256 x 256 tile in a partial slot: 32 fragments
+// of 16 x 16 per wave, four floats per lane, laid out [fragment][thread]
+// so that every fragment's store is one contiguous 8 KB run.
+constexpr int64_t kPartialSlotFloats = int64_t(256) * 256;
 
 // Work-groups are handed to the 8 XCDs (each with its own L2) in turn: group
 // w runs on XCD w % 8.  A stage therefore keeps one tile list per XCD, and
@@ -169,8 +181,10 @@ hipError_t noalloc_scratch(void **ptr);
 
 // ---- launchers (gemm.hip) ----
 // mats: the launch's table (per-matrix operands and coefficients).
-hipError_t launch_ns_stage(GemmMode mode, bool fp32, const MatDev *mats,
+// role: 0 whole tiles, 1 pieces of split tiles, 2 their reduce entries
+// (TileEntry); splitk: the partial slots (nullptr when the launch has none).
+hipError_t launch_ns_stage(GemmMode mode, bool fp32, int role, const MatDev *mats,
                            const TileEntry *tiles, const StageXcd &xcd,
-                           StepScalars s, hipStream_t st);
+                           StepScalars s, float *splitk, hipStream_t st);
 
 }  // namespace dmuon

@@ -282,10 +282,31 @@ def test_small_matrices_run_in_fp32(nsd, k):
     a 128-wide matrix of the same call keeps the bf16 chain."""
     from _gpu_util import TOL_O_FP32
     shapes = SMALL + [(128, 512)]
-    kinds = [kd for kd, _ in nsd.step_launches(shapes, nsd.StepOptions(ns_steps=k))]
+    kinds = [kd for kd, f in nsd.step_launches(shapes, nsd.StepOptions(ns_steps=k)) if f > 0]
     assert kinds.count("final") == 2
     say(f"small matrices, ns_steps {k}")
     case = Case(SMALL, "bf16", "bf16", seed=60 + k, m_std=1e-3)
     opts = nsd.StepOptions(ns_steps=k, gram_ns=True)
     err = check_step(case, opts, case.run_gpu(opts), case.run_oracle(opts), tol_o=TOL_O_FP32)
+    say(f"  worst O rel err {err:.3e}")
+
+
+@pytest.mark.parametrize("shapes,k,gram,fp32", [
+    ([(2048, 2048)], 5, False, False),      # Gram and Square split (36 tiles of 32 steps)
+    ([(2048, 2048)], 8, False, False),      # with B's pairs: Apply and Final split too
+    ([(2048, 4608)], 6, True, False),       # Gram-space chain, P and T pairs
+    ([(2048, 2048)], 5, False, True),       # fp32 mode: 64-step tiles, every stage split
+    ([(2048, 2048), (300, 700)], 5, True, False),   # tiles of one and of several pieces side by side
+])
+def test_split_k_stages(nsd, shapes, k, gram, fp32):
+    """Launches with fewer tiles than CUs run as pieces over K plus a reduce
+    launch (the plan shows each split stage as a piece launch and a reduce
+    launch of the same kind); the result matches the oracle."""
+    opts = nsd.StepOptions(ns_steps=k, gram_ns=gram, ns_fp32=fp32)
+    L = nsd.step_launches(shapes, opts)
+    assert any(f == 0 for kd, f in L if kd in ("gram", "square", "apply", "final"))
+    dt = "f32" if fp32 else "bf16"
+    case = Case(shapes, dt, dt, seed=70 + k, m_std=1e-3)
+    say(f"split-K step {shapes}, ns_steps {k}, gram_ns {gram}, fp32 {fp32}")
+    err = check_step(case, opts, case.run_gpu(opts), case.run_oracle(opts))
     say(f"  worst O rel err {err:.3e}")

@@ -201,7 +201,46 @@ def test_random_plans_are_consistent(seed):
             if k > 0:
                 n_small = any(small(min(r, c)) for r, c in shapes)
                 n_big = any(not small(min(r, c)) for r, c in shapes)
-                assert [x for x, _ in L].count("final") == n_small + n_big
+                assert [x for x, f in L if f > 0].count("final") == n_small + n_big
+                check_split_launches(L)
+
+
+def check_split_launches(L):
+    """A split stage is a launch of pieces (the stage's flops) followed by a
+    launch of reduce entries of the same kind (no flops)."""
+    gemm = ("gram", "square", "apply", "final")
+    for j, (kind, f) in enumerate(L):
+        if kind in gemm and f == 0:
+            assert j > 0 and L[j - 1][0] == kind and L[j - 1][1] > 0, (j, L)
+
+
+def test_split_k_where_launches_leave_cus_idle():
+    """Qwen2.5-1.5B layer: its Gram launches (about a hundred tiles, up to
+    140 K steps) run split; the Llama-3.1-8B share (1088+ tiles per launch)
+    and short-K launches (24 steps) do not.  A single 2048 x 2048 matrix
+    splits its symmetric stages, and Apply too where its K loop is long."""
+    from synth import workload
+    w = workload(2)
+    shapes = [(r, c) for _, r, c in w.shapes]
+    for gram in (False, True):
+        L = nsd.step_launches(shapes, nsd.StepOptions(gram_ns=gram))
+        check_split_launches(L)
+        reduces = [k for k, f in L if k in ("gram", "square", "apply", "final") and f == 0]
+        assert reduces and set(reduces) == {"gram"}, reduces
+    L = nsd.step_launches(LLAMA8B_OWNER0, nsd.StepOptions(gram_ns=True))
+    assert all(f > 0 for k, f in L if k in ("gram", "square", "apply", "final"))
+    # a single 2048 x 2048 matrix: 36 symmetric tiles of 32 K steps split;
+    # 64 Apply tiles of 32 steps do not (two pieces would not pay for the
+    # reduce), but do when B's pairs double Apply's K loop (ns_steps 8) and
+    # in the fp32 mode (64 steps of 32 elements)
+    def split_kinds(opts):
+        L = nsd.step_launches([(2048, 2048)], opts)
+        check_split_launches(L)
+        assert sum(f for _, f in L) == direct_flops(2048, 2048, opts.ns_steps, opts.ns_fp32)
+        return {k for k, f in L if k in ("gram", "square", "apply", "final") and f == 0}
+    assert split_kinds(nsd.StepOptions()) == {"gram", "square"}
+    assert split_kinds(nsd.StepOptions(ns_steps=8)) == {"gram", "square", "apply", "final"}
+    assert split_kinds(nsd.StepOptions(ns_fp32=True)) == {"gram", "square", "apply", "final"}
 
 
 def test_nonfinite_flags_offset():
