@@ -20,32 +20,39 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// Every buffer the kernels read or write element by element is device
+// (global) memory.  Accesses go through address-space-1 pointers: a generic
+// pointer compiles to flat instructions, which the compiler must assume may
+// alias LDS and which also count on the LDS wait counter, so each LDS access
+// after one would wait for it.
+typedef __attribute__((address_space(1))) uint16_t g_u16;
+typedef __attribute__((address_space(1))) float g_f32;
+
 // Element access by run-time dtype code for caller buffers.
 __device__ __forceinline__ float load_elem(const void *p, int32_t dt, int64_t i) {
-  return dt == kBF16 ? bf16_bits_to_f32(static_cast<const uint16_t *>(p)[i])
-                     : static_cast<const float *>(p)[i];
+  return dt == kBF16 ? bf16_bits_to_f32(((const g_u16 *)p)[i]) : ((const g_f32 *)p)[i];
 }
 
 __device__ __forceinline__ void store_elem(void *p, int32_t dt, int64_t i, float v) {
   if (dt == kBF16)
-    static_cast<uint16_t *>(p)[i] = f32_to_bf16_bits(v);
+    ((g_u16 *)p)[i] = f32_to_bf16_bits(v);
   else
-    static_cast<float *>(p)[i] = v;
+    ((g_f32 *)p)[i] = v;
 }
 
 // Workspace element type: bf16 (stored as raw bits) or fp32.
 template <typename T> struct WsType;
 template <> struct WsType<uint16_t> {
   static __device__ __forceinline__ float ld(const uint16_t *p, int64_t i) {
-    return bf16_bits_to_f32(p[i]);
+    return bf16_bits_to_f32(((const g_u16 *)p)[i]);
   }
   static __device__ __forceinline__ void st(uint16_t *p, int64_t i, float v) {
-    p[i] = f32_to_bf16_bits(v);
+    ((g_u16 *)p)[i] = f32_to_bf16_bits(v);
   }
 };
 template <> struct WsType<float> {
-  static __device__ __forceinline__ float ld(const float *p, int64_t i) { return p[i]; }
-  static __device__ __forceinline__ void st(float *p, int64_t i, float v) { p[i] = v; }
+  static __device__ __forceinline__ float ld(const float *p, int64_t i) { return ((const g_f32 *)p)[i]; }
+  static __device__ __forceinline__ void st(float *p, int64_t i, float v) { ((g_f32 *)p)[i] = v; }
 };
 
 // Index of the entry whose [first, next first) range holds `w`, for a

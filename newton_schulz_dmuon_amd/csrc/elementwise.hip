@@ -30,18 +30,21 @@ __device__ __forceinline__ double block_sum_f64(double v, double *lds) {
   return s;  // valid in thread 0
 }
 
+typedef unsigned int vu32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) vu32x2 g_u32x2;
+typedef __attribute__((address_space(1))) f32x4 g_f32x4;
+
 // Four consecutive bf16 or fp32 values at flat index i (i multiple of 4).
 __device__ __forceinline__ f32x4 load_grad4(const void *g, int32_t dt, int64_t i) {
   f32x4 r;
   if (dt == kBF16) {
-    const uint2 v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(g) + i);
+    const vu32x2 v = *(const g_u32x2 *)(static_cast<const uint16_t *>(g) + i);
     r[0] = __uint_as_float(v.x << 16);
     r[1] = __uint_as_float(v.x & 0xffff0000u);
     r[2] = __uint_as_float(v.y << 16);
     r[3] = __uint_as_float(v.y & 0xffff0000u);
   } else {
-    const float4 v = *reinterpret_cast<const float4 *>(static_cast<const float *>(g) + i);
-    r[0] = v.x; r[1] = v.y; r[2] = v.z; r[3] = v.w;
+    r = *(const g_f32x4 *)(static_cast<const float *>(g) + i);
   }
   return r;
 }
@@ -51,15 +54,15 @@ __device__ __forceinline__ f32x4 load_grad4(const void *g, int32_t dt, int64_t i
 template <typename T> struct Vec4St;
 template <> struct Vec4St<uint16_t> {
   static __device__ __forceinline__ void st(uint16_t *p, const float (&v)[4]) {
-    uint2 u;
+    vu32x2 u;
     u.x = f32_to_bf16_bits(v[0]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[1])) << 16);
     u.y = f32_to_bf16_bits(v[2]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[3])) << 16);
-    *reinterpret_cast<uint2 *>(p) = u;
+    *(g_u32x2 *)p = u;
   }
 };
 template <> struct Vec4St<float> {
   static __device__ __forceinline__ void st(float *p, const float (&v)[4]) {
-    *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    *(g_f32x4 *)p = f32x4{v[0], v[1], v[2], v[3]};
   }
 };
 
@@ -131,28 +134,52 @@ __global__ __launch_bounds__(256) void finalize_norm_kernel(const MatDev *__rest
 // so that M is read in 512-byte and X^T written in 128-byte row segments.
 // The 1/(||U||_F + eps) scale is applied by the first iteration's Gram and
 // Apply epilogues, so M is read once.
-__device__ __forceinline__ void momentum4(const MatDev &d, int64_t ur, int64_t uc, float mu, bool nesterov,
-                                          bool vec, float (&u)[4]) {
+// A thread's two four-element pieces are loaded before either is updated
+// (mom_load for both, then momentum4 for both), so that four HBM reads per
+// thread are in flight at once.
+struct MomPiece {
+  int64_t ur, uc;
+  bool full;  // four valid elements with 16-byte aligned M: vector path
+  f32x4 m;
+  f32x4 g;
+};
+
+__device__ __forceinline__ MomPiece mom_load(const MatDev &d, int64_t ur, int64_t uc, bool vec) {
+  MomPiece pc;
+  pc.ur = ur;
+  pc.uc = uc;
+  pc.full = vec && ur < d.rows && uc + 4 <= d.cols;
+  if (pc.full) {
+    const int64_t idx = ur * d.cols + uc;
+    pc.m = *(const g_f32x4 *)(d.mom + idx);
+    pc.g = load_grad4(d.grad, d.grad_dt, idx);
+  }
+  return pc;
+}
+
+__device__ __forceinline__ void momentum4(const MatDev &d, const MomPiece &pc, float mu, bool nesterov,
+                                          float (&u)[4]) {
   u[0] = u[1] = u[2] = u[3] = 0.f;
-  if (ur >= d.rows || uc >= d.cols) return;
-  const int64_t idx = ur * d.cols + uc;
-  if (vec && uc + 4 <= d.cols) {
-    float4 mv = *reinterpret_cast<const float4 *>(d.mom + idx);
-    const f32x4 g = load_grad4(d.grad, d.grad_dt, idx);
+  if (pc.ur >= d.rows || pc.uc >= d.cols) return;
+  const int64_t idx = pc.ur * d.cols + pc.uc;
+  if (pc.full) {
+    f32x4 mv = pc.m;
+    const f32x4 g = pc.g;
     mv.x = fmaf(mu, mv.x, g[0]);
     mv.y = fmaf(mu, mv.y, g[1]);
     mv.z = fmaf(mu, mv.z, g[2]);
     mv.w = fmaf(mu, mv.w, g[3]);
-    *reinterpret_cast<float4 *>(d.mom + idx) = mv;
+    *(g_f32x4 *)(d.mom + idx) = mv;
     u[0] = mv.x; u[1] = mv.y; u[2] = mv.z; u[3] = mv.w;
     if (nesterov)
 #pragma unroll
       for (int k = 0; k < 4; ++k) u[k] = fmaf(mu, u[k], g[k]);
   } else {
-    for (int k = 0; k < 4 && uc + k < d.cols; ++k) {
+    g_f32 *const mom = (g_f32 *)d.mom;
+    for (int k = 0; k < 4 && pc.uc + k < d.cols; ++k) {
       const float g = load_elem(d.grad, d.grad_dt, idx + k);
-      const float m = fmaf(mu, d.mom[idx + k], g);
-      d.mom[idx + k] = m;
+      const float m = fmaf(mu, mom[idx + k], g);
+      mom[idx + k] = m;
       u[k] = nesterov ? fmaf(mu, m, g) : m;
     }
   }
@@ -185,11 +212,17 @@ __global__ __launch_bounds__(kOrientThreads) void momentum_orient_kernel(
     // 8192 contiguous elements of X^T per group: two runs of 4096, four
     // elements per thread in each (a run lies within one row: m_p is a
     // multiple of 256)
+    MomPiece pc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t e0 = t * (2 * TT * TT) + h * (TT * TT) + 4 * tid;
+      pc[h] = mom_load(d, e0 / d.mp, e0 % d.mp, vec);
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int64_t e0 = t * (2 * TT * TT) + h * (TT * TT) + 4 * tid;
       float u[4];
-      momentum4(d, e0 / d.mp, e0 % d.mp, mu, s.nesterov, vec, u);
+      momentum4(d, pc[h], mu, s.nesterov, u);
 #pragma unroll
       for (int k = 0; k < 4; ++k) acc += (double)u[k] * u[k];
       store_xt4(d, e0, u);  // X^T[ur][uc .. uc+3], zeros in the padding
@@ -200,10 +233,13 @@ __global__ __launch_bounds__(kOrientThreads) void momentum_orient_kernel(
     const int64_t blocks_n = d.np / (2 * TT);
     const int64_t i0 = (t / blocks_n) * TT, j0 = (t % blocks_n) * (2 * TT);
     const int p = tid >> 4, q = (tid & 15) * 4;
+    MomPiece pc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) pc[h] = mom_load(d, i0 + p, j0 + h * TT + q, vec);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       float u[4];
-      momentum4(d, i0 + p, j0 + h * TT + q, mu, s.nesterov, vec, u);
+      momentum4(d, pc[h], mu, s.nesterov, u);
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         tile[p][h * TT + q + k] = u[k];
@@ -222,7 +258,7 @@ __global__ __launch_bounds__(kOrientThreads) void momentum_orient_kernel(
     }
   }
   const double tot = block_sum_f64(acc, red);
-  if (tid == 0) d.partials[t] = tot;
+  if (tid == 0) ((__attribute__((address_space(1))) double *)d.partials)[t] = tot;
 }
 
 // ns_steps = 0: O = U * inv_norm (already r x c), P -= lr*scale*O.

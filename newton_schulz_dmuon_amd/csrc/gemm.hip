@@ -247,6 +247,8 @@ __device__ __forceinline__ void stage_tile_put_t(lds_char *lds, int r, int c0, c
 
 // Writes the staged tile to dst (row-major, leading dimension ld elements)
 // with 16-byte stores: thread t moves chunks t, t + 512, ... (row = f / 32).
+// All 16 LDS reads are issued before the first store, so their latencies
+// overlap instead of adding up (64 VGPRs, free at this point).
 // Starts with a barrier (the puts are visible); a later put into the same
 // LDS needs lds_barrier() first (every wave's flush reads done).
 template <int SW>
@@ -255,12 +257,19 @@ __device__ __forceinline__ void stage_tile_flush(lds_char *lds, uint16_t *dst, i
   // opaque: each flush rebuilds its addresses instead of keeping them live
   // across the epilogue's other flushes
   asm volatile("" : "+v"(tid));
+  u32x4 v[16];
 #pragma unroll
   for (int q = 0; q < 16; ++q) {
     const int f = q * 512 + tid;
     const int row = f >> 5, chunk = f & 31;
-    const u32x4 v = *(const lds_u32x4 *)(lds + row * 512 + tile_swz<SW>(row, chunk) * 16);
-    *reinterpret_cast<u32x4 *>(dst + row * ld + chunk * 8) = v;
+    v[q] = *(const lds_u32x4 *)(lds + row * 512 + tile_swz<SW>(row, chunk) * 16);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    const int f = q * 512 + tid;
+    const int row = f >> 5, chunk = f & 31;
+    *(g_u32x4 *)(dst + row * ld + chunk * 8) = v[q];
   }
 }
 
@@ -563,6 +572,13 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
     }
   };
 
+  // In a diagonal tile of a symmetric output, rows 128-255 x columns 0-127
+  // lie below the diagonal: the epilogue stores the upper triangle and its
+  // mirror and never these values, so the two waves holding them (wm = 1,
+  // wn < 2) skip their products and only keep the barrier schedule.
+  constexpr bool kSymOut = MODE == kModeGram || MODE == kModeSquare;
+  const bool lower_quadrant = kSymOut && ti == tj && wm == 1 && wn < 2;
+
   Frag fa, fb;
   // Waves 0-3 (the tile's rows 0-127) and waves 4-7 (rows 128-255) run the
   // same step: a read phase (next stage's loads issued, both sub-steps'
@@ -593,8 +609,10 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
       __builtin_amdgcn_sched_barrier(0);
       lds_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      mfma_frag(fa);
-      mfma_frag(fb);
+      if (!lower_quadrant) {
+        mfma_frag(fa);
+        mfma_frag(fb);
+      }
       __builtin_amdgcn_sched_barrier(0);
       dma_barrier();
       __builtin_amdgcn_sched_barrier(0);
@@ -645,7 +663,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
 
   // The first iteration's X is U unnormalised (X0 = U * inv_norm): A0 picks
   // up inv_norm^2 and the first X' (or O) inv_norm.
-  const float inv = d.first_it ? *d.inv_norm : 1.f;
+  const float inv = d.first_it ? *(const g_f32 *)d.inv_norm : 1.f;
   const float gram_scale = inv * inv;
   if (MODE == kModeGram || MODE == kModeSquare) {
     T *out = static_cast<T *>(MODE == kModeGram ? d.a : d.b);
@@ -797,42 +815,47 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
       PT *const P = static_cast<PT *>(d.param);
       PT *const Orth = static_cast<PT *>(d.orth);
       PT *const Packed = static_cast<PT *>(d.packed);  // nullable copy of the updated P
-      // bf16 P: all 16 pieces of a half are read before the half is staged,
-      // so their latency hides behind the X^T reads and the LDS puts; fp32 P
-      // reads its pieces in batches of 4 after staging (register budget)
+      // bf16 P: the 16 pieces of both halves are read before the first half
+      // is staged, so their latency hides behind the staging and the first
+      // half's update; fp32 P reads its pieces in batches of 4 after staging
+      // (register budget)
       constexpr bool kPre = sizeof(PT) == 2;
       constexpr int kBatch = kPre ? 16 : 4;
+      // Piece q of this thread in half h: staged block (r, c), P element
+      // (pr, pc), n valid.
+      struct Piece {
+        int r, c, n;
+        int64_t idx;
+      };
+      auto piece_of = [&](int h, int q) {
+        Piece pc_;
+        int64_t pr, pcol;
+        if (tp) {
+          pc_.r = q * 16 + (tid >> 5), pc_.c = (tid & 31) * 4;
+          pr = static_cast<int64_t>(tj) * kTile + pc_.r;
+          pcol = static_cast<int64_t>(ti) * kTile + h * kWaveM + pc_.c;
+        } else {
+          pc_.r = q * 8 + (tid >> 6), pc_.c = (tid & 63) * 4;
+          pr = static_cast<int64_t>(ti) * kTile + h * kWaveM + pc_.r;
+          pcol = static_cast<int64_t>(tj) * kTile + pc_.c;
+        }
+        pc_.n = (pr < d.rows && pcol < d.cols) ? static_cast<int>(min<int64_t>(4, d.cols - pcol)) : 0;
+        pc_.idx = pr * d.cols + pcol;
+        return pc_;
+      };
+      typename Vec4<PT>::Raw pre[kPre ? kWavesM : 1][kPre ? 16 : 1];
+      if constexpr (kPre) {
 #pragma unroll
-      for (int h = 0; h < kWavesM; ++h) {
-        // Piece q of this thread: staged block (r, c), P element (pr, pc), n valid.
-        struct Piece {
-          int r, c, n;
-          int64_t idx;
-        };
-        auto piece = [&](int q) {
-          Piece pc_;
-          int64_t pr, pcol;
-          if (tp) {
-            pc_.r = q * 16 + (tid >> 5), pc_.c = (tid & 31) * 4;
-            pr = static_cast<int64_t>(tj) * kTile + pc_.r;
-            pcol = static_cast<int64_t>(ti) * kTile + h * kWaveM + pc_.c;
-          } else {
-            pc_.r = q * 8 + (tid >> 6), pc_.c = (tid & 63) * 4;
-            pr = static_cast<int64_t>(ti) * kTile + h * kWaveM + pc_.r;
-            pcol = static_cast<int64_t>(tj) * kTile + pc_.c;
-          }
-          pc_.n = (pr < d.rows && pcol < d.cols) ? static_cast<int>(min<int64_t>(4, d.cols - pcol)) : 0;
-          pc_.idx = pr * d.cols + pcol;
-          return pc_;
-        };
-        typename Vec4<PT>::Raw pre[kPre ? 16 : 1];
-        if constexpr (kPre) {
+        for (int h = 0; h < kWavesM; ++h)
 #pragma unroll
           for (int q = 0; q < 16; ++q) {
-            const Piece pp = piece(q);
-            if (vec_ok && pp.n == 4) pre[q] = Vec4<PT>::raw(P + pp.idx);
+            const Piece pp = piece_of(h, q);
+            if (vec_ok && pp.n == 4) pre[h][q] = Vec4<PT>::raw(P + pp.idx);
           }
-        }
+      }
+#pragma unroll
+      for (int h = 0; h < kWavesM; ++h) {
+        auto piece = [&](int q) { return piece_of(h, q); };
         if (h > 0) lds_barrier();  // the previous half has been read
         if (wm == h) {
 #pragma unroll
@@ -860,7 +883,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
           for (int qq = 0; qq < kBatch; ++qq) {
             const Piece pp = piece(q0 + qq);
             if constexpr (kPre)
-              praw[qq] = pre[q0 + qq];
+              praw[qq] = pre[h][q0 + qq];
             else if (vec_ok && pp.n == 4)
               praw[qq] = Vec4<PT>::raw(P + pp.idx);
           }
