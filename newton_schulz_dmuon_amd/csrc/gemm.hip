@@ -182,6 +182,49 @@ template <> struct Vec4<float> {
   }
 };
 
+// Eight consecutive elements of a caller's buffer: one 16-byte access for
+// bf16, two for fp32; the address is 16-byte aligned.
+template <typename T> struct Vec8;
+template <> struct Vec8<uint16_t> {
+  typedef u32x4 Raw;
+  static __device__ __forceinline__ Raw raw(const uint16_t *p) { return *(const g_u32x4 *)p; }
+  static __device__ __forceinline__ void cvt(const Raw &v, float (&o)[8]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      o[2 * k] = __uint_as_float(v[k] << 16);
+      o[2 * k + 1] = __uint_as_float(v[k] & 0xffff0000u);
+    }
+  }
+  static __device__ __forceinline__ void st(uint16_t *p, const float (&v)[8]) {
+    u32x4 u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      u[k] = static_cast<uint32_t>(f32_to_bf16_bits(v[2 * k])) |
+             (static_cast<uint32_t>(f32_to_bf16_bits(v[2 * k + 1])) << 16);
+    *(g_u32x4 *)p = u;
+  }
+};
+template <> struct Vec8<float> {
+  struct Raw {
+    u32x4 a, b;
+  };
+  static __device__ __forceinline__ Raw raw(const float *p) {
+    return Raw{*(const g_u32x4 *)p, *(const g_u32x4 *)(p + 4)};
+  }
+  static __device__ __forceinline__ void cvt(const Raw &v, float (&o)[8]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      o[k] = __uint_as_float(v.a[k]);
+      o[4 + k] = __uint_as_float(v.b[k]);
+    }
+  }
+  static __device__ __forceinline__ void st(float *p, const float (&v)[8]) {
+    *(g_u32x4 *)p = u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])};
+    *(g_u32x4 *)(p + 4) =
+        u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])};
+  }
+};
+
 // Row-major 256 x 256 bf16 tile in LDS (512-byte rows, 32 chunks of 16 B),
 // two chunk swizzles, one per way the tile is filled:
 //  kSwzRows: stage_tile_put writes four rows of one column (2-byte stores);
@@ -796,13 +839,18 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
     // O = (aX + BX) * inv for the tile (rows over m, columns over n) goes
     // through LDS as fp32, one half of the rows at a time (the waves with
     // wm == h hold half h): row-major when P = O (m x n), transposed when
-    // P = O^T (n x m).  Then all threads update P in four-element pieces
-    // along its rows: P -= lr*scale*O, and orth_out = O.  The aX term is
-    // already in the accumulators: it was captured from the X^T tile in LDS
-    // during the mainloop, as in Apply.
+    // P = O^T (n x m).  Then all threads update P in eight-element pieces
+    // along its rows (16-byte accesses: the epilogue is bound by the number
+    // of memory instructions, not by bytes): P -= lr*scale*O, and
+    // orth_out = O.  The aX term is already in the accumulators: it was
+    // captured from the X^T tile in LDS during the mainloop, as in Apply.
     const float step = s.lr * d.scale;
     const bool tp = d.transposed != 0;
-    const bool vec_ok = (d.cols & 3) == 0;  // rows of P start 4-element aligned
+    // rows of P start 8-element aligned and every buffer is 16-byte aligned
+    const bool vec_ok =
+        (d.cols & 7) == 0 &&
+        ((reinterpret_cast<uintptr_t>(d.param) | reinterpret_cast<uintptr_t>(d.packed) |
+          reinterpret_cast<uintptr_t>(d.orth)) & 15) == 0;
     typedef __attribute__((address_space(3))) float lds_f32;
     typedef __attribute__((address_space(3))) u32x4 lds_v4;
     // [128][256] fp32, 1 KB rows: chunk XOR 4 * ((row / 4) mod 4), so the four
@@ -810,17 +858,22 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
     auto o_at = [&](int r, int c) { return r * 1024 + (((c >> 2) ^ (((r >> 2) & 3) << 2)) * 16) + (c & 3) * 4; };
     // [256][128] fp32, 512-byte rows: chunk XOR 4 * (row mod 4)
     auto ot_at = [&](int r, int c) { return r * 512 + (((c >> 2) ^ ((r & 3) << 2)) * 16); };
+    // A piece's two 16-byte halves are read in the order (sw, 1 - sw): the 16
+    // lanes of one LDS read pass hold 16 consecutive pieces of one row, and
+    // with sw = bit 3 of the lane they touch 16 distinct bank groups.
+    const int sw = (lane >> 3) & 1;
     auto update = [&](auto ptag) {
       using PT = decltype(ptag);
       PT *const P = static_cast<PT *>(d.param);
       PT *const Orth = static_cast<PT *>(d.orth);
       PT *const Packed = static_cast<PT *>(d.packed);  // nullable copy of the updated P
-      // bf16 P: the 16 pieces of both halves are read before the first half
+      // bf16 P: the 8 pieces of both halves are read before the first half
       // is staged, so their latency hides behind the staging and the first
-      // half's update; fp32 P reads its pieces in batches of 4 after staging
+      // half's update; fp32 P reads its pieces in batches of 2 after staging
       // (register budget)
       constexpr bool kPre = sizeof(PT) == 2;
-      constexpr int kBatch = kPre ? 16 : 4;
+      constexpr int kPieces = 8;
+      constexpr int kBatch = kPre ? kPieces : 2;
       // Piece q of this thread in half h: staged block (r, c), P element
       // (pr, pc), n valid.
       struct Piece {
@@ -831,26 +884,26 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
         Piece pc_;
         int64_t pr, pcol;
         if (tp) {
-          pc_.r = q * 16 + (tid >> 5), pc_.c = (tid & 31) * 4;
+          pc_.r = q * 32 + (tid >> 4), pc_.c = (tid & 15) * 8;
           pr = static_cast<int64_t>(tj) * kTile + pc_.r;
           pcol = static_cast<int64_t>(ti) * kTile + h * kWaveM + pc_.c;
         } else {
-          pc_.r = q * 8 + (tid >> 6), pc_.c = (tid & 63) * 4;
+          pc_.r = q * 16 + (tid >> 5), pc_.c = (tid & 31) * 8;
           pr = static_cast<int64_t>(ti) * kTile + h * kWaveM + pc_.r;
           pcol = static_cast<int64_t>(tj) * kTile + pc_.c;
         }
-        pc_.n = (pr < d.rows && pcol < d.cols) ? static_cast<int>(min<int64_t>(4, d.cols - pcol)) : 0;
+        pc_.n = (pr < d.rows && pcol < d.cols) ? static_cast<int>(min<int64_t>(8, d.cols - pcol)) : 0;
         pc_.idx = pr * d.cols + pcol;
         return pc_;
       };
-      typename Vec4<PT>::Raw pre[kPre ? kWavesM : 1][kPre ? 16 : 1];
+      typename Vec8<PT>::Raw pre[kPre ? kWavesM : 1][kPre ? kPieces : 1];
       if constexpr (kPre) {
 #pragma unroll
         for (int h = 0; h < kWavesM; ++h)
 #pragma unroll
-          for (int q = 0; q < 16; ++q) {
+          for (int q = 0; q < kPieces; ++q) {
             const Piece pp = piece_of(h, q);
-            if (vec_ok && pp.n == 4) pre[h][q] = Vec4<PT>::raw(P + pp.idx);
+            if (vec_ok && pp.n == 8) pre[h][q] = Vec8<PT>::raw(P + pp.idx);
           }
       }
 #pragma unroll
@@ -877,30 +930,37 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
         }
         lds_barrier();
 #pragma unroll
-        for (int q0 = 0; q0 < 16; q0 += kBatch) {
-          typename Vec4<PT>::Raw praw[kBatch];
+        for (int q0 = 0; q0 < kPieces; q0 += kBatch) {
+          typename Vec8<PT>::Raw praw[kBatch];
 #pragma unroll
           for (int qq = 0; qq < kBatch; ++qq) {
             const Piece pp = piece(q0 + qq);
             if constexpr (kPre)
               praw[qq] = pre[h][q0 + qq];
-            else if (vec_ok && pp.n == 4)
-              praw[qq] = Vec4<PT>::raw(P + pp.idx);
+            else if (vec_ok && pp.n == 8)
+              praw[qq] = Vec8<PT>::raw(P + pp.idx);
           }
 #pragma unroll
           for (int qq = 0; qq < kBatch; ++qq) {
             const Piece pp = piece(q0 + qq);
             if (pp.n == 0) continue;
-            const u32x4 u = *(const lds_v4 *)(lds + (tp ? ot_at(pp.r, pp.c) : o_at(pp.r, pp.c)));
-            const f32x4 o = Vec4<float>::cvt(u);
-            if (vec_ok && pp.n == 4) {
-              const f32x4 pv = Vec4<PT>::cvt(praw[qq]);
-              f32x4 nv;
+            auto at = [&](int c) { return tp ? ot_at(pp.r, c) : o_at(pp.r, c); };
+            const u32x4 u0 = *(const lds_v4 *)(lds + at(pp.c + 4 * sw));
+            const u32x4 u1 = *(const lds_v4 *)(lds + at(pp.c + 4 - 4 * sw));
+            float o[8];
 #pragma unroll
-              for (int v = 0; v < 4; ++v) nv[v] = fmaf(-step, o[v], pv[v]);
-              Vec4<PT>::st(P + pp.idx, nv);
-              if (Packed) Vec4<PT>::st(Packed + pp.idx, nv);
-              if (Orth) Vec4<PT>::st(Orth + pp.idx, o);
+            for (int v = 0; v < 4; ++v) {
+              o[v] = __uint_as_float(sw ? u1[v] : u0[v]);
+              o[4 + v] = __uint_as_float(sw ? u0[v] : u1[v]);
+            }
+            if (vec_ok && pp.n == 8) {
+              float pv[8], nv[8];
+              Vec8<PT>::cvt(praw[qq], pv);
+#pragma unroll
+              for (int v = 0; v < 8; ++v) nv[v] = fmaf(-step, o[v], pv[v]);
+              Vec8<PT>::st(P + pp.idx, nv);
+              if (Packed) Vec8<PT>::st(Packed + pp.idx, nv);
+              if (Orth) Vec8<PT>::st(Orth + pp.idx, o);
             } else {
               for (int v = 0; v < pp.n; ++v) {
                 if (d.orth) store_elem(d.orth, d.param_dt, pp.idx + v, o[v]);
