@@ -339,7 +339,7 @@ def main(argv=None) -> int:
             flops[kk] += v
     ns_total = sum(flops.values())
     executed = sum(f for _, f in launches)
-    gemm_kinds = ("gram", "square", "apply", "final")
+    gemm_kinds = ("gram", "square", "gram_square", "apply", "final")
     ns_ms = sum(sum(v) for nm, v in per.items() if nm in gemm_kinds) / args.steps
     peak = PEAK_FP32_TFLOPS if args.fp32_ns else PEAK_BF16_TFLOPS
     value = ns_total / (ms * 1e-3) / 1e12
@@ -378,6 +378,7 @@ def main(argv=None) -> int:
         ach = kind_flops[dom] / (sum(per[dom]) / args.steps * 1e-3) / 1e12
         kernel = {"gram": "ns_gemm_kernel<Gram> (A = X X^T)",
                   "square": "ns_gemm_kernel<Square> (symmetric m x m products)",
+                  "gram_square": "ns_gemm_kernel<GramSquare> (Gram and Square tiles of different matrices)",
                   "apply": "ns_gemm_kernel<Apply> (X <- aX + BX / X <- QX)",
                   "final": "ns_gemm_kernel<Final> (last apply + update)"}[dom]
         roofline = {"bound": "mfma", "kernel": kernel,

@@ -110,7 +110,9 @@ enum {
   DMUON_LAUNCH_GRAM = 4,            /* A = X X^T                                */
   DMUON_LAUNCH_SQUARE = 5,          /* symmetric m x m product (+ bA + diag)    */
   DMUON_LAUNCH_APPLY = 6,           /* X <- aX + BX (Gram-space: X <- Q X)      */
-  DMUON_LAUNCH_FINAL = 7            /* last apply + parameter update            */
+  DMUON_LAUNCH_FINAL = 7,           /* last apply + parameter update            */
+  DMUON_LAUNCH_GRAM_SQUARE = 8      /* Gram tiles of some matrices and Square
+                                       tiles of others, in one launch          */
 };
 
 /* One launch of a step, as dmuon_step_launches describes it. */
@@ -310,9 +312,11 @@ int dmuon_muon_step_packed(const dmuon_matrix *mats, int32_t n,
  * the Newton-Schulz launches.  The direct chain runs Gram, Square, Apply
  * per iteration (the last Apply carries the parameter update); with
  * DMUON_FLAG_GRAM_NS the Gram-space chain's launches are merged into that
- * sequence, each chain keeping its order and a launch of each chain of the
- * same kind becoming one grouped launch (along a longest common subsequence
- * of the two kind sequences); dmuon_step_launches lists the result.
+ * sequence, each chain keeping its order: a launch of each chain becomes one
+ * grouped launch where both have the same kind, or where one is a Gram and
+ * the other a Square launch (kind DMUON_LAUNCH_GRAM_SQUARE), the pairs
+ * chosen to maximise 2 per same-kind pair plus 1 per mixed pair over the
+ * two kind sequences; dmuon_step_launches lists the result.
  * Only the first
  * n_events are recorded; n_events = 0 makes this dmuon_muon_step.
  * Errors: those of dmuon_muon_step; INVALID_ARG for n_events < 0 or a NULL

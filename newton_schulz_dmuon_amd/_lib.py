@@ -32,7 +32,7 @@ FLAG_CHECK_FINITE = 1 << 3
 
 # dmuon_launch_info.kind
 LAUNCH_KINDS = ("momentum_sumsq", "momentum_orient", "norm", "update_direct", "gram", "square",
-                "apply", "final")
+                "apply", "final", "gram_square")
 
 EXPORTED = ("dmuon_abi_version", "dmuon_error_string", "dmuon_last_error",
             "dmuon_partition_lpt", "dmuon_pack_offsets", "dmuon_workspace_bytes",

@@ -323,21 +323,11 @@ __device__ __forceinline__ void stage_tile_flush(lds_char *lds, uint16_t *dst, i
 // epilogue).
 constexpr int kRoleWhole = 0, kRolePiece = 1, kRoleReduce = 2;
 
+// One tile (or piece of a tile) of stage MODE: the work-group's whole work.
+// lds: the work-group's 128 KB, [2 stages][L, R][256 rows][128 B].
 template <typename T, int MODE, int ROLE>
-__global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restrict__ mats,
-                                                           const TileEntry *__restrict__ tiles,
-                                                           StageXcd xcd, StepScalars s,
-                                                           f32x4 *__restrict__ splitk) {
-  __shared__ __attribute__((aligned(1024))) char smem[4 * kOperandBytes];  // 128 KB
-  // C cast: generic -> LDS address space.  [2 stages][L, R][256 rows][128 B]
-  lds_char *const lds = (lds_char *)smem;
-
-  // this work-group's tile: entry w / 8 of XCD (w % 8)'s list
-  const int32_t w = static_cast<int32_t>(blockIdx.x);
-  const int32_t xi = w % kXcds, k = w / kXcds;
-  if (k >= xcd.count[xi]) return;  // whole group leaves before any barrier
-  const TileEntry e = tiles[xcd.first[xi] + k];
-  const MatDev &d = mats[e.mat];
+__device__ __forceinline__ void gemm_tile(lds_char *const lds, const MatDev &d, const TileEntry &e,
+                                          const StepScalars &s, f32x4 *__restrict__ splitk) {
   const int32_t ti = e.ti, tj = e.tj;
 
   // Gram reads X^T (n_p x m_p): its operand tiles are MN-major, K = n runs
@@ -977,6 +967,32 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   }
 }
 
+// The grouped launch of one stage: work-group w runs entry w / 8 of XCD
+// (w % 8)'s tile list.  A launch of Gram and Square tiles of different
+// matrices (kModeGramSquare) runs each tile with its matrix's stage.
+template <typename T, int MODE, int ROLE>
+__global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restrict__ mats,
+                                                           const TileEntry *__restrict__ tiles,
+                                                           StageXcd xcd, StepScalars s,
+                                                           f32x4 *__restrict__ splitk) {
+  __shared__ __attribute__((aligned(1024))) char smem[4 * kOperandBytes];  // 128 KB
+  // C cast: generic -> LDS address space
+  lds_char *const lds = (lds_char *)smem;
+  const int32_t w = static_cast<int32_t>(blockIdx.x);
+  const int32_t xi = w % kXcds, k = w / kXcds;
+  if (k >= xcd.count[xi]) return;  // whole group leaves before any barrier
+  const TileEntry e = tiles[xcd.first[xi] + k];
+  const MatDev &d = mats[e.mat];
+  if constexpr (MODE == kModeGramSquare) {
+    if (d.gemm_kind == kModeGram)
+      gemm_tile<T, kModeGram, ROLE>(lds, d, e, s, splitk);
+    else
+      gemm_tile<T, kModeSquare, ROLE>(lds, d, e, s, splitk);
+  } else {
+    gemm_tile<T, MODE, ROLE>(lds, d, e, s, splitk);
+  }
+}
+
 template <typename T, int ROLE>
 hipError_t launch_role(GemmMode mode, const MatDev *mats, const TileEntry *tiles, const StageXcd &xcd,
                        StepScalars s, f32x4 *splitk, hipStream_t st) {
@@ -993,6 +1009,10 @@ hipError_t launch_role(GemmMode mode, const MatDev *mats, const TileEntry *tiles
       break;
     case kModeApply:
       hipLaunchKernelGGL((ns_gemm_kernel<T, kModeApply, ROLE>), grid, block, 0, st, mats, tiles, xcd, s, splitk);
+      break;
+    case kModeGramSquare:
+      hipLaunchKernelGGL((ns_gemm_kernel<T, kModeGramSquare, ROLE>), grid, block, 0, st, mats, tiles, xcd, s,
+                         splitk);
       break;
     default:
       hipLaunchKernelGGL((ns_gemm_kernel<T, kModeFinal, ROLE>), grid, block, 0, st, mats, tiles, xcd, s, splitk);

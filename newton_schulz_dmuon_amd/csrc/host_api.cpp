@@ -132,7 +132,8 @@ enum LaunchKind : int32_t {
   kLkGram = DMUON_LAUNCH_GRAM,
   kLkSquare = DMUON_LAUNCH_SQUARE,
   kLkApply = DMUON_LAUNCH_APPLY,
-  kLkFinal = DMUON_LAUNCH_FINAL
+  kLkFinal = DMUON_LAUNCH_FINAL,
+  kLkGramSquare = DMUON_LAUNCH_GRAM_SQUARE  // parts of kinds Gram and Square
 };
 
 // Workspace buffers a GEMM launch can name per matrix: the direct chain uses
@@ -155,22 +156,26 @@ struct Part {
   int32_t group, a, b, r, cur, first;
   float ca, cb, cc, cdiag;
   int32_t l_lo = kBufNone, r_lo = kBufNone, o_lo = kBufNone;
+  int32_t kind = 0;  // the stage this part runs (kLkGram ... kLkFinal)
   auto key() const {
-    return std::make_tuple(group, a, b, r, cur, first, ca, cb, cc, cdiag, l_lo, r_lo, o_lo);
+    return std::make_tuple(group, a, b, r, cur, first, ca, cb, cc, cdiag, l_lo, r_lo, o_lo, kind);
   }
   bool operator<(const Part &o) const { return key() < o.key(); }
   // passes of the K loop (each a full product): 1 + one per low half read;
   // a Square without its own R reads L twice
-  int32_t passes(int32_t kind) const {
+  int32_t passes() const {
     const bool r_split = r_lo != kBufNone || (kind == DMUON_LAUNCH_SQUARE && r == kBufNone && l_lo != kBufNone);
     return 1 + (l_lo != kBufNone) + (kind == DMUON_LAUNCH_SQUARE && r_split);
   }
+  // tile-list stage: 0 Gram, 1 Square, 2 Apply / Final
+  int32_t stage() const { return kind == kLkGram ? 0 : kind == kLkSquare ? 1 : 2; }
 };
 
 struct Launch {
   int32_t kind;
   bool fp32 = false;        // fp32 operands (kernel instance); parts share it
-  std::vector<Part> parts;  // GEMM launches; all of one kind
+  std::vector<Part> parts;  // GEMM launches: all of this kind, or (kLkGramSquare)
+                            // of kinds Gram and Square
   int32_t table = 0;        // MatDev table: the parts' matrices, in order
   int32_t list = 0;         // tile list over that table
   int32_t role = 0;         // 0 whole tiles, 1 pieces of split tiles, 2 their reduce
@@ -199,25 +204,27 @@ struct Plan {
   int64_t total_bytes = 0;
 };
 
-// Tile lists of one grouped GEMM stage (0 Gram, 1 Square, 2 Apply), one per
-// XCD.  Tiles are grouped into blocks that share operand panels: 4 x 4 tile
+// Tile lists of one grouped GEMM launch, one per XCD; every matrix has its
+// stage (0 Gram, 1 Square, 2 Apply; a launch can hold Gram and Square
+// matrices).  Tiles are grouped into blocks that share operand panels: 4 x 4 tile
 // blocks of the upper triangle for the symmetric products (they read panels
 // ti and tj of one matrix), 4 x 8 blocks for Apply (B panel ti, X^T panel
 // tj).  Blocks go, costliest first (tiles x K depth, ties in matrix order),
 // to the XCD with the least work so far; each XCD's list keeps that order, so
 // its 32 CUs work through long-K tiles first and the tiles running together
 // on one XCD read few distinct panels through its L2.
-void build_stage_tiles(const std::vector<MatDev> &mats, const std::vector<int32_t> &passes, int st,
-                       std::vector<TileEntry> &out, StageXcd &xcd) {
+void build_stage_tiles(const std::vector<MatDev> &mats, const std::vector<int32_t> &passes,
+                       const std::vector<int32_t> &stages, std::vector<TileEntry> &out, StageXcd &xcd) {
   struct Block {
     int64_t cost;
     int32_t mat, ti0, tj0;
   };
-  const bool sym = st < 2;
-  const int bm = 4, bn = sym ? 4 : 8;
   std::vector<Block> blocks;
   for (int32_t i = 0; i < static_cast<int32_t>(mats.size()); ++i) {
     const MatDev &d = mats[i];
+    const int32_t st = stages[i];
+    const bool sym = st < 2;
+    const int bm = 4, bn = sym ? 4 : 8;
     const int64_t depth = (st == 0 ? d.np : d.mp) * passes[i];
     const int32_t rows = d.tm, cols = sym ? d.tm : d.tn;
     for (int32_t bi = 0; bi < rows; bi += bm)
@@ -238,6 +245,8 @@ void build_stage_tiles(const std::vector<MatDev> &mats, const std::vector<int32_
       if (load[y] < load[x]) x = y;
     load[x] += b.cost;
     const MatDev &d = mats[b.mat];
+    const bool sym = stages[b.mat] < 2;
+    const int bm = 4, bn = sym ? 4 : 8;
     const int32_t rows = d.tm, cols = sym ? d.tm : d.tn;
     for (int32_t ti = b.ti0; ti < std::min(b.ti0 + bm, rows); ++ti)
       for (int32_t tj = b.tj0; tj < std::min(b.tj0 + bn, cols); ++tj)
@@ -259,13 +268,13 @@ std::mutex g_tiles_mu;
 std::map<std::vector<int64_t>, std::pair<std::vector<TileEntry>, StageXcd>> g_tiles_cache;
 constexpr size_t kTilesCacheMax = 64;
 
-void cached_stage_tiles(const std::vector<MatDev> &mats, const std::vector<int32_t> &passes, int st,
-                        std::vector<TileEntry> &out, StageXcd &xcd) {
+void cached_stage_tiles(const std::vector<MatDev> &mats, const std::vector<int32_t> &passes,
+                        const std::vector<int32_t> &stages, std::vector<TileEntry> &out, StageXcd &xcd) {
   std::vector<int64_t> key;
-  key.reserve(1 + 5 * mats.size());
-  key.push_back(st);
+  key.reserve(6 * mats.size());
   for (size_t i = 0; i < mats.size(); ++i) {
     const MatDev &d = mats[i];
+    key.push_back(stages[i]);
     key.push_back(d.mp);
     key.push_back(d.np);
     key.push_back(d.tm);
@@ -281,7 +290,7 @@ void cached_stage_tiles(const std::vector<MatDev> &mats, const std::vector<int32
       return;
     }
   }
-  build_stage_tiles(mats, passes, st, out, xcd);
+  build_stage_tiles(mats, passes, stages, out, xcd);
   std::lock_guard<std::mutex> lock(g_tiles_mu);
   if (g_tiles_cache.size() >= kTilesCacheMax) g_tiles_cache.clear();
   g_tiles_cache.emplace(std::move(key), std::make_pair(out, xcd));
@@ -426,7 +435,7 @@ std::vector<int64_t> row_steps(const Plan &p, const Launch &l) {
   for (const Part &pt : l.parts)
     for (int32_t i : p.groups[pt.group]) {
       const MatDev &d = p.mats[i];
-      out.push_back(pt.passes(l.kind) * ((l.kind == kLkGram ? d.np : d.mp) / kstep));
+      out.push_back(pt.passes() * ((pt.kind == kLkGram ? d.np : d.mp) / kstep));
     }
   return out;
 }
@@ -503,8 +512,9 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
     Launch l;
     l.kind = kind;
     l.parts = std::move(parts);
+    for (Part &pt : l.parts) pt.kind = kind;
     // executed flops: every pass of the K loop is a full product
-    for (const Part &pt : l.parts) l.flops += flops(pt.group, kind) * pt.passes(kind);
+    for (const Part &pt : l.parts) l.flops += flops(pt.group, kind) * pt.passes();
     chain.push_back(std::move(l));
   };
   std::vector<Launch> chain[3];
@@ -591,26 +601,44 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
     for (Launch &l : chain[1]) l.fp32 = fp32;
   }
   // The two chains touch disjoint matrices: merge them into one sequence
-  // that keeps each chain's order and runs a launch of each chain of the
-  // same kind as one grouped launch (a longest common subsequence of the
-  // kinds), which fills the chip better than either launch alone.
+  // that keeps each chain's order and runs a launch of each chain as one
+  // grouped launch where it can, which fills the chip better than either
+  // launch alone.  Launches of the same kind merge (score 2); a Gram launch
+  // of one chain merges with a Square launch of the other (score 1: one
+  // kernel instance dispatches each tile to its stage's code).  The merge
+  // maximises the total score by dynamic programming over the two chains; a
+  // list-schedule simulation of workload 4 (Llama-3.1-8B share) puts this
+  // weighting at the best merge of any weighting (19 launches instead of 21).
+  auto mixable = [](int32_t x, int32_t y) {
+    return (x == kLkGram && y == kLkSquare) || (x == kLkSquare && y == kLkGram);
+  };
   std::vector<Launch> merged;
   {
     const size_t n0 = chain[0].size(), n1 = chain[1].size();
-    std::vector<std::vector<int32_t>> lcs(n0 + 1, std::vector<int32_t>(n1 + 1, 0));
-    for (size_t i = n0; i-- > 0;)
-      for (size_t j = n1; j-- > 0;)
-        lcs[i][j] = chain[0][i].kind == chain[1][j].kind ? lcs[i + 1][j + 1] + 1
-                                                         : std::max(lcs[i + 1][j], lcs[i][j + 1]);
+    std::vector<std::vector<int32_t>> best(n0 + 1, std::vector<int32_t>(n1 + 1, 0));
+    auto pair_score = [&](size_t i, size_t j) {
+      const int32_t x = chain[0][i].kind, y = chain[1][j].kind;
+      return x == y ? 2 : mixable(x, y) ? 1 : 0;
+    };
+    for (size_t i = n0 + 1; i-- > 0;)
+      for (size_t j = n1 + 1; j-- > 0;) {
+        if (i == n0 && j == n1) continue;
+        int32_t b = 0;
+        if (i < n0) b = std::max(b, best[i + 1][j]);
+        if (j < n1) b = std::max(b, best[i][j + 1]);
+        if (i < n0 && j < n1 && pair_score(i, j) > 0) b = std::max(b, best[i + 1][j + 1] + pair_score(i, j));
+        best[i][j] = b;
+      }
     size_t i = 0, j = 0;
     while (i < n0 || j < n1) {
-      if (i < n0 && j < n1 && chain[0][i].kind == chain[1][j].kind && lcs[i][j] == lcs[i + 1][j + 1] + 1) {
+      if (i < n0 && j < n1 && pair_score(i, j) > 0 && best[i][j] == best[i + 1][j + 1] + pair_score(i, j)) {
         Launch l = chain[0][i];
+        if (l.kind != chain[1][j].kind) l.kind = kLkGramSquare;
         l.parts.insert(l.parts.end(), chain[1][j].parts.begin(), chain[1][j].parts.end());
         l.flops += chain[1][j].flops;
         merged.push_back(std::move(l));
         ++i, ++j;
-      } else if (j >= n1 || (i < n0 && lcs[i + 1][j] >= lcs[i][j + 1])) {
+      } else if (j >= n1 || (i < n0 && best[i + 1][j] >= best[i][j + 1])) {
         merged.push_back(chain[0][i++]);
       } else {
         merged.push_back(chain[1][j++]);
@@ -630,7 +658,7 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
   }
   // tables and tile lists, shared by launches with equal parts / groups
   std::map<std::vector<Part>, int32_t> table_of;
-  std::map<std::pair<int32_t, std::vector<int32_t>>, int32_t> list_of;
+  std::map<std::vector<int32_t>, int32_t> list_of;
   for (Launch &l : merged) {
     auto t = table_of.find(l.parts);
     if (t == table_of.end()) {
@@ -638,25 +666,25 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
       p.tables.push_back(l.parts);
     }
     l.table = t->second;
-    const int32_t st = l.kind == kLkGram ? 0 : l.kind == kLkSquare ? 1 : 2;
-    std::vector<int32_t> gs;  // (group, passes) of every part
+    std::vector<int32_t> key;  // (group, passes, stage) of every part
     for (const Part &pt : l.parts) {
-      gs.push_back(pt.group);
-      gs.push_back(pt.passes(l.kind));
+      key.push_back(pt.group);
+      key.push_back(pt.passes());
+      key.push_back(pt.stage());
     }
-    auto key = std::make_pair(st, gs);
     auto li = list_of.find(key);
     if (li == list_of.end()) {
       std::vector<MatDev> shapes;
-      std::vector<int32_t> passes;
-      for (size_t q = 0; q < gs.size(); q += 2)
-        for (int32_t i : p.groups[gs[q]]) {
+      std::vector<int32_t> passes, stages;
+      for (size_t q = 0; q < key.size(); q += 3)
+        for (int32_t i : p.groups[key[q]]) {
           shapes.push_back(p.mats[i]);
-          passes.push_back(gs[q + 1]);
+          passes.push_back(key[q + 1]);
+          stages.push_back(key[q + 2]);
         }
       p.lists.emplace_back();
       p.list_xcd.emplace_back();
-      cached_stage_tiles(shapes, passes, st, p.lists.back(), p.list_xcd.back());
+      cached_stage_tiles(shapes, passes, stages, p.lists.back(), p.list_xcd.back());
       li = list_of.emplace(key, static_cast<int32_t>(p.lists.size()) - 1).first;
     }
     l.list = li->second;
@@ -785,29 +813,34 @@ bool plan_consistent(const Plan &p) {
     if (l.table < 1 || l.table > static_cast<int32_t>(p.tables.size())) return false;
     if (l.list < 0 || l.list >= static_cast<int32_t>(p.lists.size())) return false;
     std::vector<const MatDev *> rows;
+    std::vector<bool> row_sym;
     for (const Part &pt : p.tables[l.table - 1]) {
       if (pt.group < 0 || pt.group > 2) return false;
+      // a part runs its launch's stage; a mixed launch holds Gram and
+      // Square parts only
+      if (l.kind == kLkGramSquare ? pt.kind != kLkGram && pt.kind != kLkSquare : pt.kind != l.kind) return false;
       // a capturing Square (b A from its R tile) must not read a pair: the
       // capture is taken in the first pass only
-      if (l.kind == kLkSquare && pt.cb != 0.f && (pt.l_lo != kBufNone || pt.r_lo != kBufNone)) return false;
-      if (l.kind != kLkSquare && (pt.r_lo != kBufNone || pt.o_lo != kBufNone)) return false;
-      if (l.kind == kLkGram && pt.l_lo != kBufNone) return false;
+      if (pt.kind == kLkSquare && pt.cb != 0.f && (pt.l_lo != kBufNone || pt.r_lo != kBufNone)) return false;
+      if (pt.kind != kLkSquare && (pt.r_lo != kBufNone || pt.o_lo != kBufNone)) return false;
+      if (pt.kind == kLkGram && pt.l_lo != kBufNone) return false;
       for (int32_t i : p.groups[pt.group]) {
         rows.push_back(&p.mats[i]);
+        row_sym.push_back(pt.kind == kLkGram || pt.kind == kLkSquare);
         for (int32_t b : {pt.a, pt.b, pt.r, pt.l_lo, pt.r_lo, pt.o_lo})
           if (b != kBufNone && !(p.have[i] >> b & 1u)) return false;
         // the second X^T buffer is read (cur = 1) or written (Apply); the
         // sizing pass has no addresses yet
-        const bool needs_xt1 = pt.cur || l.kind == kLkApply;
+        const bool needs_xt1 = pt.cur || pt.kind == kLkApply;
         if (needs_xt1 && p.mats[i].xt[0] && !p.mats[i].xt[1]) return false;
       }
     }
-    const bool sym = l.kind == kLkGram || l.kind == kLkSquare;
     const int32_t n = static_cast<int32_t>(rows.size());
     const std::vector<int64_t> rs = row_steps(p, l);
     for (const TileEntry &e : p.lists[l.list]) {
       if (e.mat < 0 || e.mat >= n) return false;
       const MatDev &d = *rows[e.mat];
+      const bool sym = row_sym[e.mat];
       if (e.ti >= d.tm || e.tj >= (sym ? d.tm : d.tn) || (sym && e.tj < e.ti)) return false;
       // pieces: a step range inside the tile's K loop and a slot; reduce
       // entries: at least one slot, all inside the partial region
@@ -846,6 +879,7 @@ std::vector<MatDev> table_contents(const Plan &p, size_t t) {
       d.cc = pt.cc;
       d.cdiag = pt.cdiag;
       d.first_it = pt.first;
+      d.gemm_kind = pt.kind == kLkGram ? kModeGram : kModeSquare;
       out.push_back(d);
     }
   }
@@ -1193,10 +1227,11 @@ static int muon_step_impl(const dmuon_matrix *mats, int32_t n, const dmuon_step_
         rc = launched(launch_update_direct(dm, n, p.ew_total, sc, s), "update_direct launch");
         break;
       default: {
-        const GemmMode mode = l.kind == kLkGram     ? kModeGram
-                              : l.kind == kLkSquare ? kModeSquare
-                              : l.kind == kLkApply  ? kModeApply
-                                                    : kModeFinal;
+        const GemmMode mode = l.kind == kLkGram         ? kModeGram
+                              : l.kind == kLkSquare     ? kModeSquare
+                              : l.kind == kLkGramSquare ? kModeGramSquare
+                              : l.kind == kLkApply      ? kModeApply
+                                                        : kModeFinal;
         const TileEntry *tl = reinterpret_cast<const TileEntry *>(ws + p.off_list[l.list]);
         float *splitk = p.off_splitk >= 0 ? reinterpret_cast<float *>(ws + p.off_splitk) : nullptr;
         rc = launched(launch_ns_stage(mode, l.fp32, l.role, dtab(l.table), tl, p.list_xcd[l.list], sc, splitk, s),

@@ -75,6 +75,9 @@ struct MatDev {
   int32_t ws_f32;       // X^T, A, B of this matrix are fp32 (the fp32 mode, or
                         // a matrix with min(r, c) < kFp32BelowM in a bf16
                         // step), else bf16
+  int32_t gemm_kind;    // in a launch of Gram and Square tiles
+                        // (kModeGramSquare): kModeGram or kModeSquare for
+                        // this matrix; unused otherwise
 };
 
 // One 256 x 256 output tile of a grouped GEMM stage, or a piece of one
@@ -117,7 +120,9 @@ enum GemmMode : int32_t {
                     // -> B; R = A unless sq_r is set (then cb = 0: a product
                     // of two commuting symmetric matrices, itself symmetric)
   kModeApply = 2,   // C = a X + B X                             -> X', X'^T
-  kModeFinal = 3    // last apply: P -= lr*scale*C, orth <- C
+  kModeFinal = 3,   // last apply: P -= lr*scale*C, orth <- C
+  kModeGramSquare = 4  // Gram or Square tiles of different matrices in one
+                       // launch, per MatDev::gemm_kind
 };
 
 // ---- launchers (elementwise.hip) ----

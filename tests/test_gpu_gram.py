@@ -45,7 +45,7 @@ WIDE = [
 def _kinds(nsd, shapes, opts):
     """Launch kinds of the step, without the reduce launches of split stages
     (a GEMM kind with no flops of its own)."""
-    gemm = ("gram", "square", "apply", "final")
+    gemm = ("gram", "square", "apply", "final", "gram_square")
     return [k for k, f in nsd.step_launches(shapes, opts) if f > 0 or k not in gemm]
 
 

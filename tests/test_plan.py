@@ -208,7 +208,7 @@ def test_random_plans_are_consistent(seed):
 def check_split_launches(L):
     """A split stage is a launch of pieces (the stage's flops) followed by a
     launch of reduce entries of the same kind (no flops)."""
-    gemm = ("gram", "square", "apply", "final")
+    gemm = ("gram", "square", "apply", "final", "gram_square")
     for j, (kind, f) in enumerate(L):
         if kind in gemm and f == 0:
             assert j > 0 and L[j - 1][0] == kind and L[j - 1][1] > 0, (j, L)
@@ -274,3 +274,30 @@ def test_nonfinite_flags_offset():
 def test_launch_info_layout_matches_header():
     assert ctypes.sizeof(_lib.LaunchInfo) == 16
     assert _lib.LaunchInfo.kind.offset == 0 and _lib.LaunchInfo.flops.offset == 8
+
+
+def test_gram_and_square_launches_of_the_two_chains_merge():
+    """The two chains' launches merge where they can: same kinds, and a Gram
+    launch of one chain with a Square launch of the other (one launch of
+    kind gram_square).  On the Llama-3.1-8B owner-0 share (direct chain for
+    q_proj, Gram-space chain for the rest) this turns 23 launches into 21:
+    the two q_proj Gram launches that had nothing of their kind to merge
+    with share a launch with a Gram-space Square.  The executed flops are
+    the two chains' own; a share with one chain only has no mixed launch."""
+    L = nsd.step_launches(LLAMA8B_OWNER0, nsd.StepOptions(gram_ns=True))
+    kinds = [k for k, _ in L]
+    assert len(L) == 21 and kinds.count("gram_square") == 2, kinds
+    q = [s for s in LLAMA8B_OWNER0 if s == (4096, 4096)]
+    rest = [s for s in LLAMA8B_OWNER0 if s != (4096, 4096)]
+    apart_q = nsd.step_launches(q, nsd.StepOptions(gram_ns=True))
+    apart_rest = nsd.step_launches(rest, nsd.StepOptions(gram_ns=True))
+    assert sum(f for _, f in L) == sum(f for _, f in apart_q) + sum(f for _, f in apart_rest)
+    assert "gram_square" not in [k for k, _ in apart_q] + [k for k, _ in apart_rest]
+    # each mixed launch carries a q_proj Gram (8 x m(m+1)n) and one Gram-space
+    # Square over k, gate, up and down (m^2(m+1) each)
+    g = 8 * 4096 * 4097 * 4096
+    sq = 8 * 1024 * 1024 * 1025 + 12 * 4096 * 4096 * 4097
+    assert [f for k, f in L if k == "gram_square"] == [g + sq, g + sq]
+    # split launches of every kind stay well formed
+    for shapes in (LLAMA8B_OWNER0, [(513, 513), (300, 700), (700, 300), (256, 1024)]):
+        check_split_launches(nsd.step_launches(shapes, nsd.StepOptions(gram_ns=True)))
