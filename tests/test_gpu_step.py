@@ -310,3 +310,16 @@ def test_split_k_stages(nsd, shapes, k, gram, fp32):
     say(f"split-K step {shapes}, ns_steps {k}, gram_ns {gram}, fp32 {fp32}")
     err = check_step(case, opts, case.run_gpu(opts), case.run_oracle(opts))
     say(f"  worst O rel err {err:.3e}")
+
+
+@pytest.mark.parametrize("shape", [(2, 1 << 22), (1 << 22, 3)])
+def test_longest_side(nsd, shape):
+    """A matrix at the step's limit of 2^22 elements per side (16-bit tile
+    indices up to 16383, 32-bit row-block offsets): m < 128, so its chain
+    runs in fp32; its one Gram tile has 131072 K steps and runs split over
+    K, its Apply has 16384 tiles."""
+    say(f"longest side {shape}")
+    case = Case([shape], "bf16", "bf16", seed=13, m_std=1e-3)
+    opts = nsd.StepOptions()
+    err = check_step(case, opts, case.run_gpu(opts), case.run_oracle(opts))
+    say(f"  O rel err {err:.3e}")
