@@ -25,6 +25,12 @@
 //           also stored to the packed slot when the step has one, and X'
 //           to orth_out; no workspace write
 //
+// A launch can also hold Gram tiles of some matrices and Square tiles of
+// others (the two chains of one step sharing a launch): its instance reads
+// each tile's stage from the matrix's table row and runs that stage's tile
+// function.  In a diagonal tile of Gram or Square, the waves whose quadrant
+// lies below the diagonal skip their products.
+//
 // From six iterations on, B (and every P of the Gram-space chain) is kept
 // as a bf16 hi + lo pair, hi = RNE(v), lo = RNE(v - hi): Square stores both
 // halves, and a product that reads a pair runs its K loop over one more
