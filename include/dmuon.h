@@ -118,7 +118,10 @@ enum {
 /* One launch of a step, as dmuon_step_launches describes it. */
 typedef struct {
   int32_t kind;         /* DMUON_LAUNCH_*                                    */
-  int32_t reserved;     /* 0                                                 */
+  int32_t tile;         /* GEMM launches: the output tile edge, 256, or 128
+                           for a bf16 Square launch of whole tiles whose
+                           256-tiles would leave CUs idle; 0 for the
+                           element-wise launches                             */
   double flops;         /* flops the GEMM launches execute (symmetric
                            products as their upper triangle: m(m+1)n for
                            A = X X^T, m^2(m+1) for an m x m product, 2m^2 n

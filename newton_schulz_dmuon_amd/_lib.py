@@ -73,7 +73,7 @@ class StepConfig(ctypes.Structure):
 
 class LaunchInfo(ctypes.Structure):
     """``dmuon_launch_info``"""
-    _fields_ = [("kind", ctypes.c_int32), ("reserved", ctypes.c_int32), ("flops", ctypes.c_double)]
+    _fields_ = [("kind", ctypes.c_int32), ("tile", ctypes.c_int32), ("flops", ctypes.c_double)]
 
 
 class Tensor(ctypes.Structure):

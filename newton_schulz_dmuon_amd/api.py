@@ -103,10 +103,11 @@ def matrices(params, grads=None, momenta=None, scales=None, orth_out=None,
     return arr, n
 
 
-def step_launches(shapes: Sequence, opts: StepOptions):
+def step_launches(shapes: Sequence, opts: StepOptions, tiles: bool = False):
     """The step's launch sequence for matrices of these ``(rows, cols)``
     shapes: a list of ``(kind, algorithmic_flops)``, kind a name from
-    ``_lib.LAUNCH_KINDS``.  Host-only."""
+    ``_lib.LAUNCH_KINDS``; with ``tiles``, ``(kind, flops, tile_edge)``
+    (0 for the element-wise launches).  Host-only."""
     n = len(shapes)
     arr = (Matrix * max(n, 1))()
     for i, (r, c) in enumerate(shapes):
@@ -117,6 +118,8 @@ def step_launches(shapes: Sequence, opts: StepOptions):
     check(lib.dmuon_step_launches(arr, n, ctypes.byref(cfg), None, 0, ctypes.byref(count)))
     out = (LaunchInfo * max(count.value, 1))()
     check(lib.dmuon_step_launches(arr, n, ctypes.byref(cfg), out, count.value, ctypes.byref(count)))
+    if tiles:
+        return [(_lib.LAUNCH_KINDS[out[j].kind], out[j].flops, out[j].tile) for j in range(count.value)]
     return [(_lib.LAUNCH_KINDS[out[j].kind], out[j].flops) for j in range(count.value)]
 
 

@@ -58,6 +58,11 @@
 // distinct 16-byte bank groups of the 256-byte LDS line (two rows per line),
 // which the bank-conflict counter confirms at zero.
 //
+// A bf16 Square launch with too few 256-tiles to fill the CUs runs 128x128
+// tiles instead (ns_gemm_small_kernel): the same tile function with every
+// extent halved, each wave 64x32 = 4x2 MFMA blocks, 2 x 32 KB of LDS, and
+// two work-groups per CU, so four times the tiles share the CUs.
+//
 // Operands are zero-padded to multiples of 256 in the workspace, so no
 // load or store is masked except the caller-visible writes of Final.
 
@@ -256,13 +261,16 @@ __device__ __forceinline__ f32x4 bf16_low_part(const f32x4 &v) {
   return r;
 }
 
+// The staged tile is TS x TS bf16 (TS = 256: 512-byte rows of 32 chunks;
+// TS = 128: 256-byte rows of 16 chunks, the swizzles staying inside a row).
 // Puts rows r0 .. r0+3 of column c (one lane's four values) as bf16.
+template <int TS = 256>
 __device__ __forceinline__ void stage_tile_put(lds_char *lds, int r0, int c, const f32x4 &v) {
   typedef __attribute__((address_space(3))) uint16_t lds_u16;
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int row = r0 + k;
-    const int off = row * 512 + tile_swz<kSwzRows>(row, c >> 3) * 16 + (c & 7) * 2;
+    const int off = row * (2 * TS) + tile_swz<kSwzRows>(row, c >> 3) * 16 + (c & 7) * 2;
     *(lds_u16 *)(lds + off) = f32_to_bf16_bits(v[k]);
   }
 }
@@ -272,9 +280,12 @@ __device__ __forceinline__ void stage_tile_put(lds_char *lds, int r0, int c, con
 // when c > row.  Every element of the tile is written once, so the stored
 // tile is exactly symmetric even when the product is only symmetric in
 // exact arithmetic (A P^2 and Q P of the Gram-space chain).
+template <int TS = 256>
 __device__ __forceinline__ void stage_tile_put_sym(lds_char *lds, int r0, int c, const f32x4 &v) {
   typedef __attribute__((address_space(3))) uint16_t lds_u16;
-  auto at = [](int row, int col) { return row * 512 + tile_swz<kSwzRows>(row, col >> 3) * 16 + (col & 7) * 2; };
+  auto at = [](int row, int col) {
+    return row * (2 * TS) + tile_swz<kSwzRows>(row, col >> 3) * 16 + (col & 7) * 2;
+  };
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int row = r0 + k;
@@ -286,38 +297,43 @@ __device__ __forceinline__ void stage_tile_put_sym(lds_char *lds, int r0, int c,
 
 // Puts elements c0 .. c0+3 of row r (c0 a multiple of four) as bf16: the
 // transposed placement of a lane's four values.
+template <int TS = 256>
 __device__ __forceinline__ void stage_tile_put_t(lds_char *lds, int r, int c0, const f32x4 &v) {
   typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
   u32x2 u;
   u.x = static_cast<uint32_t>(f32_to_bf16_bits(v[0])) | (static_cast<uint32_t>(f32_to_bf16_bits(v[1])) << 16);
   u.y = static_cast<uint32_t>(f32_to_bf16_bits(v[2])) | (static_cast<uint32_t>(f32_to_bf16_bits(v[3])) << 16);
-  *(lds_u32x2 *)(lds + r * 512 + tile_swz<kSwzCols>(r, c0 >> 3) * 16 + (c0 & 7) * 2) = u;
+  *(lds_u32x2 *)(lds + r * (2 * TS) + tile_swz<kSwzCols>(r, c0 >> 3) * 16 + (c0 & 7) * 2) = u;
 }
 
 // Writes the staged tile to dst (row-major, leading dimension ld elements)
-// with 16-byte stores: thread t moves chunks t, t + 512, ... (row = f / 32).
-// All 16 LDS reads are issued before the first store, so their latencies
-// overlap instead of adding up (64 VGPRs, free at this point).
+// with 16-byte stores: thread t moves chunks t, t + 512, ... (TS / 8 chunks
+// per row).  All of a thread's LDS reads (16 for TS = 256, 4 for 128) are
+// issued before its first store, so their latencies overlap instead of
+// adding up.
 // Starts with a barrier (the puts are visible); a later put into the same
 // LDS needs lds_barrier() first (every wave's flush reads done).
-template <int SW>
+template <int SW, int TS = 256>
 __device__ __forceinline__ void stage_tile_flush(lds_char *lds, uint16_t *dst, int64_t ld, int tid) {
+  constexpr int kChunksPerRow = TS / 8, kPerThread = TS * TS / 8 / 512;
+  constexpr int kRowShift = TS == 256 ? 5 : 4;
+  static_assert(kChunksPerRow == (1 << kRowShift), "chunks per row");
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
   // opaque: each flush rebuilds its addresses instead of keeping them live
   // across the epilogue's other flushes
   asm volatile("" : "+v"(tid));
-  u32x4 v[16];
+  u32x4 v[kPerThread];
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
+  for (int q = 0; q < kPerThread; ++q) {
     const int f = q * 512 + tid;
-    const int row = f >> 5, chunk = f & 31;
-    v[q] = *(const lds_u32x4 *)(lds + row * 512 + tile_swz<SW>(row, chunk) * 16);
+    const int row = f >> kRowShift, chunk = f & (kChunksPerRow - 1);
+    v[q] = *(const lds_u32x4 *)(lds + row * (2 * TS) + tile_swz<SW>(row, chunk) * 16);
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
+  for (int q = 0; q < kPerThread; ++q) {
     const int f = q * 512 + tid;
-    const int row = f >> 5, chunk = f & 31;
+    const int row = f >> kRowShift, chunk = f & (kChunksPerRow - 1);
     *(g_u32x4 *)(dst + row * ld + chunk * 8) = v[q];
   }
 }
@@ -331,9 +347,20 @@ constexpr int kRoleWhole = 0, kRolePiece = 1, kRoleReduce = 2;
 
 // One tile (or piece of a tile) of stage MODE: the work-group's whole work.
 // lds: the work-group's 128 KB, [2 stages][L, R][256 rows][128 B].
-template <typename T, int MODE, int ROLE>
+// TS: the tile size, 256 (every stage) or 128 (Square, bf16 whole tiles,
+// for launches with too few 256-tiles to fill the chip): the same 2 x 4
+// waves, each computing (TS / 2) x (TS / 4), on a 64 KB operand ring.
+template <typename T, int MODE, int ROLE, int TS = 256>
 __device__ __forceinline__ void gemm_tile(lds_char *const lds, const MatDev &d, const TileEntry &e,
                                           const StepScalars &s, f32x4 *__restrict__ splitk) {
+  static_assert(TS == 256 || (TS == 128 && MODE == kModeSquare && ROLE == kRoleWhole && sizeof(T) == 2),
+                "128-tiles: bf16 Square, whole tiles");
+  // the tile's geometry (shadowing the 256-tile constants)
+  constexpr int kTile = TS;
+  constexpr int kWaveM = kTile / kWavesM, kWaveN = kTile / kWavesN;
+  constexpr int kFragM = kWaveM / 16, kFragN = kWaveN / 16;
+  constexpr int kOperandBytes = kTile * kRowBytes, kHalfBytes = kOperandBytes / 2;
+  constexpr int kStageBytes = 2 * kOperandBytes;
   const int32_t ti = e.ti, tj = e.tj;
 
   // Gram reads X^T (n_p x m_p): its operand tiles are MN-major, K = n runs
@@ -432,7 +459,7 @@ __device__ __forceinline__ void gemm_tile(lds_char *const lds, const MatDev &d, 
         go += static_cast<uint32_t>(h * (kHalfBytes / (kRowBytes / static_cast<int>(sizeof(T))))) +
               static_cast<uint32_t>(lpc ^ mn_swz<T>(row)) * 16;
       else
-        go += static_cast<uint32_t>(h * 128) * static_cast<uint32_t>(ld_bytes) +
+        go += static_cast<uint32_t>(h * (kTile / 2)) * static_cast<uint32_t>(ld_bytes) +
               static_cast<uint32_t>(swz(lpc, row)) * 16;
       __builtin_amdgcn_global_load_lds(
           (const void *)(src + go),
@@ -745,9 +772,9 @@ __device__ __forceinline__ void gemm_tile(lds_char *const lds, const MatDev &d, 
         }
         if constexpr (kStage) {
           if (ti != tj)
-            stage_tile_put(lds, wm * kWaveM + i * 16 + 4 * g4, wn * kWaveN + j * 16 + r16, val);
+            stage_tile_put<TS>(lds, wm * kWaveM + i * 16 + 4 * g4, wn * kWaveN + j * 16 + r16, val);
           else
-            stage_tile_put_sym(lds, wm * kWaveM + i * 16 + 4 * g4, wn * kWaveN + j * 16 + r16, val);
+            stage_tile_put_sym<TS>(lds, wm * kWaveM + i * 16 + 4 * g4, wn * kWaveN + j * 16 + r16, val);
           acc[i][j] = val;  // kept for the mirror tile
         } else if (ti != tj) {
 #pragma unroll
@@ -770,15 +797,15 @@ __device__ __forceinline__ void gemm_tile(lds_char *const lds, const MatDev &d, 
       // mirror tile (tj, ti) staged the transposed way
       uint16_t *const o16 = reinterpret_cast<uint16_t *>(out);
       uint16_t *const lo16 = MODE == kModeSquare ? reinterpret_cast<uint16_t *>(d.out_lo) : nullptr;
-      stage_tile_flush<kSwzRows>(lds, o16 + tile_ij, mp, tid);
+      stage_tile_flush<kSwzRows, TS>(lds, o16 + tile_ij, mp, tid);
       if (ti != tj) {
         lds_barrier();
 #pragma unroll
         for (int i = 0; i < kFragM; ++i)
 #pragma unroll
           for (int j = 0; j < kFragN; ++j)
-            stage_tile_put_t(lds, wn * kWaveN + j * 16 + r16, wm * kWaveM + i * 16 + 4 * g4, acc[i][j]);
-        stage_tile_flush<kSwzCols>(lds, o16 + tile_ji, mp, tid);
+            stage_tile_put_t<TS>(lds, wn * kWaveN + j * 16 + r16, wm * kWaveM + i * 16 + 4 * g4, acc[i][j]);
+        stage_tile_flush<kSwzCols, TS>(lds, o16 + tile_ji, mp, tid);
       }
       if (lo16) {
         // The low halves go to the same LDS slots as the high ones: opaque
@@ -794,20 +821,20 @@ __device__ __forceinline__ void gemm_tile(lds_char *const lds, const MatDev &d, 
           for (int j = 0; j < kFragN; ++j) {
             const f32x4 lo = bf16_low_part(acc[i][j]);
             if (ti != tj)
-              stage_tile_put(lds, wm * kWaveM + i * 16 + 4 * lg4, wn * kWaveN + j * 16 + lr16, lo);
+              stage_tile_put<TS>(lds, wm * kWaveM + i * 16 + 4 * lg4, wn * kWaveN + j * 16 + lr16, lo);
             else
-              stage_tile_put_sym(lds, wm * kWaveM + i * 16 + 4 * lg4, wn * kWaveN + j * 16 + lr16, lo);
+              stage_tile_put_sym<TS>(lds, wm * kWaveM + i * 16 + 4 * lg4, wn * kWaveN + j * 16 + lr16, lo);
           }
-        stage_tile_flush<kSwzRows>(lds, lo16 + tile_ij, mp, tid);
+        stage_tile_flush<kSwzRows, TS>(lds, lo16 + tile_ij, mp, tid);
         if (ti != tj) {
           lds_barrier();
 #pragma unroll
           for (int i = 0; i < kFragM; ++i)
 #pragma unroll
             for (int j = 0; j < kFragN; ++j)
-              stage_tile_put_t(lds, wn * kWaveN + j * 16 + lr16, wm * kWaveM + i * 16 + 4 * lg4,
+              stage_tile_put_t<TS>(lds, wn * kWaveN + j * 16 + lr16, wm * kWaveM + i * 16 + 4 * lg4,
                                bf16_low_part(acc[i][j]));
-          stage_tile_flush<kSwzCols>(lds, lo16 + tile_ji, mp, tid);
+          stage_tile_flush<kSwzCols, TS>(lds, lo16 + tile_ji, mp, tid);
         }
       }
     }
@@ -824,12 +851,12 @@ __device__ __forceinline__ void gemm_tile(lds_char *const lds, const MatDev &d, 
         for (int v = 0; v < 4; ++v) val[v] = acc[i][j][v] * inv;
         // X'^T[col][row .. row+3]: four consecutive elements of a row
         if constexpr (kStage)
-          stage_tile_put_t(lds, wn * kWaveN + j * 16 + r16, wm * kWaveM + i * 16 + 4 * g4, val);
+          stage_tile_put_t<TS>(lds, wn * kWaveN + j * 16 + r16, wm * kWaveM + i * 16 + 4 * g4, val);
         else
           Vec4<T>::st(XTn + col * mp + row, val);
       }
     if constexpr (kStage)
-      stage_tile_flush<kSwzCols>(lds, reinterpret_cast<uint16_t *>(XTn) + static_cast<int64_t>(tj) * kTile * mp +
+      stage_tile_flush<kSwzCols, TS>(lds, reinterpret_cast<uint16_t *>(XTn) + static_cast<int64_t>(tj) * kTile * mp +
                                           static_cast<int64_t>(ti) * kTile, mp, tid);
   } else {  // kModeFinal
     // O = (aX + BX) * inv for the tile (rows over m, columns over n) goes
@@ -999,6 +1026,20 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_kernel(const MatDev *__restr
   }
 }
 
+// Square launches of 128 x 128 tiles (bf16, whole tiles): the same work-group
+// of 8 waves on a 64 KB operand ring, so that two work-groups fit on a CU.
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void ns_gemm_small_kernel(const MatDev *__restrict__ mats, const TileEntry *__restrict__ tiles, StageXcd xcd,
+                          StepScalars s) {
+  __shared__ __attribute__((aligned(1024))) char smem[4 * 128 * kRowBytes];  // 64 KB
+  lds_char *const lds = (lds_char *)smem;
+  const int32_t w = static_cast<int32_t>(blockIdx.x);
+  const int32_t xi = w % kXcds, k = w / kXcds;
+  if (k >= xcd.count[xi]) return;  // whole group leaves before any barrier
+  const TileEntry e = tiles[xcd.first[xi] + k];
+  gemm_tile<uint16_t, kModeSquare, kRoleWhole, 128>(lds, mats[e.mat], e, s, nullptr);
+}
+
 template <typename T, int ROLE>
 hipError_t launch_role(GemmMode mode, const MatDev *mats, const TileEntry *tiles, const StageXcd &xcd,
                        StepScalars s, f32x4 *splitk, hipStream_t st) {
@@ -1039,6 +1080,16 @@ hipError_t launch_t(GemmMode mode, int role, const MatDev *mats, const TileEntry
 }
 
 }  // namespace
+
+hipError_t launch_ns_small_square(const MatDev *mats, const TileEntry *tiles, const StageXcd &xcd, StepScalars s,
+                                  hipStream_t st) {
+  int32_t longest = 0;
+  for (int x = 0; x < kXcds; ++x) longest = xcd.count[x] > longest ? xcd.count[x] : longest;
+  if (longest == 0) return hipSuccess;
+  const dim3 grid(static_cast<uint32_t>(longest) * kXcds), block(kThreads);
+  hipLaunchKernelGGL(ns_gemm_small_kernel, grid, block, 0, st, mats, tiles, xcd, s);
+  return hipGetLastError();
+}
 
 hipError_t launch_ns_stage(GemmMode mode, bool fp32, int role, const MatDev *mats, const TileEntry *tiles,
                            const StageXcd &xcd, StepScalars s, float *splitk, hipStream_t st) {

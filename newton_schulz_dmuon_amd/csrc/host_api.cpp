@@ -179,6 +179,7 @@ struct Launch {
   int32_t table = 0;        // MatDev table: the parts' matrices, in order
   int32_t list = 0;         // tile list over that table
   int32_t role = 0;         // 0 whole tiles, 1 pieces of split tiles, 2 their reduce
+  int32_t tile = 256;       // tile size: 256, or 128 (bf16 Square, whole tiles)
   double flops = 0;         // algorithmic flops (symmetric products: upper triangle)
 };
 
@@ -214,7 +215,8 @@ struct Plan {
 // its 32 CUs work through long-K tiles first and the tiles running together
 // on one XCD read few distinct panels through its L2.
 void build_stage_tiles(const std::vector<MatDev> &mats, const std::vector<int32_t> &passes,
-                       const std::vector<int32_t> &stages, std::vector<TileEntry> &out, StageXcd &xcd) {
+                       const std::vector<int32_t> &stages, int32_t tile, std::vector<TileEntry> &out,
+                       StageXcd &xcd) {
   struct Block {
     int64_t cost;
     int32_t mat, ti0, tj0;
@@ -226,7 +228,7 @@ void build_stage_tiles(const std::vector<MatDev> &mats, const std::vector<int32_
     const bool sym = st < 2;
     const int bm = 4, bn = sym ? 4 : 8;
     const int64_t depth = (st == 0 ? d.np : d.mp) * passes[i];
-    const int32_t rows = d.tm, cols = sym ? d.tm : d.tn;
+    const int32_t rows = static_cast<int32_t>(d.mp / tile), cols = static_cast<int32_t>((sym ? d.mp : d.np) / tile);
     for (int32_t bi = 0; bi < rows; bi += bm)
       for (int32_t bj = sym ? bi : 0; bj < cols; bj += bn) {
         int64_t nt = 0;
@@ -247,7 +249,7 @@ void build_stage_tiles(const std::vector<MatDev> &mats, const std::vector<int32_
     const MatDev &d = mats[b.mat];
     const bool sym = stages[b.mat] < 2;
     const int bm = 4, bn = sym ? 4 : 8;
-    const int32_t rows = d.tm, cols = sym ? d.tm : d.tn;
+    const int32_t rows = static_cast<int32_t>(d.mp / tile), cols = static_cast<int32_t>((sym ? d.mp : d.np) / tile);
     for (int32_t ti = b.ti0; ti < std::min(b.ti0 + bm, rows); ++ti)
       for (int32_t tj = b.tj0; tj < std::min(b.tj0 + bn, cols); ++tj)
         if (!sym || tj >= ti)
@@ -269,9 +271,11 @@ std::map<std::vector<int64_t>, std::pair<std::vector<TileEntry>, StageXcd>> g_ti
 constexpr size_t kTilesCacheMax = 64;
 
 void cached_stage_tiles(const std::vector<MatDev> &mats, const std::vector<int32_t> &passes,
-                        const std::vector<int32_t> &stages, std::vector<TileEntry> &out, StageXcd &xcd) {
+                        const std::vector<int32_t> &stages, int32_t tile, std::vector<TileEntry> &out,
+                        StageXcd &xcd) {
   std::vector<int64_t> key;
-  key.reserve(6 * mats.size());
+  key.reserve(1 + 6 * mats.size());
+  key.push_back(tile);
   for (size_t i = 0; i < mats.size(); ++i) {
     const MatDev &d = mats[i];
     key.push_back(stages[i]);
@@ -290,7 +294,7 @@ void cached_stage_tiles(const std::vector<MatDev> &mats, const std::vector<int32
       return;
     }
   }
-  build_stage_tiles(mats, passes, stages, out, xcd);
+  build_stage_tiles(mats, passes, stages, tile, out, xcd);
   std::lock_guard<std::mutex> lock(g_tiles_mu);
   if (g_tiles_cache.size() >= kTilesCacheMax) g_tiles_cache.clear();
   g_tiles_cache.emplace(std::move(key), std::make_pair(out, xcd));
@@ -401,6 +405,20 @@ std::vector<int32_t> choose_pieces(const std::vector<int64_t> &steps) {
     }
   }
   return best;
+}
+
+// A Square launch can run 128 x 128 tiles instead (bf16, whole tiles): four
+// times the tiles, each a quarter of the work, two work-groups per CU.  The
+// estimate: a 128-tile K step costs kSmallStepCost of a 256-tile step on
+// one of 2 x kCUs slots; the 128-tiles are taken when their list schedule
+// beats the 256-tiles' by kSmallMargin.
+constexpr double kSmallStepCost = 0.5;
+constexpr double kSmallMargin = 0.8;
+bool small_tiles_pay(const std::vector<int64_t> &steps256, const std::vector<int64_t> &steps128) {
+  if (steps256.empty() || static_cast<int64_t>(steps256.size()) >= kCUs) return false;
+  const double t256 = static_cast<double>(list_makespan(steps256, kCUs));
+  const double t128 = kSmallStepCost * static_cast<double>(list_makespan(steps128, 2 * kCUs));
+  return t128 < kSmallMargin * t256;
 }
 
 // Per-XCD lists of entries with costs: costliest first, each to the XCD
@@ -684,15 +702,44 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
         }
       p.lists.emplace_back();
       p.list_xcd.emplace_back();
-      cached_stage_tiles(shapes, passes, stages, p.lists.back(), p.list_xcd.back());
+      cached_stage_tiles(shapes, passes, stages, 256, p.lists.back(), p.list_xcd.back());
       li = list_of.emplace(key, static_cast<int32_t>(p.lists.size()) - 1).first;
     }
     l.list = li->second;
-    // split K where the launch leaves CUs idle
-    const std::vector<TileEntry> &tl = p.lists[l.list];
     const std::vector<int64_t> rs = row_steps(p, l);
     std::vector<int64_t> steps;
-    for (const TileEntry &e : tl) steps.push_back(rs[e.mat]);
+    for (const TileEntry &e : p.lists[l.list]) steps.push_back(rs[e.mat]);
+    // a bf16 Square launch with too few 256-tiles for the CUs runs 128-tiles
+    // where the list-schedule estimate says they finish sooner
+    if (l.kind == kLkSquare && !l.fp32) {
+      std::vector<int32_t> key128 = key;
+      key128.push_back(128);
+      auto l128 = list_of.find(key128);
+      if (l128 == list_of.end()) {
+        std::vector<MatDev> shapes;
+        std::vector<int32_t> passes, stages;
+        for (size_t q = 0; q < key.size(); q += 3)
+          for (int32_t i : p.groups[key[q]]) {
+            shapes.push_back(p.mats[i]);
+            passes.push_back(key[q + 1]);
+            stages.push_back(key[q + 2]);
+          }
+        p.lists.emplace_back();
+        p.list_xcd.emplace_back();
+        cached_stage_tiles(shapes, passes, stages, 128, p.lists.back(), p.list_xcd.back());
+        l128 = list_of.emplace(key128, static_cast<int32_t>(p.lists.size()) - 1).first;
+      }
+      std::vector<int64_t> steps128;
+      for (const TileEntry &e : p.lists[l128->second]) steps128.push_back(rs[e.mat]);
+      if (small_tiles_pay(steps, steps128)) {
+        l.tile = 128;
+        l.list = l128->second;
+        p.prog.push_back(std::move(l));
+        continue;
+      }
+    }
+    // split K where the launch leaves CUs idle
+    const std::vector<TileEntry> &tl = p.lists[l.list];
     const std::vector<int32_t> pieces = choose_pieces(steps);
     if (*std::max_element(pieces.begin(), pieces.end()) > 1) {
       std::vector<std::pair<int64_t, TileEntry>> pc, rd;
@@ -836,12 +883,15 @@ bool plan_consistent(const Plan &p) {
       }
     }
     const int32_t n = static_cast<int32_t>(rows.size());
+    // 128-tiles: bf16 Square launches of whole tiles only
+    if (l.tile != 256 && (l.tile != 128 || l.kind != kLkSquare || l.fp32 || l.role != 0)) return false;
     const std::vector<int64_t> rs = row_steps(p, l);
     for (const TileEntry &e : p.lists[l.list]) {
       if (e.mat < 0 || e.mat >= n) return false;
       const MatDev &d = *rows[e.mat];
       const bool sym = row_sym[e.mat];
-      if (e.ti >= d.tm || e.tj >= (sym ? d.tm : d.tn) || (sym && e.tj < e.ti)) return false;
+      const int64_t rows = d.mp / l.tile, cols = (sym ? d.mp : d.np) / l.tile;
+      if (e.ti >= rows || e.tj >= cols || (sym && e.tj < e.ti)) return false;
       // pieces: a step range inside the tile's K loop and a slot; reduce
       // entries: at least one slot, all inside the partial region
       if (l.role == 1 && (e.k0 < 0 || e.k1 <= e.k0 || e.k1 > rs[e.mat] || e.slot < 0 || e.slot >= p.splitk_slots))
@@ -1234,8 +1284,12 @@ static int muon_step_impl(const dmuon_matrix *mats, int32_t n, const dmuon_step_
                                                         : kModeFinal;
         const TileEntry *tl = reinterpret_cast<const TileEntry *>(ws + p.off_list[l.list]);
         float *splitk = p.off_splitk >= 0 ? reinterpret_cast<float *>(ws + p.off_splitk) : nullptr;
-        rc = launched(launch_ns_stage(mode, l.fp32, l.role, dtab(l.table), tl, p.list_xcd[l.list], sc, splitk, s),
-                      "Newton-Schulz stage launch");
+        if (l.tile == 128)
+          rc = launched(launch_ns_small_square(dtab(l.table), tl, p.list_xcd[l.list], sc, s),
+                        "Newton-Schulz stage launch (128-tiles)");
+        else
+          rc = launched(launch_ns_stage(mode, l.fp32, l.role, dtab(l.table), tl, p.list_xcd[l.list], sc, splitk, s),
+                        "Newton-Schulz stage launch");
       }
     }
     if (rc) return rc;
@@ -1264,7 +1318,8 @@ int dmuon_step_launches(const dmuon_matrix *mats, int32_t n, const dmuon_step_co
   *count = static_cast<int32_t>(p.prog.size());
   for (int32_t j = 0; j < cap && j < *count; ++j) {
     out[j].kind = p.prog[j].kind;
-    out[j].reserved = 0;
+    const bool gemm = p.prog[j].kind >= kLkGram;
+    out[j].tile = gemm ? p.prog[j].tile : 0;
     out[j].flops = p.prog[j].flops;
   }
   return DMUON_OK;

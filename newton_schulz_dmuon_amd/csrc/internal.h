@@ -191,5 +191,9 @@ hipError_t noalloc_scratch(void **ptr);
 hipError_t launch_ns_stage(GemmMode mode, bool fp32, int role, const MatDev *mats,
                            const TileEntry *tiles, const StageXcd &xcd,
                            StepScalars s, float *splitk, hipStream_t st);
+// A bf16 Square launch of 128 x 128 tiles (TileEntry ti, tj in 128-tile
+// units; whole tiles only).
+hipError_t launch_ns_small_square(const MatDev *mats, const TileEntry *tiles, const StageXcd &xcd,
+                                  StepScalars s, hipStream_t st);
 
 }  // namespace dmuon

@@ -292,7 +292,7 @@ def test_small_matrices_run_in_fp32(nsd, k):
 
 
 @pytest.mark.parametrize("shapes,k,gram,fp32", [
-    ([(2048, 2048)], 5, False, False),      # Gram and Square split (36 tiles of 32 steps)
+    ([(2048, 2048)], 5, False, False),      # Gram splits (36 tiles of 32 steps)
     ([(2048, 2048)], 8, False, False),      # with B's pairs: Apply and Final split too
     ([(2048, 4608)], 6, True, False),       # Gram-space chain, P and T pairs
     ([(2048, 2048)], 5, False, True),       # fp32 mode: 64-step tiles, every stage split
@@ -308,6 +308,25 @@ def test_split_k_stages(nsd, shapes, k, gram, fp32):
     dt = "f32" if fp32 else "bf16"
     case = Case(shapes, dt, dt, seed=70 + k, m_std=1e-3)
     say(f"split-K step {shapes}, ns_steps {k}, gram_ns {gram}, fp32 {fp32}")
+    err = check_step(case, opts, case.run_gpu(opts), case.run_oracle(opts))
+    say(f"  worst O rel err {err:.3e}")
+
+
+@pytest.mark.parametrize("shapes,k,gram", [
+    ([(1000, 1500)], 5, False),                          # 8 x 8 128-tiles, the last rows ragged
+    ([(1000, 1500), (129, 640)], 8, False),              # B's pairs; 2 x 2 beside 8 x 8
+    ([(1536, 1536), (256, 1536), (1536, 4608)], 6, True),  # Gram-space chain beside the direct one
+    ([(1536, 1536), (256, 1536), (1536, 8960)], 5, True),  # Qwen2.5-1.5B shapes: q, k, down
+])
+def test_square_launches_of_128_tiles(nsd, shapes, k, gram):
+    """Square launches with fewer 256-tiles than CUs run 128 x 128 tiles
+    (two work-groups per CU; diagonal tiles skip their below-diagonal
+    quarter and mirror the rest); the result matches the oracle."""
+    opts = nsd.StepOptions(ns_steps=k, gram_ns=gram)
+    L = nsd.step_launches(shapes, opts, tiles=True)
+    assert any(kd == "square" and t == 128 for kd, _, t in L), L
+    case = Case(shapes, "bf16", "bf16", seed=80 + k, m_std=1e-3)
+    say(f"128-tile Square launches {shapes}, ns_steps {k}, gram_ns {gram}")
     err = check_step(case, opts, case.run_gpu(opts), case.run_oracle(opts))
     say(f"  worst O rel err {err:.3e}")
 

@@ -229,18 +229,47 @@ def test_split_k_where_launches_leave_cus_idle():
         assert reduces and set(reduces) == {"gram"}, reduces
     L = nsd.step_launches(LLAMA8B_OWNER0, nsd.StepOptions(gram_ns=True))
     assert all(f > 0 for k, f in L if k in ("gram", "square", "apply", "final"))
-    # a single 2048 x 2048 matrix: 36 symmetric tiles of 32 K steps split;
-    # 64 Apply tiles of 32 steps do not (two pieces would not pay for the
-    # reduce), but do when B's pairs double Apply's K loop (ns_steps 8) and
-    # in the fp32 mode (64 steps of 32 elements)
+    # a single 2048 x 2048 matrix: 36 symmetric Gram tiles of 32 K steps
+    # split (its Square launches run 128-tiles instead); 64 Apply tiles of 32
+    # steps do not (two pieces would not pay for the reduce), but do when B's
+    # pairs double Apply's K loop (ns_steps 8); in the fp32 mode (64 steps of
+    # 32 elements, no 128-tiles) every stage splits
     def split_kinds(opts):
         L = nsd.step_launches([(2048, 2048)], opts)
         check_split_launches(L)
         assert sum(f for _, f in L) == direct_flops(2048, 2048, opts.ns_steps, opts.ns_fp32)
         return {k for k, f in L if k in ("gram", "square", "apply", "final") and f == 0}
-    assert split_kinds(nsd.StepOptions()) == {"gram", "square"}
-    assert split_kinds(nsd.StepOptions(ns_steps=8)) == {"gram", "square", "apply", "final"}
+    assert split_kinds(nsd.StepOptions()) == {"gram"}
+    assert split_kinds(nsd.StepOptions(ns_steps=8)) == {"gram", "apply", "final"}
     assert split_kinds(nsd.StepOptions(ns_fp32=True)) == {"gram", "square", "apply", "final"}
+
+
+def test_square_launches_with_few_tiles_run_128_tiles():
+    """A bf16 Square launch whose 256-tiles would leave CUs idle runs
+    128 x 128 tiles (four times the tiles, two work-groups per CU), never
+    split; every other GEMM launch runs 256-tiles.  The Qwen2.5-1.5B layer's
+    Square launches (78 upper-triangle 256-tiles at 1536) take 128-tiles; the
+    Llama-3.1-8B share's (1088+ tiles per launch) do not, nor does the fp32
+    mode."""
+    from synth import workload
+    w = workload(2)
+    qwen = [(r, c) for _, r, c in w.shapes]
+    for shapes, opts, want in ((qwen, nsd.StepOptions(), 128), (qwen, nsd.StepOptions(gram_ns=True), 128),
+                               (qwen, nsd.StepOptions(ns_steps=8), 128),
+                               (qwen, nsd.StepOptions(ns_fp32=True), 256),
+                               (LLAMA8B_OWNER0, nsd.StepOptions(gram_ns=True), 256),
+                               (LLAMA8B_OWNER0, nsd.StepOptions(), 256)):
+        L = nsd.step_launches(shapes, opts, tiles=True)
+        assert [(k, f) for k, f, _ in L] == nsd.step_launches(shapes, opts)
+        for j, (k, f, t) in enumerate(L):
+            if k in ("momentum_sumsq", "momentum_orient", "norm", "update_direct"):
+                assert t == 0
+            elif k == "square" and f > 0:
+                assert t == want, (j, L)
+                if t == 128:  # whole tiles: no reduce launch follows
+                    assert j + 1 == len(L) or L[j + 1][:2] != ("square", 0.0)
+            else:
+                assert t == 256, (j, L)
 
 
 def test_nonfinite_flags_offset():
