@@ -54,7 +54,8 @@ def kernel_metadata(tmp_path):
 def test_kernels_use_no_scratch(tmp_path):
     kernels = kernel_metadata(tmp_path)
     names = " ".join(kernels)
-    for k in ("ns_gemm_kernel", "momentum_orient_kernel", "adamw_kernel", "pack_copy_kernel"):
+    for k in ("ns_gemm_kernel", "ns_gemm_small_kernel", "momentum_orient_kernel", "adamw_kernel",
+              "pack_copy_kernel"):
         assert k in names, f"{k} missing from the code objects"
     bad = {k: v for k, v in kernels.items()
            if v.get("private_segment_fixed_size", 0) or v.get("vgpr_spill_count", 0)}
