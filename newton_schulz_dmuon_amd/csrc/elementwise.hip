@@ -32,6 +32,8 @@ __device__ __forceinline__ double block_sum_f64(double v, double *lds) {
 
 typedef unsigned int vu32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(1))) vu32x2 g_u32x2;
+typedef unsigned int vu32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) vu32x4 g_u32x4;
 typedef __attribute__((address_space(1))) f32x4 g_f32x4;
 
 // Four consecutive bf16 or fp32 values at flat index i (i multiple of 4).
@@ -48,23 +50,6 @@ __device__ __forceinline__ f32x4 load_grad4(const void *g, int32_t dt, int64_t i
   }
   return r;
 }
-
-// Four consecutive workspace elements as one 8-byte (bf16) or 16-byte (fp32)
-// store (address: a multiple of four elements).
-template <typename T> struct Vec4St;
-template <> struct Vec4St<uint16_t> {
-  static __device__ __forceinline__ void st(uint16_t *p, const float (&v)[4]) {
-    vu32x2 u;
-    u.x = f32_to_bf16_bits(v[0]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[1])) << 16);
-    u.y = f32_to_bf16_bits(v[2]) | (static_cast<uint32_t>(f32_to_bf16_bits(v[3])) << 16);
-    *(g_u32x2 *)p = u;
-  }
-};
-template <> struct Vec4St<float> {
-  static __device__ __forceinline__ void st(float *p, const float (&v)[4]) {
-    *(g_f32x4 *)p = f32x4{v[0], v[1], v[2], v[3]};
-  }
-};
 
 // M <- mu*M + G over one chunk; partial sum of U^2, U = M or G + mu*M.
 __global__ __launch_bounds__(kEwThreads) void momentum_sumsq_kernel(
@@ -129,54 +114,72 @@ __global__ __launch_bounds__(256) void finalize_norm_kernel(const MatDev *__rest
 //   U = M (or G + mu*M), its sum of squares into partials[group],
 //   U written unnormalised as X^T (n_p x m_p), zero in the padding.
 // A tall matrix is its own X^T: group t takes its contiguous elements
-// [4096 t, 4096 t + 4096) (long row runs keep HBM pages open).  Otherwise
+// [8192 t, 8192 t + 8192) (long row runs keep HBM pages open).  Otherwise
 // X^T = U^T and group t takes a 64 x 128 block of U, transposed through LDS,
 // so that M is read in 512-byte and X^T written in 128-byte row segments.
-// The 1/(||U||_F + eps) scale is applied by the first iteration's Gram and
-// Apply epilogues, so M is read once.
-// A thread's two four-element pieces are loaded before either is updated
-// (mom_load for both, then momentum4 for both), so that four HBM reads per
-// thread are in flight at once.
+// Every thread takes eight consecutive elements: M as two 16-byte vectors,
+// a bf16 G and a bf16 X^T segment as one.  The 1/(||U||_F + eps) scale is
+// applied by the first iteration's Gram and Apply epilogues, so M is read
+// once.
 struct MomPiece {
   int64_t ur, uc;
-  bool full;  // four valid elements with 16-byte aligned M: vector path
-  f32x4 m;
-  f32x4 g;
+  bool full;  // eight valid elements with 16-byte aligned M: vector path
+  f32x4 m[2];
+  f32x4 g[2];
 };
+
+// Eight consecutive bf16 or fp32 values at flat index i (i multiple of 4;
+// one 16-byte bf16 load when i is a multiple of 8).
+__device__ __forceinline__ void load_grad8(const void *g, int32_t dt, int64_t i, f32x4 (&r)[2]) {
+  if (dt == kBF16 && (i & 7) == 0) {
+    const vu32x4 v = *(const g_u32x4 *)(static_cast<const uint16_t *>(g) + i);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      r[h][0] = __uint_as_float(v[2 * h] << 16);
+      r[h][1] = __uint_as_float(v[2 * h] & 0xffff0000u);
+      r[h][2] = __uint_as_float(v[2 * h + 1] << 16);
+      r[h][3] = __uint_as_float(v[2 * h + 1] & 0xffff0000u);
+    }
+  } else {
+    r[0] = load_grad4(g, dt, i);
+    r[1] = load_grad4(g, dt, i + 4);
+  }
+}
 
 __device__ __forceinline__ MomPiece mom_load(const MatDev &d, int64_t ur, int64_t uc, bool vec) {
   MomPiece pc;
   pc.ur = ur;
   pc.uc = uc;
-  pc.full = vec && ur < d.rows && uc + 4 <= d.cols;
+  pc.full = vec && ur < d.rows && uc + 8 <= d.cols;
   if (pc.full) {
     const int64_t idx = ur * d.cols + uc;
-    pc.m = *(const g_f32x4 *)(d.mom + idx);
-    pc.g = load_grad4(d.grad, d.grad_dt, idx);
+    pc.m[0] = *(const g_f32x4 *)(d.mom + idx);
+    pc.m[1] = *(const g_f32x4 *)(d.mom + idx + 4);
+    load_grad8(d.grad, d.grad_dt, idx, pc.g);
   }
   return pc;
 }
 
-__device__ __forceinline__ void momentum4(const MatDev &d, const MomPiece &pc, float mu, bool nesterov,
-                                          float (&u)[4]) {
-  u[0] = u[1] = u[2] = u[3] = 0.f;
+__device__ __forceinline__ void momentum8(const MatDev &d, const MomPiece &pc, float mu, bool nesterov,
+                                          float (&u)[8]) {
+#pragma unroll
+  for (int k = 0; k < 8; ++k) u[k] = 0.f;
   if (pc.ur >= d.rows || pc.uc >= d.cols) return;
   const int64_t idx = pc.ur * d.cols + pc.uc;
   if (pc.full) {
-    f32x4 mv = pc.m;
-    const f32x4 g = pc.g;
-    mv.x = fmaf(mu, mv.x, g[0]);
-    mv.y = fmaf(mu, mv.y, g[1]);
-    mv.z = fmaf(mu, mv.z, g[2]);
-    mv.w = fmaf(mu, mv.w, g[3]);
-    *(g_f32x4 *)(d.mom + idx) = mv;
-    u[0] = mv.x; u[1] = mv.y; u[2] = mv.z; u[3] = mv.w;
-    if (nesterov)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) u[k] = fmaf(mu, u[k], g[k]);
+    for (int h = 0; h < 2; ++h) {
+      f32x4 mv = pc.m[h];
+      const f32x4 g = pc.g[h];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) mv[k] = fmaf(mu, mv[k], g[k]);
+      *(g_f32x4 *)(d.mom + idx + 4 * h) = mv;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) u[4 * h + k] = nesterov ? fmaf(mu, mv[k], g[k]) : mv[k];
+    }
   } else {
     g_f32 *const mom = (g_f32 *)d.mom;
-    for (int k = 0; k < 4 && pc.uc + k < d.cols; ++k) {
+    for (int k = 0; k < 8 && pc.uc + k < d.cols; ++k) {
       const float g = load_elem(d.grad, d.grad_dt, idx + k);
       const float m = fmaf(mu, mom[idx + k], g);
       mom[idx + k] = m;
@@ -185,20 +188,36 @@ __device__ __forceinline__ void momentum4(const MatDev &d, const MomPiece &pc, f
   }
 }
 
-// Four consecutive elements of X^T in the matrix's workspace type: bf16, or
-// fp32 (the fp32 mode, and small matrices in a bf16 step).
-__device__ __forceinline__ void store_xt4(const MatDev &d, int64_t idx, const float (&u)[4]) {
-  if (d.ws_f32)
-    Vec4St<float>::st(static_cast<float *>(d.xt[0]) + idx, u);
-  else
-    Vec4St<uint16_t>::st(static_cast<uint16_t *>(d.xt[0]) + idx, u);
+// Eight consecutive elements of X^T in the matrix's workspace type: one
+// 16-byte bf16 store, or two fp32 ones (the fp32 mode, and small matrices in
+// a bf16 step).  idx is a multiple of 8.
+__device__ __forceinline__ void store_xt8(const MatDev &d, int64_t idx, const float (&u)[8]) {
+  if (d.ws_f32) {
+    float *const p = static_cast<float *>(d.xt[0]) + idx;
+    *(g_f32x4 *)p = f32x4{u[0], u[1], u[2], u[3]};
+    *(g_f32x4 *)(p + 4) = f32x4{u[4], u[5], u[6], u[7]};
+  } else {
+    vu32x4 v;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      v[k] = f32_to_bf16_bits(u[2 * k]) | (static_cast<uint32_t>(f32_to_bf16_bits(u[2 * k + 1])) << 16);
+    *(g_u32x4 *)(static_cast<uint16_t *>(d.xt[0]) + idx) = v;
+  }
 }
+
+// The transpose tile: U[i0 + r][j0 + c] at LDS word r * kTrStride + c +
+// 4 * (c / 64).  A row write (16 lanes per row, eight columns each, four
+// rows per instruction) and a column read (eight lanes per column, eight
+// rows each) then touch 64 distinct banks: the stride is 1 mod 8, and the
+// four-word gap shifts the columns 64-127 of a row by half a bank octet.
+constexpr int kTrStride = 137;
+__device__ __forceinline__ int tr_pos(int r, int c) { return r * kTrStride + c + ((c >> 6) << 2); }
 
 __global__ __launch_bounds__(kOrientThreads) void momentum_orient_kernel(
     const MatDev *__restrict__ mats, int32_t nmat, StepScalars s) {
   constexpr int TT = static_cast<int>(kTrTile);
-  static_assert(TT * TT == kOrientThreads * 4, "four elements per thread and tile");
-  __shared__ float tile[TT][2 * TT + 1];
+  static_assert(2 * TT * TT == kOrientThreads * 8, "eight elements per thread and group");
+  __shared__ float tile[TT * kTrStride];
   __shared__ double red[kOrientThreads / 64];
   const int64_t w = blockIdx.x;
   const int32_t mi = find_range(nmat, w, [&](int32_t i) { return mats[i].tr_first; });
@@ -208,54 +227,36 @@ __global__ __launch_bounds__(kOrientThreads) void momentum_orient_kernel(
   const int tid = threadIdx.x;
   const bool vec = (d.cols & 3) == 0;  // rows of M start 16-byte aligned
   double acc = 0.0;
+  float u[8];
   if (d.transposed) {
-    // 8192 contiguous elements of X^T per group: two runs of 4096, four
-    // elements per thread in each (a run lies within one row: m_p is a
-    // multiple of 256)
-    MomPiece pc[2];
+    // 8192 contiguous elements of X^T per group, eight per thread (a run
+    // of eight lies within one row: m_p is a multiple of 256)
+    const int64_t e0 = t * (2 * TT * TT) + 8 * tid;
+    const MomPiece pc = mom_load(d, e0 / d.mp, e0 % d.mp, vec);
+    momentum8(d, pc, mu, s.nesterov, u);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t e0 = t * (2 * TT * TT) + h * (TT * TT) + 4 * tid;
-      pc[h] = mom_load(d, e0 / d.mp, e0 % d.mp, vec);
-    }
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t e0 = t * (2 * TT * TT) + h * (TT * TT) + 4 * tid;
-      float u[4];
-      momentum4(d, pc[h], mu, s.nesterov, u);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) acc += (double)u[k] * u[k];
-      store_xt4(d, e0, u);  // X^T[ur][uc .. uc+3], zeros in the padding
-    }
+    for (int k = 0; k < 8; ++k) acc += (double)u[k] * u[k];
+    store_xt8(d, e0, u);  // X^T[ur][uc .. uc+7], zeros in the padding
   } else {
     // block rows i0 .. i0+63 (m), columns j0 .. j0+127 (n); thread: row p,
-    // columns q and q + 64 (4 each)
+    // columns q .. q+7
     const int64_t blocks_n = d.np / (2 * TT);
     const int64_t i0 = (t / blocks_n) * TT, j0 = (t % blocks_n) * (2 * TT);
-    const int p = tid >> 4, q = (tid & 15) * 4;
-    MomPiece pc[2];
+    const int p = tid >> 4, q = (tid & 15) * 8;
+    const MomPiece pc = mom_load(d, i0 + p, j0 + q, vec);
+    momentum8(d, pc, mu, s.nesterov, u);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) pc[h] = mom_load(d, i0 + p, j0 + h * TT + q, vec);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float u[4];
-      momentum4(d, pc[h], mu, s.nesterov, u);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        tile[p][h * TT + q + k] = u[k];
-        acc += (double)u[k] * u[k];
-      }
+    for (int k = 0; k < 8; ++k) {
+      tile[tr_pos(p, q) + k] = u[k];
+      acc += (double)u[k] * u[k];
     }
     __syncthreads();
-    // X^T rows j0 + a (a < 128), elements i0 + b .. b+3
+    // X^T row j0 + a (a < 128), elements i0 + b .. b+7
+    const int a = tid >> 3, b = (tid & 7) * 8;
+    float vt[8];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int a = (tid >> 4) + h * TT, b = (tid & 15) * 4;
-      float vt[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) vt[k] = tile[b + k][a];
-      store_xt4(d, (j0 + a) * d.mp + i0 + b, vt);
-    }
+    for (int k = 0; k < 8; ++k) vt[k] = tile[tr_pos(b + k, a)];
+    store_xt8(d, (j0 + a) * d.mp + i0 + b, vt);
   }
   const double tot = block_sum_f64(acc, red);
   if (tid == 0) ((__attribute__((address_space(1))) double *)d.partials)[t] = tot;
