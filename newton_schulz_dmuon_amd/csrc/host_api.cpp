@@ -710,8 +710,9 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
     std::vector<int64_t> steps;
     for (const TileEntry &e : p.lists[l.list]) steps.push_back(rs[e.mat]);
     // a bf16 Square launch with too few 256-tiles for the CUs runs 128-tiles
-    // where the list-schedule estimate says they finish sooner
-    if (l.kind == kLkSquare && !l.fp32) {
+    // where the list-schedule estimate says they finish sooner (a 128-tile
+    // list enters the plan, and the workspace, only when taken)
+    if (l.kind == kLkSquare && !l.fp32 && static_cast<int64_t>(steps.size()) < kCUs) {
       std::vector<int32_t> key128 = key;
       key128.push_back(128);
       auto l128 = list_of.find(key128);
@@ -724,14 +725,18 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
             passes.push_back(key[q + 1]);
             stages.push_back(key[q + 2]);
           }
-        p.lists.emplace_back();
-        p.list_xcd.emplace_back();
-        cached_stage_tiles(shapes, passes, stages, 128, p.lists.back(), p.list_xcd.back());
-        l128 = list_of.emplace(key128, static_cast<int32_t>(p.lists.size()) - 1).first;
+        std::vector<TileEntry> t128;
+        StageXcd x128;
+        cached_stage_tiles(shapes, passes, stages, 128, t128, x128);
+        std::vector<int64_t> steps128;
+        for (const TileEntry &e : t128) steps128.push_back(rs[e.mat]);
+        if (small_tiles_pay(steps, steps128)) {
+          p.lists.push_back(std::move(t128));
+          p.list_xcd.push_back(x128);
+          l128 = list_of.emplace(key128, static_cast<int32_t>(p.lists.size()) - 1).first;
+        }
       }
-      std::vector<int64_t> steps128;
-      for (const TileEntry &e : p.lists[l128->second]) steps128.push_back(rs[e.mat]);
-      if (small_tiles_pay(steps, steps128)) {
+      if (l128 != list_of.end()) {
         l.tile = 128;
         l.list = l128->second;
         p.prog.push_back(std::move(l));
