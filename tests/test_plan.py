@@ -174,6 +174,9 @@ def test_step_launches_errors():
     out = (_lib.LaunchInfo * 4)()
     assert lib.dmuon_step_launches(arr, 1, ctypes.byref(cfg), out, 4, ctypes.byref(cnt)) == _lib.OK
     assert cnt.value == 17 and [out[j].kind for j in range(4)] == [1, 2, 4, 5]
+    # element-wise launches report no tile; an 8 x 8 matrix runs its chain
+    # in fp32 on 256-tiles
+    assert [out[j].tile for j in range(4)] == [0, 0, 256, 256]
 
 
 @pytest.mark.parametrize("seed", range(12))
@@ -302,7 +305,8 @@ def test_nonfinite_flags_offset():
 
 def test_launch_info_layout_matches_header():
     assert ctypes.sizeof(_lib.LaunchInfo) == 16
-    assert _lib.LaunchInfo.kind.offset == 0 and _lib.LaunchInfo.flops.offset == 8
+    assert _lib.LaunchInfo.kind.offset == 0 and _lib.LaunchInfo.tile.offset == 4
+    assert _lib.LaunchInfo.flops.offset == 8
 
 
 def test_gram_and_square_launches_of_the_two_chains_merge():
