@@ -334,3 +334,51 @@ def test_gram_and_square_launches_of_the_two_chains_merge():
     # split launches of every kind stay well formed
     for shapes in (LLAMA8B_OWNER0, [(513, 513), (300, 700), (700, 300), (256, 1024)]):
         check_split_launches(nsd.step_launches(shapes, nsd.StepOptions(gram_ns=True)))
+
+
+def test_concurrent_host_calls_agree():
+    """The planner's tile-list cache is shared by every caller (a mutex
+    guards it, and a full cache is cleared): host threads planning
+    different shape sets at once, more sets than the cache holds, get
+    the same launch sequences and workspace sizes as one thread alone."""
+    import threading
+    import numpy as np
+    rng = np.random.default_rng(7)
+    sets = []
+    for _ in range(80):
+        n = int(rng.integers(1, 8))
+        sets.append([(int(rng.choice([17, 300, 513, 1024, 1536, 4096])),
+                      int(rng.choice([33, 256, 700, 1536, 4096, 8960]))) for _ in range(n)])
+    opts = [nsd.StepOptions(gram_ns=g, ns_steps=k) for g in (False, True) for k in (5, 8)]
+
+    def plan(shapes, o):
+        L = nsd.step_launches(shapes, o, tiles=True)
+        arr = (_lib.Matrix * len(shapes))()
+        for i, (r, c) in enumerate(shapes):
+            arr[i] = _lib.Matrix(None, 0, 0, None, None, None, r, c, 1.0, 0, 0)
+        out = ctypes.c_size_t(0)
+        cfg = o.to_c()
+        _lib.check(_lib.load().dmuon_workspace_bytes(arr, len(shapes), ctypes.byref(cfg), ctypes.byref(out)))
+        return L, out.value
+
+    want = {(i, j): plan(s, o) for i, s in enumerate(sets) for j, o in enumerate(opts)}
+    got, errors = {}, []
+
+    def worker(t):
+        try:
+            for rep in range(3):
+                for i in range(t % 5, len(sets), 5):
+                    for j, o in enumerate(opts):
+                        got[(t, rep, i, j)] = plan(sets[i], o)
+        except Exception as e:  # noqa: BLE001 (reported below)
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(8)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors, errors
+    assert len(got) == 8 * 3 * 16 * len(opts)
+    for (t, rep, i, j), v in got.items():
+        assert v == want[(i, j)], (t, rep, sets[i], j)
