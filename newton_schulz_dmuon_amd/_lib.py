@@ -9,7 +9,10 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdmuon.so")
+# DMUON_LIB names another build of the same library (for instance the one
+# with sanitized host code); by default the one built next to this file
+LIB_PATH = os.environ.get("DMUON_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                       "libdmuon.so")
 
 ABI_VERSION = 1
 
