@@ -227,6 +227,8 @@ def main(argv=None) -> int:
     ap.add_argument("--repeat", type=int, default=1, help="copies of each --shape")
     ap.add_argument("--ns-steps", type=int, default=None)
     ap.add_argument("--fp32-ns", action="store_true", help="fp32 checking mode")
+    ap.add_argument("--chain-launch", action="store_true",
+                    help="every bf16 product of the step in one dependency-driven launch")
     ap.add_argument("--direct-ns", action="store_true",
                     help="direct chain for every matrix (default: Gram-space chain where n >= 2m, ns_steps >= 5)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -276,7 +278,8 @@ def main(argv=None) -> int:
         P.append((torch.randn(r, c, generator=gen, device=dev) * w.param_std).to(pdt))
         M.append(torch.zeros(r, c, dtype=torch.float32, device=dev))
     scales = [update_scale(r, c) for _, r, c in shapes]
-    opts = nsd.StepOptions(ns_steps=K, ns_fp32=args.fp32_ns, gram_ns=not args.direct_ns)
+    opts = nsd.StepOptions(ns_steps=K, ns_fp32=args.fp32_ns, gram_ns=not args.direct_ns,
+                           chain_launch=args.chain_launch)
     ws = nsd.Workspace()
     ws_bytes = nsd.workspace_bytes(P, opts)
     wsbuf = ws.get(ws_bytes, dev)
@@ -339,7 +342,7 @@ def main(argv=None) -> int:
             flops[kk] += v
     ns_total = sum(flops.values())
     executed = sum(f for _, f in launches)
-    gemm_kinds = ("gram", "square", "gram_square", "apply", "final")
+    gemm_kinds = ("gram", "square", "gram_square", "apply", "final", "chain")
     ns_ms = sum(sum(v) for nm, v in per.items() if nm in gemm_kinds) / args.steps
     peak = PEAK_FP32_TFLOPS if args.fp32_ns else PEAK_BF16_TFLOPS
     value = ns_total / (ms * 1e-3) / 1e12
@@ -380,7 +383,8 @@ def main(argv=None) -> int:
                   "square": "ns_gemm_kernel<Square> (symmetric m x m products)",
                   "gram_square": "ns_gemm_kernel<GramSquare> (Gram and Square tiles of different matrices)",
                   "apply": "ns_gemm_kernel<Apply> (X <- aX + BX / X <- QX)",
-                  "final": "ns_gemm_kernel<Final> (last apply + update)"}[dom]
+                  "final": "ns_gemm_kernel<Final> (last apply + update)",
+                  "chain": "ns_gemm_chain_kernel (every bf16 stage, one launch)"}[dom]
         roofline = {"bound": "mfma", "kernel": kernel,
                     "achieved": round(ach, 2), "peak": peak, "unit": "TFLOP/s",
                     "frac": round(ach / peak, 4),
@@ -394,7 +398,7 @@ def main(argv=None) -> int:
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32" if args.fp32_ns else "bf16", "data": "synthetic",
         "config": {"workload": w.name, "matrices": len(shapes), "elements": elem,
-                   "ns_steps": K, "gram_ns": opts.gram_ns,
+                   "ns_steps": K, "gram_ns": opts.gram_ns, "chain_launch": opts.chain_launch,
                    "param_dtype": w.param_dtype, "grad_dtype": w.grad_dtype,
                    "parallelism": "one owner's share on 1 GPU"},
         # MFMA use: the executed flops over the step, as a share of the

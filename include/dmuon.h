@@ -98,7 +98,22 @@ enum {
    * one int32 per matrix (1 or 0) in the workspace, at the offset
    * dmuon_nonfinite_flags_offset() gives.  It only reports: non-finite
    * values still propagate through that matrix's step, as without it. */
-  DMUON_FLAG_CHECK_FINITE = 1u << 3
+  DMUON_FLAG_CHECK_FINITE = 1u << 3,
+  /* Run every bf16 Newton-Schulz product of the step as one dependency-
+   * driven launch (this library's own design; the pages describe no kernel
+   * structure): each matrix's tiles
+   * of all its stages go to one XCD, whose work-groups take them in stage
+   * order and wait, per matrix, for the previous stage's tiles; no launch
+   * boundary separates stages.  Same tile code as the grouped launches
+   * (256 x 256 tiles, no split K, no 128-tiles), so results match the
+   * grouped launches bit for bit where those use whole 256-tiles.
+   * Matrices that run their chain in fp32 keep their grouped launches.  A
+   * wait that exceeds about a second gives up (the result is then wrong, the
+   * step always ends).  Off by default: pinning each matrix to one XCD
+   * makes the XCDs stream different matrices at once, and on the
+   * Llama-3.1-8B owner share the step is about 28% slower than with the
+   * grouped launches even with every wait removed. */
+  DMUON_FLAG_CHAIN_LAUNCH = 1u << 4
 };
 
 /* Launch kinds reported by dmuon_step_launches. */
@@ -111,8 +126,10 @@ enum {
   DMUON_LAUNCH_SQUARE = 5,          /* symmetric m x m product (+ bA + diag)    */
   DMUON_LAUNCH_APPLY = 6,           /* X <- aX + BX (Gram-space: X <- Q X)      */
   DMUON_LAUNCH_FINAL = 7,           /* last apply + parameter update            */
-  DMUON_LAUNCH_GRAM_SQUARE = 8      /* Gram tiles of some matrices and Square
+  DMUON_LAUNCH_GRAM_SQUARE = 8,     /* Gram tiles of some matrices and Square
                                        tiles of others, in one launch          */
+  DMUON_LAUNCH_CHAIN = 9            /* DMUON_FLAG_CHAIN_LAUNCH: every bf16
+                                       product of the step, one launch         */
 };
 
 /* One launch of a step, as dmuon_step_launches describes it. */

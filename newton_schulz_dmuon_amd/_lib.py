@@ -32,10 +32,11 @@ FLAG_NS_FP32 = 1 << 0
 FLAG_NESTEROV = 1 << 1
 FLAG_GRAM_NS = 1 << 2
 FLAG_CHECK_FINITE = 1 << 3
+FLAG_CHAIN_LAUNCH = 1 << 4
 
 # dmuon_launch_info.kind
 LAUNCH_KINDS = ("momentum_sumsq", "momentum_orient", "norm", "update_direct", "gram", "square",
-                "apply", "final", "gram_square")
+                "apply", "final", "gram_square", "chain")
 
 EXPORTED = ("dmuon_abi_version", "dmuon_error_string", "dmuon_last_error",
             "dmuon_partition_lpt", "dmuon_pack_offsets", "dmuon_workspace_bytes",

@@ -73,12 +73,16 @@ class StepOptions:
     gram_ns: bool = False
     # record per matrix whether U holds a NaN or an Inf (nonfinite_flags)
     check_finite: bool = False
+    # every bf16 product of the step in one dependency-driven launch (see
+    # DMUON_FLAG_CHAIN_LAUNCH)
+    chain_launch: bool = False
 
     def to_c(self) -> StepConfig:
         flags = (_lib.FLAG_NESTEROV if self.nesterov else 0) | \
                 (_lib.FLAG_NS_FP32 if self.ns_fp32 else 0) | \
                 (_lib.FLAG_GRAM_NS if self.gram_ns else 0) | \
-                (_lib.FLAG_CHECK_FINITE if self.check_finite else 0)
+                (_lib.FLAG_CHECK_FINITE if self.check_finite else 0) | \
+                (_lib.FLAG_CHAIN_LAUNCH if self.chain_launch else 0)
         return StepConfig(self.a, self.b, self.c, int(self.ns_steps), self.lr,
                           self.momentum, self.eps, flags)
 

@@ -348,6 +348,13 @@ __global__ __launch_bounds__(kEwThreads) void adamw_kernel(AdamBatch b, AdamScal
   }
 }
 
+// Zeroes n int32 (the chained mode's tickets and counters): a kernel, so
+// that a captured step records no memset node.
+__global__ __launch_bounds__(256) void zero_i32_kernel(int32_t *__restrict__ p, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) ((__attribute__((address_space(1))) int32_t *)p)[i] = 0;
+}
+
 constexpr int kPackThreads = 256;
 
 // Byte copies of a batch of matrices; 16-byte vectors for the body, bytes
@@ -377,6 +384,12 @@ hipError_t launch_momentum_sumsq(const MatDev *mats, int32_t nmat, int64_t total
 
 hipError_t launch_finalize_norm(const MatDev *mats, int32_t nmat, float eps, hipStream_t st) {
   hipLaunchKernelGGL(finalize_norm_kernel, dim3((uint32_t)nmat), dim3(256), 0, st, mats, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_i32(int32_t *p, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(zero_i32_kernel, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, st, p, n);
   return hipGetLastError();
 }
 

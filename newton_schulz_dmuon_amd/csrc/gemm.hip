@@ -1040,6 +1040,75 @@ void ns_gemm_small_kernel(const MatDev *__restrict__ mats, const TileEntry *__re
   gemm_tile<uint16_t, kModeSquare, kRoleWhole, 128>(lds, mats[e.mat], e, s, nullptr);
 }
 
+// One launch for all bf16 stages of a step (the chained mode).  Every matrix
+// has all of its tiles, of every stage, in one XCD's queue, in the order of
+// the stages; a work-group takes the next entry of its own XCD's queue (the
+// hardware XCC id picks the queue), waits until the previous stage of that
+// matrix has signalled all its tiles, runs the tile with its stage's code and
+// signals.  An entry waits only on entries earlier in the same queue, which
+// running work-groups took before it, so every wait ends; a wait that has not
+// ended after kChainSpinLimit polls sets the timeout word and goes on (wrong
+// values, never a hang).  Producer and consumer share the XCD's L2: the
+// producer's stores have reached it (vmcnt) before it signals, and the
+// consumer drops its CU's L1 lines before it reads.
+// Entry fields: k0 = counter waited on (-1: none), k1 = the count it waits
+// for, slot = counter signalled.  sync: kXcds tickets, the timeout word at
+// kXcds, counters from kChainCounters.
+constexpr int32_t kChainSpinLimit = 1 << 20;
+
+__device__ __forceinline__ int32_t xcc_id() {
+  int32_t v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID, 0, 4)" : "=s"(v));
+  return v;
+}
+
+__global__ __launch_bounds__(kThreads) void ns_gemm_chain_kernel(const MatDev *__restrict__ mats,
+                                                                 const TileEntry *__restrict__ tiles, StageXcd xcd,
+                                                                 StepScalars s, int32_t *__restrict__ sync) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * kStageBytes];
+  __shared__ int32_t ticket;
+  lds_char *const lds = (lds_char *)smem;
+  const int32_t xi = xcc_id() & (kXcds - 1);
+  if (threadIdx.x == 0) ticket = __hip_atomic_fetch_add(sync + xi, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int32_t k = ticket;
+  if (k >= xcd.count[xi]) return;  // the whole group leaves
+  const TileEntry e = tiles[xcd.first[xi] + k];
+  if (e.k0 >= 0) {
+    if (threadIdx.x == 0) {
+      int32_t *const c = sync + kChainCounters + e.k0;
+      for (int32_t spins = 0; __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < e.k1;) {
+        __builtin_amdgcn_s_sleep(8);
+        if (++spins == kChainSpinLimit) {
+          __hip_atomic_store(sync + kXcds, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+    }
+    __syncthreads();
+    asm volatile("buffer_inv sc0\n\ts_waitcnt vmcnt(0)" ::: "memory");
+  }
+  const MatDev &d = mats[e.mat];
+  switch (d.gemm_kind) {
+    case kModeGram:
+      gemm_tile<uint16_t, kModeGram, kRoleWhole>(lds, d, e, s, nullptr);
+      break;
+    case kModeSquare:
+      gemm_tile<uint16_t, kModeSquare, kRoleWhole>(lds, d, e, s, nullptr);
+      break;
+    case kModeApply:
+      gemm_tile<uint16_t, kModeApply, kRoleWhole>(lds, d, e, s, nullptr);
+      break;
+    default:
+      gemm_tile<uint16_t, kModeFinal, kRoleWhole>(lds, d, e, s, nullptr);
+      break;
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores have reached L2
+  __syncthreads();
+  if (threadIdx.x == 0)
+    __hip_atomic_fetch_add(sync + kChainCounters + e.slot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <typename T, int ROLE>
 hipError_t launch_role(GemmMode mode, const MatDev *mats, const TileEntry *tiles, const StageXcd &xcd,
                        StepScalars s, f32x4 *splitk, hipStream_t st) {
@@ -1088,6 +1157,16 @@ hipError_t launch_ns_small_square(const MatDev *mats, const TileEntry *tiles, co
   if (longest == 0) return hipSuccess;
   const dim3 grid(static_cast<uint32_t>(longest) * kXcds), block(kThreads);
   hipLaunchKernelGGL(ns_gemm_small_kernel, grid, block, 0, st, mats, tiles, xcd, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_ns_chain(const MatDev *mats, const TileEntry *tiles, const StageXcd &xcd, StepScalars s,
+                           int32_t *sync, hipStream_t st) {
+  int32_t longest = 0;
+  for (int x = 0; x < kXcds; ++x) longest = xcd.count[x] > longest ? xcd.count[x] : longest;
+  if (longest == 0) return hipSuccess;
+  const dim3 grid(static_cast<uint32_t>(longest) * kXcds), block(kThreads);
+  hipLaunchKernelGGL(ns_gemm_chain_kernel, grid, block, 0, st, mats, tiles, xcd, s, sync);
   return hipGetLastError();
 }
 

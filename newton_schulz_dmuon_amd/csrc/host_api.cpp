@@ -91,7 +91,8 @@ int validate_config(const dmuon_step_config *cfg) {
   for (float v : vals)
     if (!std::isfinite(v)) return fail(DMUON_ERR_INVALID_ARG, "non-finite step coefficient");
   if (cfg->eps < 0.f) return fail(DMUON_ERR_INVALID_ARG, "eps < 0");
-  const uint32_t known = DMUON_FLAG_NS_FP32 | DMUON_FLAG_NESTEROV | DMUON_FLAG_GRAM_NS | DMUON_FLAG_CHECK_FINITE;
+  const uint32_t known = DMUON_FLAG_NS_FP32 | DMUON_FLAG_NESTEROV | DMUON_FLAG_GRAM_NS | DMUON_FLAG_CHECK_FINITE |
+                         DMUON_FLAG_CHAIN_LAUNCH;
   if (cfg->flags & ~known) return fail(DMUON_ERR_INVALID_ARG, "unknown flag bits 0x%x", cfg->flags & ~known);
   return DMUON_OK;
 }
@@ -133,7 +134,8 @@ enum LaunchKind : int32_t {
   kLkSquare = DMUON_LAUNCH_SQUARE,
   kLkApply = DMUON_LAUNCH_APPLY,
   kLkFinal = DMUON_LAUNCH_FINAL,
-  kLkGramSquare = DMUON_LAUNCH_GRAM_SQUARE  // parts of kinds Gram and Square
+  kLkGramSquare = DMUON_LAUNCH_GRAM_SQUARE,  // parts of kinds Gram and Square
+  kLkChain = DMUON_LAUNCH_CHAIN              // every bf16 part of the step
 };
 
 // Workspace buffers a GEMM launch can name per matrix: the direct chain uses
@@ -201,6 +203,7 @@ struct Plan {
   std::vector<int64_t> off_table, off_list;
   int64_t off_partials = 0, off_inv = 0, off_flags = -1;
   int64_t off_splitk = -1, splitk_slots = 0;  // partial slots of split tiles
+  int64_t off_chain = -1, chain_counters = 0;  // chained mode: tickets, timeout, counters
   int64_t table_bytes = 0;  // [0, table_bytes) is uploaded
   int64_t total_bytes = 0;
 };
@@ -470,6 +473,115 @@ bool small_fp32(const MatDev &d, const dmuon_step_config &cfg) {
   return !(cfg.flags & DMUON_FLAG_NS_FP32) && d.m < kFp32BelowM;
 }
 
+// The chained mode (DMUON_FLAG_CHAIN_LAUNCH): the bf16 launches of the
+// merged program become one launch.  Its table is the launches' tables one
+// after the other, so row r is one matrix at one stage.  Each matrix goes,
+// with all its stages, to one XCD (largest total work first, to the XCD with
+// the least so far); an XCD's queue holds its matrices' tiles in program
+// order (launch by launch; a stage's tiles in the blocks of
+// build_stage_tiles).  Entry fields: k0 = the counter of the matrix's
+// previous launch (-1 for its first), k1 = that launch's tile count for the
+// matrix, slot = the counter of this launch for the matrix.  All of a
+// matrix's rows in one launch (Square launches can hold two parts of it)
+// signal one counter.
+void chain_launch(Plan &p, const std::vector<Launch> &in_chain) {
+  Launch c;
+  c.kind = kLkChain;
+  for (const Launch &l : in_chain) {
+    c.parts.insert(c.parts.end(), l.parts.begin(), l.parts.end());
+    c.flops += l.flops;
+  }
+  p.tables.push_back(c.parts);
+  c.table = static_cast<int32_t>(p.tables.size());
+  const std::vector<int64_t> rs = row_steps(p, c);
+  struct Row {
+    int32_t row, mat, launch;
+    bool sym;
+  };
+  std::vector<Row> rows;
+  for (size_t j = 0; j < in_chain.size(); ++j)
+    for (const Part &pt : in_chain[j].parts)
+      for (int32_t i : p.groups[pt.group])
+        rows.push_back(Row{static_cast<int32_t>(rows.size()), i, static_cast<int32_t>(j),
+                           pt.kind == kLkGram || pt.kind == kLkSquare});
+  auto tiles_of = [&](const Row &r) {
+    const MatDev &d = p.mats[r.mat];
+    return r.sym ? static_cast<int64_t>(d.tm) * (d.tm + 1) / 2 : static_cast<int64_t>(d.tm) * d.tn;
+  };
+  // owner XCD of every matrix, by total work
+  const int32_t n = static_cast<int32_t>(p.mats.size());
+  std::vector<int64_t> work(n, 0);
+  for (const Row &r : rows) work[r.mat] += tiles_of(r) * rs[r.row];
+  std::vector<int32_t> order;
+  for (int32_t i = 0; i < n; ++i)
+    if (work[i] > 0) order.push_back(i);
+  std::stable_sort(order.begin(), order.end(), [&](int32_t a, int32_t b) { return work[a] > work[b]; });
+  std::vector<int32_t> owner(n, -1);
+  int64_t load[kXcds] = {0};
+  for (int32_t i : order) {
+    int x = 0;
+    for (int y = 1; y < kXcds; ++y)
+      if (load[y] < load[x]) x = y;
+    load[x] += work[i];
+    owner[i] = x;
+  }
+  // counters: one per (matrix, launch); each row waits on its matrix's
+  // previous launch
+  std::map<std::pair<int32_t, int32_t>, int32_t> counter;
+  std::map<int32_t, int64_t> tiles_in;  // counter -> tiles that signal it
+  std::vector<int32_t> last(n, -1);     // the matrix's latest counter so far
+  std::vector<int32_t> wait_on(rows.size(), -1), sig(rows.size(), -1);
+  for (const Row &r : rows) {
+    auto key = std::make_pair(r.mat, r.launch);
+    auto it = counter.find(key);
+    if (it == counter.end()) {
+      wait_on[r.row] = last[r.mat];
+      it = counter.emplace(key, static_cast<int32_t>(counter.size())).first;
+      last[r.mat] = it->second;
+    } else {
+      // a second row of the matrix in the same launch waits as the first did
+      for (const Row &q : rows)
+        if (q.row < r.row && q.mat == r.mat && q.launch == r.launch) {
+          wait_on[r.row] = wait_on[q.row];
+          break;
+        }
+    }
+    sig[r.row] = it->second;
+    tiles_in[it->second] += tiles_of(r);
+  }
+  p.chain_counters = static_cast<int64_t>(counter.size());
+  std::vector<TileEntry> lists[kXcds];
+  for (const Row &r : rows) {
+    const MatDev &d = p.mats[r.mat];
+    const int32_t bm = 4, bn = r.sym ? 4 : 8;
+    const int32_t rows_t = d.tm, cols_t = r.sym ? d.tm : d.tn;
+    const int32_t w = wait_on[r.row];
+    const int32_t need = w >= 0 ? static_cast<int32_t>(tiles_in[w]) : 0;
+    for (int32_t bi = 0; bi < rows_t; bi += bm)
+      for (int32_t bj = r.sym ? bi : 0; bj < cols_t; bj += bn)
+        for (int32_t ti = bi; ti < std::min(bi + bm, rows_t); ++ti)
+          for (int32_t tj = bj; tj < std::min(bj + bn, cols_t); ++tj)
+            if (!r.sym || tj >= ti) {
+              TileEntry e{r.row, static_cast<uint16_t>(ti), static_cast<uint16_t>(tj)};
+              e.k0 = w;
+              e.k1 = need;
+              e.slot = sig[r.row];
+              lists[owner[r.mat]].push_back(e);
+            }
+  }
+  p.lists.emplace_back();
+  p.list_xcd.emplace_back();
+  std::vector<TileEntry> &out = p.lists.back();
+  StageXcd &xcd = p.list_xcd.back();
+  for (int x = 0; x < kXcds; ++x) {
+    xcd.first[x] = static_cast<int32_t>(out.size());
+    xcd.count[x] = static_cast<int32_t>(lists[x].size());
+    out.insert(out.end(), lists[x].begin(), lists[x].end());
+  }
+  c.list = static_cast<int32_t>(p.lists.size()) - 1;
+  p.prog.push_back(std::move(c));
+}
+
 void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg, char *ws,
                 Plan &p) {
   const bool fp32 = cfg.flags & DMUON_FLAG_NS_FP32;
@@ -674,6 +786,13 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
     p.prog.push_back(Launch{kLkMomentumOrient});
     p.prog.push_back(Launch{kLkNorm});
   }
+  p.chain_counters = 0;
+  if ((cfg.flags & DMUON_FLAG_CHAIN_LAUNCH) && K > 0) {
+    std::vector<Launch> rest, in_chain;
+    for (Launch &l : merged) (l.fp32 ? rest : in_chain).push_back(std::move(l));
+    if (!in_chain.empty()) chain_launch(p, in_chain);
+    merged = std::move(rest);
+  }
   // tables and tile lists, shared by launches with equal parts / groups
   std::map<std::vector<Part>, int32_t> table_of;
   std::map<std::vector<int32_t>, int32_t> list_of;
@@ -814,6 +933,11 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
     p.off_flags = off;
     off = round_up(off + 4 * int64_t(n), 256);
   }
+  p.off_chain = -1;
+  if (p.chain_counters > 0) {  // tickets, timeout word, counters
+    p.off_chain = off;
+    off = round_up(off + 4 * (kChainCounters + p.chain_counters), 256);
+  }
   for (int32_t i = 0; i < n; ++i) {
     MatDev &d = p.mats[i];
     // sum-of-squares partials: one per orientation tile, or per flat chunk
@@ -855,6 +979,41 @@ void build_plan(const dmuon_matrix *in, int32_t n, const dmuon_step_config &cfg,
   p.total_bytes = off;
 }
 
+// The chained launch's waits: every entry waits (k0 >= 0) only for a
+// counter whose k1 signalling entries all sit earlier in the same XCD's
+// queue, so that the work-groups holding them took their tickets first and
+// are running; counters are signalled only by entries of one XCD.
+bool chain_consistent(const Plan &p, const Launch &l) {
+  if (l.role != 0 || l.tile != 256 || l.fp32 || p.off_chain < 0) return false;
+  const std::vector<TileEntry> &tl = p.lists[l.list];
+  const StageXcd &xcd = p.list_xcd[l.list];
+  const int64_t nc = p.chain_counters;
+  std::vector<int64_t> total(nc, 0);
+  std::vector<int32_t> xcd_of(nc, -1);
+  for (int x = 0; x < kXcds; ++x)
+    for (int32_t q = xcd.first[x]; q < xcd.first[x] + xcd.count[x]; ++q) {
+      const TileEntry &e = tl[q];
+      if (e.slot < 0 || e.slot >= nc) return false;
+      if (xcd_of[e.slot] >= 0 && xcd_of[e.slot] != x) return false;
+      xcd_of[e.slot] = x;
+      ++total[e.slot];
+    }
+  for (int x = 0; x < kXcds; ++x) {
+    std::vector<int64_t> seen(nc, 0);
+    for (int32_t q = xcd.first[x]; q < xcd.first[x] + xcd.count[x]; ++q) {
+      const TileEntry &e = tl[q];
+      if (e.k0 >= 0) {
+        if (e.k0 >= nc || xcd_of[e.k0] != x || e.k1 != total[e.k0] || seen[e.k0] != total[e.k0]) return false;
+        if (e.k0 == e.slot) return false;
+      } else if (e.k0 != -1) {
+        return false;
+      }
+      ++seen[e.slot];
+    }
+  }
+  return true;
+}
+
 // Internal consistency of a plan, checked on the host before any launch:
 // every tile of every GEMM launch names a matrix of that launch's table and
 // a tile inside it (upper triangle for the symmetric stages), and each
@@ -870,7 +1029,10 @@ bool plan_consistent(const Plan &p) {
       if (pt.group < 0 || pt.group > 2) return false;
       // a part runs its launch's stage; a mixed launch holds Gram and
       // Square parts only
-      if (l.kind == kLkGramSquare ? pt.kind != kLkGram && pt.kind != kLkSquare : pt.kind != l.kind) return false;
+      if (l.kind == kLkChain ? pt.kind < kLkGram || pt.kind > kLkFinal
+          : l.kind == kLkGramSquare ? pt.kind != kLkGram && pt.kind != kLkSquare
+                                    : pt.kind != l.kind)
+        return false;
       // a capturing Square (b A from its R tile) must not read a pair: the
       // capture is taken in the first pass only
       if (pt.kind == kLkSquare && pt.cb != 0.f && (pt.l_lo != kBufNone || pt.r_lo != kBufNone)) return false;
@@ -903,6 +1065,7 @@ bool plan_consistent(const Plan &p) {
         return false;
       if (l.role == 2 && (e.k1 != 0 || e.k0 < 1 || e.slot < 0 || e.slot + e.k0 > p.splitk_slots)) return false;
     }
+    if (l.kind == kLkChain && !chain_consistent(p, l)) return false;
   }
   return true;
 }
@@ -934,7 +1097,10 @@ std::vector<MatDev> table_contents(const Plan &p, size_t t) {
       d.cc = pt.cc;
       d.cdiag = pt.cdiag;
       d.first_it = pt.first;
-      d.gemm_kind = pt.kind == kLkGram ? kModeGram : kModeSquare;
+      d.gemm_kind = pt.kind == kLkGram     ? kModeGram
+                    : pt.kind == kLkSquare ? kModeSquare
+                    : pt.kind == kLkApply  ? kModeApply
+                                           : kModeFinal;
       out.push_back(d);
     }
   }
@@ -1289,7 +1455,13 @@ static int muon_step_impl(const dmuon_matrix *mats, int32_t n, const dmuon_step_
                                                         : kModeFinal;
         const TileEntry *tl = reinterpret_cast<const TileEntry *>(ws + p.off_list[l.list]);
         float *splitk = p.off_splitk >= 0 ? reinterpret_cast<float *>(ws + p.off_splitk) : nullptr;
-        if (l.tile == 128)
+        if (l.kind == kLkChain) {
+          int32_t *const sync = reinterpret_cast<int32_t *>(ws + p.off_chain);
+          rc = check_launch(launch_zero_i32(sync, kChainCounters + p.chain_counters, s), "chained launch reset");
+          if (!rc)
+            rc = launched(launch_ns_chain(dtab(l.table), tl, p.list_xcd[l.list], sc, sync, s),
+                          "chained Newton-Schulz launch");
+        } else if (l.tile == 128)
           rc = launched(launch_ns_small_square(dtab(l.table), tl, p.list_xcd[l.list], sc, s),
                         "Newton-Schulz stage launch (128-tiles)");
         else

@@ -193,6 +193,13 @@ hipError_t launch_ns_stage(GemmMode mode, bool fp32, int role, const MatDev *mat
                            StepScalars s, float *splitk, hipStream_t st);
 // A bf16 Square launch of 128 x 128 tiles (TileEntry ti, tj in 128-tile
 // units; whole tiles only).
+// The chained mode's one launch of every bf16 stage (gemm.hip): sync holds
+// kXcds tickets, a timeout word and the stage counters from kChainCounters,
+// all zero at the start (launch_zero_i32).
+constexpr int32_t kChainCounters = 16;
+hipError_t launch_ns_chain(const MatDev *mats, const TileEntry *tiles, const StageXcd &xcd, StepScalars s,
+                           int32_t *sync, hipStream_t st);
+hipError_t launch_zero_i32(int32_t *p, int64_t n, hipStream_t st);
 hipError_t launch_ns_small_square(const MatDev *mats, const TileEntry *tiles, const StageXcd &xcd,
                                   StepScalars s, hipStream_t st);
 

@@ -382,3 +382,36 @@ def test_concurrent_host_calls_agree():
     assert len(got) == 8 * 3 * 16 * len(opts)
     for (t, rep, i, j), v in got.items():
         assert v == want[(i, j)], (t, rep, sets[i], j)
+
+
+def test_chain_launch_plan():
+    """DMUON_FLAG_CHAIN_LAUNCH: every bf16 product of the step is one launch
+    (kind "chain", the grouped plan's flops in total, 256-tiles); matrices
+    with m < 128 keep their fp32 grouped launches; the plan's waits pass the
+    library's consistency check (every wait on earlier entries of the same
+    XCD queue), over random shape mixes, both chains, ns_steps 1 to 8."""
+    import numpy as np
+    from synth import workload
+    shapes = [(r, c) for _, r, c in workload(2).shapes]
+    for gram in (False, True):
+        grouped = nsd.step_launches(shapes, nsd.StepOptions(gram_ns=gram))
+        L = nsd.step_launches(shapes, nsd.StepOptions(gram_ns=gram, chain_launch=True), tiles=True)
+        assert [k for k, _, _ in L] == ["momentum_orient", "norm", "chain"]
+        assert L[2][2] == 256
+        assert L[2][1] == sum(f for k, f in grouped if k not in ("momentum_orient", "norm"))
+    L = nsd.step_launches([(300, 700), (17, 33)], nsd.StepOptions(chain_launch=True))
+    kinds = [k for k, _ in L]
+    assert kinds[:3] == ["momentum_orient", "norm", "chain"] and "final" in kinds[3:]
+    assert nsd.step_launches([(300, 700)], nsd.StepOptions(ns_steps=0, chain_launch=True)) == \
+        nsd.step_launches([(300, 700)], nsd.StepOptions(ns_steps=0))
+    rng = np.random.default_rng(3)
+    for _ in range(24):
+        n = int(rng.integers(1, 20))
+        sh = [(int(rng.choice([1, 17, 256, 300, 513, 1024, 2000])),
+               int(rng.choice([1, 33, 256, 700, 1024, 4096]))) for _ in range(n)]
+        for k in (1, 2, 5, 6, 8):
+            for gram in (False, True):
+                o = nsd.StepOptions(ns_steps=k, gram_ns=gram, chain_launch=True)
+                L = nsd.step_launches(sh, o)   # runs the consistency check
+                assert sum(f for _, f in L) == sum(f for _, f in nsd.step_launches(sh, nsd.StepOptions(
+                    ns_steps=k, gram_ns=gram)))
