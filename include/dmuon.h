@@ -111,8 +111,8 @@ enum {
    * wait that exceeds about a second gives up (the result is then wrong, the
    * step always ends).  Off by default: pinning each matrix to one XCD
    * makes the XCDs stream different matrices at once, and on the
-   * Llama-3.1-8B owner share the step is about 28% slower than with the
-   * grouped launches even with every wait removed. */
+   * Llama-3.1-8B owner share the step is about a third slower than with
+   * the grouped launches (a quarter even with every wait removed). */
   DMUON_FLAG_CHAIN_LAUNCH = 1u << 4
 };
 

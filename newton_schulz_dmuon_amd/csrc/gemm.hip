@@ -1048,9 +1048,12 @@ void ns_gemm_small_kernel(const MatDev *__restrict__ mats, const TileEntry *__re
 // signals.  An entry waits only on entries earlier in the same queue, which
 // running work-groups took before it, so every wait ends; a wait that has not
 // ended after kChainSpinLimit polls sets the timeout word and goes on (wrong
-// values, never a hang).  Producer and consumer share the XCD's L2: the
-// producer's stores have reached it (vmcnt) before it signals, and the
-// consumer drops its CU's L1 lines before it reads.
+// values, never a hang).  A matrix's producers and consumers run on one XCD
+// and share its L2: a producer signals once its stores have reached L2
+// (vmcnt), and a consumer takes an agent-scope acquire after its wait,
+// which drops its CU's L1 lines (a workgroup-scope invalidate let stale L1
+// lines through; an agent-scope release, an L2 write-back per tile, is not
+// needed on one L2 and cost a third of the step).
 // Entry fields: k0 = counter waited on (-1: none), k1 = the count it waits
 // for, slot = counter signalled.  sync: kXcds tickets, the timeout word at
 // kXcds, counters from kChainCounters.
@@ -1086,7 +1089,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_chain_kernel(const MatDev *_
       }
     }
     __syncthreads();
-    asm volatile("buffer_inv sc0\n\ts_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   const MatDev &d = mats[e.mat];
   switch (d.gemm_kind) {
@@ -1103,7 +1106,7 @@ __global__ __launch_bounds__(kThreads) void ns_gemm_chain_kernel(const MatDev *_
       gemm_tile<uint16_t, kModeFinal, kRoleWhole>(lds, d, e, s, nullptr);
       break;
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores have reached L2
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's stores have reached the XCD's L2
   __syncthreads();
   if (threadIdx.x == 0)
     __hip_atomic_fetch_add(sync + kChainCounters + e.slot, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
