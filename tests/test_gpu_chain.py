@@ -62,3 +62,58 @@ def test_chain_launch_equals_grouped_launches(nsd, gram):
             for i, (x, y) in enumerate(zip(g, w)):
                 assert np.array_equal(x, y), (rep, name, i, shapes[i], int((x != y).sum()))
     say(f"chained step bit-equal to the grouped launches (gram_ns {gram}), twice")
+
+
+def _run(nsd, case, opts, noalloc=False):
+    from _gpu_util import to_dev
+    P = [to_dev(p, case.pdt) for p in case.P]
+    G = [to_dev(g, case.gdt) for g in case.G]
+    M = [to_dev(m, "f32") for m in case.M]
+    O = [torch.empty_like(p) for p in P]
+    ws = None
+    if noalloc:
+        nsd.muon_step_noalloc(P, G, M, case.scales, opts, orth_out=O)
+    else:
+        ws = nsd.Workspace()
+        nsd.muon_step(P, G, M, case.scales, opts, orth_out=O, workspace=ws)
+    torch.cuda.synchronize()
+    flags = nsd.nonfinite_flags(P, opts, ws).cpu().tolist() if opts.check_finite and ws is not None else None
+    return [t.float().cpu() for t in P + M + O], flags
+
+
+def test_chain_launch_with_nesterov_and_finite_check(nsd):
+    """Nesterov look-ahead and the non-finite check in the chained mode: the
+    same bits as the grouped launches with the same flags (shapes whose
+    grouped launches run whole 256-tiles), and every flag zero."""
+    shapes = [(2048, 4096)] * 4 + [(4096, 4096)] * 2
+    base = dict(ns_steps=5, gram_ns=True, nesterov=True, check_finite=True)
+    grouped = nsd.StepOptions(**base)
+    L = nsd.step_launches(shapes, grouped, tiles=True)
+    assert all(t in (0, 256) for _, _, t in L) and all(f > 0 for kd, f, t in L if t), L
+    case = Case(shapes, "bf16", "bf16", seed=97, m_std=1e-3)
+    want, wflags = _run(nsd, case, grouped)
+    got, flags = _run(nsd, case, nsd.StepOptions(chain_launch=True, **base))
+    for i, (x, y) in enumerate(zip(got, want)):
+        assert torch.equal(x, y), i
+    assert flags == wflags == [0] * len(shapes)
+    say("chained step with Nesterov and the non-finite check: bit-equal to the grouped launches")
+
+
+def test_chain_launch_without_allocation(nsd):
+    """The chained mode through the entry point that allocates nothing (its
+    tickets and counters in the static scratch): the same bits as the
+    chained step with a workspace, on two calls in a row (the second
+    smaller), and within the bars of the oracle."""
+    for k, (shapes, ns) in enumerate([([(300, 700), (700, 300), (513, 513), (1024, 2048)], 5),
+                                      ([(200, 600), (17, 33)], 8)]):
+        opts = nsd.StepOptions(ns_steps=ns, gram_ns=True, chain_launch=True)
+        case = Case(shapes, "bf16", "bf16", seed=98 + k, m_std=1e-3)
+        got, _ = _run(nsd, case, opts, noalloc=True)
+        want, _ = _run(nsd, case, opts)
+        for i, (x, y) in enumerate(zip(got, want)):
+            assert torch.equal(x, y), (k, i)
+        n = len(shapes)
+        err = check_step(case, opts, ([x.double().numpy() for x in got[:n]],
+                                      [x.double().numpy() for x in got[n:2 * n]],
+                                      [x.double().numpy() for x in got[2 * n:]]), case.run_oracle(opts))
+        say(f"chained step without allocation {shapes}: bit-equal; O rel err {err:.3e}")
