@@ -527,29 +527,26 @@ void chain_launch(Plan &p, const std::vector<Launch> &in_chain) {
   }
   // counters: one per (matrix, launch); each row waits on its matrix's
   // previous launch
-  std::map<std::pair<int32_t, int32_t>, int32_t> counter;
-  std::map<int32_t, int64_t> tiles_in;  // counter -> tiles that signal it
-  std::vector<int32_t> last(n, -1);     // the matrix's latest counter so far
+  // (matrix, launch) -> its counter and the counter it waits on
+  std::map<std::pair<int32_t, int32_t>, std::pair<int32_t, int32_t>> counter;
+  std::vector<int64_t> tiles_in;      // counter -> tiles that signal it
+  std::vector<int32_t> last(n, -1);   // the matrix's latest counter so far
   std::vector<int32_t> wait_on(rows.size(), -1), sig(rows.size(), -1);
   for (const Row &r : rows) {
     auto key = std::make_pair(r.mat, r.launch);
     auto it = counter.find(key);
     if (it == counter.end()) {
-      wait_on[r.row] = last[r.mat];
-      it = counter.emplace(key, static_cast<int32_t>(counter.size())).first;
-      last[r.mat] = it->second;
-    } else {
-      // a second row of the matrix in the same launch waits as the first did
-      for (const Row &q : rows)
-        if (q.row < r.row && q.mat == r.mat && q.launch == r.launch) {
-          wait_on[r.row] = wait_on[q.row];
-          break;
-        }
+      // a second row of the matrix in the same launch finds this entry and
+      // waits as the first did
+      it = counter.emplace(key, std::make_pair(static_cast<int32_t>(tiles_in.size()), last[r.mat])).first;
+      tiles_in.push_back(0);
+      last[r.mat] = it->second.first;
     }
-    sig[r.row] = it->second;
-    tiles_in[it->second] += tiles_of(r);
+    sig[r.row] = it->second.first;
+    wait_on[r.row] = it->second.second;
+    tiles_in[it->second.first] += tiles_of(r);
   }
-  p.chain_counters = static_cast<int64_t>(counter.size());
+  p.chain_counters = static_cast<int64_t>(tiles_in.size());
   std::vector<TileEntry> lists[kXcds];
   for (const Row &r : rows) {
     const MatDev &d = p.mats[r.mat];
