@@ -91,7 +91,11 @@ enum {
    * n = 3.5m and ns_steps = 5.  Phases are two iterations (5 -> 2 + 2 + 1),
    * each restarting from an explicit X, which bounds the bf16 rounding of the
    * accumulated Q: on a rank-one-plus-noise input (GPU test) the error stays
-   * within 1.2x of the direct chain's. */
+   * within 1.2x of the direct chain's, and on Gaussian gradients within the
+   * 2e-2 bar.  Its limit: when the singular values spread over one or two
+   * decades, the bf16 storage of its m x m products makes it 2-3x less
+   * accurate than the direct chain and above 2e-2 (GPU test on 256 x 1024:
+   * 3.0e-2 against 1.1e-2).  Hence opt-in. */
   DMUON_FLAG_GRAM_NS = 1u << 2,
   /* Record, per matrix, whether the Newton-Schulz input U (M after the
    * momentum update, or the Nesterov look-ahead) holds a NaN or an Inf:

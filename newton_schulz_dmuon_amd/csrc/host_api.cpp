@@ -342,7 +342,10 @@ bool split_pairs(const dmuon_step_config &cfg) {
 // X <- Q X.  Over a phase Q's eigenvalues reach a^L on the directions of
 // small singular values, and its bf16 rounding is relative to that: phases
 // of three lose accuracy on ill-conditioned inputs (rank one plus noise:
-// 4-5x the direct chain's error), phases of two stay at 0.5-1.05x of it.
+// 4-5x the direct chain's error), phases of two stay at 0.5-1.05x of it
+// there and on Gaussian inputs.  With singular values spread over one or
+// two decades the chain is 2-3x less accurate than the direct one whatever
+// the split: that loss is in the bf16 storage of P, T and Q themselves.
 std::vector<int> gram_phases(int K) {
   std::vector<int> L(K / 2, 2);
   if (K % 2) L.push_back(1);
