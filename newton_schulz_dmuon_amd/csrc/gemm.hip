@@ -729,7 +729,12 @@ __device__ __forceinline__ void gemm_tile(lds_char *const lds, const MatDev &d, 
 
   // The first iteration's X is U unnormalised (X0 = U * inv_norm): A0 picks
   // up inv_norm^2 and the first X' (or O) inv_norm.
-  const float inv = d.first_it ? *(const g_f32 *)d.inv_norm : 1.f;
+  // A scalar load (written by an earlier kernel, uniform in the work-group):
+  // as a vector load it would be counted with the LDS-bound loads, and the
+  // compiler, which does not see the mainloop's own waits, would wait for
+  // every outstanding vector load (Final's parameter reads included) at its
+  // first use.
+  const float inv = d.first_it ? *(const __attribute__((address_space(4))) float *)d.inv_norm : 1.f;
   const float gram_scale = inv * inv;
   if (MODE == kModeGram || MODE == kModeSquare) {
     T *out = static_cast<T *>(MODE == kModeGram ? d.a : d.b);
@@ -871,6 +876,9 @@ __device__ __forceinline__ void gemm_tile(lds_char *const lds, const MatDev &d, 
     const bool tp = d.transposed != 0;
     // rows of P start 16-byte aligned (the buffers are: the host checks)
     const bool vec_ok = (d.cols & 7) == 0;
+    // the tile lies wholly inside P and every piece is a full vector
+    const bool whole = vec_ok && (tp ? (tj + 1) * kTile <= d.rows && (ti + 1) * kTile <= d.cols
+                                     : (ti + 1) * kTile <= d.rows && (tj + 1) * kTile <= d.cols);
     typedef __attribute__((address_space(3))) float lds_f32;
     typedef __attribute__((address_space(3))) u32x4 lds_v4;
     // [128][256] fp32, 1 KB rows: chunk XOR 4 * ((row / 4) mod 4), so the four
@@ -916,20 +924,9 @@ __device__ __forceinline__ void gemm_tile(lds_char *const lds, const MatDev &d, 
         pc_.idx = pr * d.cols + pcol;
         return pc_;
       };
-      typename Vec8<PT>::Raw pre[kPre ? kWavesM : 1][kPre ? kPieces : 1];
-      if constexpr (kPre) {
-#pragma unroll
-        for (int h = 0; h < kWavesM; ++h)
-#pragma unroll
-          for (int q = 0; q < kPieces; ++q) {
-            const Piece pp = piece_of(h, q);
-            if (vec_ok && pp.n == 8) pre[h][q] = Vec8<PT>::raw(P + pp.idx);
-          }
-      }
-#pragma unroll
-      for (int h = 0; h < kWavesM; ++h) {
-        auto piece = [&](int q) { return piece_of(h, q); };
-        if (h > 0) lds_barrier();  // the previous half has been read
+      // O of half h into LDS (the previous half read first)
+      auto stage_half = [&](int h) {
+        if (h > 0) lds_barrier();
         if (wm == h) {
 #pragma unroll
           for (int i = 0; i < kFragM; ++i)
@@ -949,6 +946,63 @@ __device__ __forceinline__ void gemm_tile(lds_char *const lds, const MatDev &d, 
             }
         }
         lds_barrier();
+      };
+      // the staged O of piece pp, its eight values in column order
+      auto staged = [&](const Piece &pp, float (&o)[8]) {
+        auto at = [&](int c) { return tp ? ot_at(pp.r, c) : o_at(pp.r, c); };
+        const u32x4 u0 = *(const lds_v4 *)(lds + at(pp.c + 4 * sw));
+        const u32x4 u1 = *(const lds_v4 *)(lds + at(pp.c + 4 - 4 * sw));
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          o[v] = __uint_as_float(sw ? u1[v] : u0[v]);
+          o[4 + v] = __uint_as_float(sw ? u0[v] : u1[v]);
+        }
+      };
+      if constexpr (kPre) {
+        if (whole) {
+          // A whole tile runs with no branch from its parameter reads to
+          // its last store, so that the compiler waits for each piece's
+          // own read (a counted vmcnt).  With a branch in between it waits
+          // for every outstanding access, the previous pieces' stores
+          // included, and each piece pays a store's whole latency.
+          typename Vec8<PT>::Raw pw[kWavesM][kPieces];
+#pragma unroll
+          for (int h = 0; h < kWavesM; ++h)
+#pragma unroll
+            for (int q = 0; q < kPieces; ++q) pw[h][q] = Vec8<PT>::raw(P + piece_of(h, q).idx);
+#pragma unroll
+          for (int h = 0; h < kWavesM; ++h) {
+            stage_half(h);
+#pragma unroll
+            for (int q = 0; q < kPieces; ++q) {
+              const Piece pp = piece_of(h, q);
+              float o[8], pv[8], nv[8];
+              staged(pp, o);
+              Vec8<PT>::cvt(pw[h][q], pv);
+#pragma unroll
+              for (int v = 0; v < 8; ++v) nv[v] = fmaf(-step, o[v], pv[v]);
+              Vec8<PT>::st(P + pp.idx, nv);
+              if (Packed) Vec8<PT>::st(Packed + pp.idx, nv);
+              if (Orth) Vec8<PT>::st(Orth + pp.idx, o);
+            }
+          }
+          return;
+        }
+      }
+      typename Vec8<PT>::Raw pre[kPre ? kWavesM : 1][kPre ? kPieces : 1];
+      if constexpr (kPre) {
+#pragma unroll
+        for (int h = 0; h < kWavesM; ++h)
+#pragma unroll
+          for (int q = 0; q < kPieces; ++q) {
+            const Piece pp = piece_of(h, q);
+            if (vec_ok && pp.n == 8) pre[h][q] = Vec8<PT>::raw(P + pp.idx);
+          }
+      }
+#pragma unroll
+      for (int h = 0; h < kWavesM; ++h) {
+        auto piece = [&](int q) { return piece_of(h, q); };
+        stage_half(h);
 #pragma unroll
         for (int q0 = 0; q0 < kPieces; q0 += kBatch) {
           typename Vec8<PT>::Raw praw[kBatch];
@@ -964,15 +1018,8 @@ __device__ __forceinline__ void gemm_tile(lds_char *const lds, const MatDev &d, 
           for (int qq = 0; qq < kBatch; ++qq) {
             const Piece pp = piece(q0 + qq);
             if (pp.n == 0) continue;
-            auto at = [&](int c) { return tp ? ot_at(pp.r, c) : o_at(pp.r, c); };
-            const u32x4 u0 = *(const lds_v4 *)(lds + at(pp.c + 4 * sw));
-            const u32x4 u1 = *(const lds_v4 *)(lds + at(pp.c + 4 - 4 * sw));
             float o[8];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              o[v] = __uint_as_float(sw ? u1[v] : u0[v]);
-              o[4 + v] = __uint_as_float(sw ? u0[v] : u1[v]);
-            }
+            staged(pp, o);
             if (vec_ok && pp.n == 8) {
               float pv[8], nv[8];
               Vec8<PT>::cvt(praw[qq], pv);
