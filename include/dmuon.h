@@ -113,7 +113,8 @@ enum {
    * grouped launches bit for bit where those use whole 256-tiles.
    * Matrices that run their chain in fp32 keep their grouped launches.  A
    * wait that exceeds about a second gives up (the result is then wrong, the
-   * step always ends).  Off by default: pinning each matrix to one XCD
+   * step always ends, and the status word of dmuon_chain_status_offset
+   * reads 1).  Off by default: pinning each matrix to one XCD
    * makes the XCDs stream different matrices at once, and on the
    * Llama-3.1-8B owner share the step is about a third slower than with
    * the grouped launches (a quarter even with every wait removed). */
@@ -232,6 +233,18 @@ int dmuon_step_launches(const dmuon_matrix *mats, int32_t n,
  * of dmuon_workspace_bytes. */
 int dmuon_nonfinite_flags_offset(const dmuon_matrix *mats, int32_t n,
                                  const dmuon_step_config *cfg, size_t *offset_out);
+
+/* Byte offset in the workspace of the int32 status word of a step with
+ * DMUON_FLAG_CHAIN_LAUNCH: the step clears it, and a wait that gives up
+ * sets it to 1 (that step's result is then wrong).  Valid once the step
+ * has completed on its stream, until the workspace is used again.  The
+ * step that allocates nothing keeps this word in its own scratch instead.
+ * Host-only.
+ * Errors: INVALID_ARG (offset_out NULL, the flag not set in cfg, or a step
+ * with no chained launch: ns_steps = 0, or every matrix in fp32) and those
+ * of dmuon_workspace_bytes. */
+int dmuon_chain_status_offset(const dmuon_matrix *mats, int32_t n,
+                              const dmuon_step_config *cfg, size_t *offset_out);
 
 /* Bytes of device workspace dmuon_muon_step needs for these matrices and
  * flags.  Host-only; validates like dmuon_muon_step except for pointers. */

@@ -6,5 +6,5 @@ from the HIP sources in ``csrc/``.  This package is its thin binding.
 
 from ._lib import DmuonError, load  # noqa: F401
 from .api import (QUINTIC, AdamWOptions, StepOptions, Workspace, adamw_step,  # noqa: F401
-                  muon_step, muon_step_noalloc, nonfinite_flags, pack, pack_offsets,
+                  chain_status, muon_step, muon_step_noalloc, nonfinite_flags, pack, pack_offsets,
                   partition_lpt, step_launches, unpack, workspace_bytes)

@@ -42,7 +42,8 @@ EXPORTED = ("dmuon_abi_version", "dmuon_error_string", "dmuon_last_error",
             "dmuon_partition_lpt", "dmuon_pack_offsets", "dmuon_workspace_bytes",
             "dmuon_pack", "dmuon_unpack", "dmuon_muon_step", "dmuon_muon_step_traced",
             "dmuon_muon_step_packed", "dmuon_adamw_step", "dmuon_step_launches",
-            "dmuon_nonfinite_flags_offset", "dmuon_muon_step_noalloc")
+            "dmuon_nonfinite_flags_offset", "dmuon_muon_step_noalloc",
+            "dmuon_chain_status_offset")
 
 # DMUON_NOALLOC_SCRATCH_BYTES
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -145,11 +146,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dmuon_step_launches.argtypes = [P(Matrix), c_i32, P(StepConfig), P(LaunchInfo), c_i32,
                                         P(c_i32)]
     lib.dmuon_nonfinite_flags_offset.argtypes = [P(Matrix), c_i32, P(StepConfig), P(ctypes.c_size_t)]
+    lib.dmuon_chain_status_offset.argtypes = [P(Matrix), c_i32, P(StepConfig), P(ctypes.c_size_t)]
     lib.dmuon_muon_step_noalloc.argtypes = [P(Matrix), c_i32, P(StepConfig), vp]
     for name in ("dmuon_partition_lpt", "dmuon_pack_offsets", "dmuon_workspace_bytes",
                  "dmuon_pack", "dmuon_unpack", "dmuon_muon_step", "dmuon_muon_step_traced",
                  "dmuon_muon_step_packed", "dmuon_adamw_step", "dmuon_step_launches",
-                 "dmuon_nonfinite_flags_offset", "dmuon_muon_step_noalloc"):
+                 "dmuon_nonfinite_flags_offset", "dmuon_muon_step_noalloc",
+                 "dmuon_chain_status_offset"):
         getattr(lib, name).restype = ctypes.c_int
     if lib.dmuon_abi_version() != ABI_VERSION:
         raise ImportError(f"libdmuon ABI {lib.dmuon_abi_version()} != {ABI_VERSION}")

@@ -142,6 +142,20 @@ def nonfinite_flags(params, opts: StepOptions, workspace: Workspace):
     return workspace.buf[off.value:off.value + 4 * n].view(torch.int32)
 
 
+def chain_status(params, opts: StepOptions, workspace: Workspace):
+    """The status word a step with ``opts.chain_launch`` left in
+    ``workspace``: a one-element device int32 tensor, 1 if a wait of the
+    chained launch gave up (that step's result is wrong), else 0.  A view of
+    the workspace; read it after the step's stream has synchronised and
+    before the workspace is used again."""
+    import torch
+    arr, n = matrices(params)
+    off = ctypes.c_size_t(0)
+    cfg = opts.to_c()
+    check(load().dmuon_chain_status_offset(arr, n, ctypes.byref(cfg), ctypes.byref(off)))
+    return workspace.buf[off.value:off.value + 4].view(torch.int32)
+
+
 def workspace_bytes(params, opts: StepOptions) -> int:
     arr, n = matrices(params)
     out = ctypes.c_size_t(0)

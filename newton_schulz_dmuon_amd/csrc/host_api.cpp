@@ -1290,6 +1290,26 @@ int dmuon_nonfinite_flags_offset(const dmuon_matrix *mats, int32_t n, const dmuo
   return DMUON_OK;
 }
 
+int dmuon_chain_status_offset(const dmuon_matrix *mats, int32_t n, const dmuon_step_config *cfg,
+                              size_t *offset_out) {
+  g_last_error.clear();
+  if (!offset_out) return fail(DMUON_ERR_INVALID_ARG, "offset_out is NULL");
+  int rc = validate_config(cfg);
+  if (rc) return rc;
+  if (!(cfg->flags & DMUON_FLAG_CHAIN_LAUNCH))
+    return fail(DMUON_ERR_INVALID_ARG, "DMUON_FLAG_CHAIN_LAUNCH is not set");
+  rc = validate_shapes(mats, n);
+  if (rc) return rc;
+  rc = validate_step_shapes(mats, n);
+  if (rc) return rc;
+  Plan p;
+  build_plan(mats, n, *cfg, nullptr, p);
+  if (p.off_chain < 0) return fail(DMUON_ERR_INVALID_ARG, "the step has no chained launch");
+  // the word after the per-XCD tickets
+  *offset_out = static_cast<size_t>(p.off_chain) + sizeof(int32_t) * kXcds;
+  return DMUON_OK;
+}
+
 int dmuon_workspace_bytes(const dmuon_matrix *mats, int32_t n, const dmuon_step_config *cfg,
                           size_t *out_bytes) {
   g_last_error.clear();

@@ -99,6 +99,28 @@ def test_chain_launch_with_nesterov_and_finite_check(nsd):
     say("chained step with Nesterov and the non-finite check: bit-equal to the grouped launches")
 
 
+def test_chain_status_word_is_cleared_and_stays_zero(nsd):
+    """The status word of the chained step (dmuon_chain_status_offset): the
+    step clears it (here pre-set to 7) and no wait gives up, so it reads 0
+    after the step."""
+    from _gpu_util import to_dev
+    shapes = [(300, 700), (700, 300), (513, 513), (1024, 2048)]
+    opts = nsd.StepOptions(ns_steps=5, gram_ns=True, chain_launch=True)
+    case = Case(shapes, "bf16", "bf16", seed=96, m_std=1e-3)
+    P = [to_dev(p, case.pdt) for p in case.P]
+    G = [to_dev(g, case.gdt) for g in case.G]
+    M = [to_dev(m, "f32") for m in case.M]
+    ws = nsd.Workspace()
+    ws.get(nsd.workspace_bytes(P, opts), P[0].device)
+    word = nsd.chain_status(P, opts, ws)
+    word.fill_(7)
+    torch.cuda.synchronize()
+    nsd.muon_step(P, G, M, case.scales, opts, workspace=ws)
+    torch.cuda.synchronize()
+    assert word.item() == 0
+    say("chained step: status word cleared, no wait gave up")
+
+
 def test_chain_launch_without_allocation(nsd):
     """The chained mode through the entry point that allocates nothing (its
     tickets and counters in the static scratch): the same bits as the

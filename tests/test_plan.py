@@ -415,3 +415,32 @@ def test_chain_launch_plan():
                 L = nsd.step_launches(sh, o)   # runs the consistency check
                 assert sum(f for _, f in L) == sum(f for _, f in nsd.step_launches(sh, nsd.StepOptions(
                     ns_steps=k, gram_ns=gram)))
+
+
+def test_chain_status_offset():
+    """DMUON_FLAG_CHAIN_LAUNCH: the status word sits 4-byte aligned inside
+    the workspace, after the per-XCD tickets and before its end; the offset
+    call is an error without the flag, without an output pointer, and for a
+    step with no chained launch (ns_steps = 0, or only fp32 matrices)."""
+    lib = _lib.load()
+
+    def call(shapes, opts, out=True):
+        arr = (_lib.Matrix * len(shapes))(*[_lib.Matrix(None, 0, 0, None, None, None, r, c, 1.0, 0, 0)
+                                            for r, c in shapes])
+        cfg = opts.to_c()
+        off, total = ctypes.c_size_t(0), ctypes.c_size_t(0)
+        rc = lib.dmuon_chain_status_offset(arr, len(shapes), ctypes.byref(cfg),
+                                           ctypes.byref(off) if out else None)
+        if rc == _lib.OK:
+            _lib.check(lib.dmuon_workspace_bytes(arr, len(shapes), ctypes.byref(cfg), ctypes.byref(total)))
+        return rc, off.value, total.value
+
+    shapes = [(300, 700), (17, 33), (513, 513)]
+    for gram in (False, True):
+        for k in (1, 5, 8):
+            rc, off, total = call(shapes, nsd.StepOptions(ns_steps=k, gram_ns=gram, chain_launch=True))
+            assert rc == _lib.OK and off % 4 == 0 and off + 4 <= total, (gram, k, off, total)
+    assert call(shapes, nsd.StepOptions())[0] == _lib.ERR_INVALID_ARG
+    assert call(shapes, nsd.StepOptions(chain_launch=True), out=False)[0] == _lib.ERR_INVALID_ARG
+    assert call(shapes, nsd.StepOptions(ns_steps=0, chain_launch=True))[0] == _lib.ERR_INVALID_ARG
+    assert call([(17, 33)], nsd.StepOptions(chain_launch=True))[0] == _lib.ERR_INVALID_ARG
