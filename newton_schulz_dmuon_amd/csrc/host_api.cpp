@@ -232,13 +232,21 @@ void build_stage_tiles(const std::vector<MatDev> &mats, const std::vector<int32_
     const int bm = 4, bn = sym ? 4 : 8;
     const int64_t depth = (st == 0 ? d.np : d.mp) * passes[i];
     const int32_t rows = static_cast<int32_t>(d.mp / tile), cols = static_cast<int32_t>((sym ? d.mp : d.np) / tile);
-    for (int32_t bi = 0; bi < rows; bi += bm)
-      for (int32_t bj = sym ? bi : 0; bj < cols; bj += bn) {
-        int64_t nt = 0;
-        for (int32_t ti = bi; ti < std::min(bi + bm, rows); ++ti)
-          for (int32_t tj = bj; tj < std::min(bj + bn, cols); ++tj) nt += (!sym || tj >= ti);
-        if (nt) blocks.push_back(Block{nt * depth, i, bi, bj});
-      }
+    auto add = [&](int32_t bi, int32_t bj) {
+      int64_t nt = 0;
+      for (int32_t ti = bi; ti < std::min(bi + bm, rows); ++ti)
+        for (int32_t tj = bj; tj < std::min(bj + bn, cols); ++tj) nt += (!sym || tj >= ti);
+      if (nt) blocks.push_back(Block{nt * depth, i, bi, bj});
+    };
+    if (sym) {
+      for (int32_t bi = 0; bi < rows; bi += bm)
+        for (int32_t bj = bi; bj < cols; bj += bn) add(bi, bj);
+    } else {
+      // column of blocks by column of blocks: the XCDs that start together
+      // take blocks of one column, which share its R panels
+      for (int32_t bj = 0; bj < cols; bj += bn)
+        for (int32_t bi = 0; bi < rows; bi += bm) add(bi, bj);
+    }
   }
   std::stable_sort(blocks.begin(), blocks.end(),
                    [](const Block &x, const Block &y) { return x.cost > y.cost; });
