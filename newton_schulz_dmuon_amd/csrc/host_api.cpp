@@ -248,8 +248,17 @@ void build_stage_tiles(const std::vector<MatDev> &mats, const std::vector<int32_
         for (int32_t bi = 0; bi < rows; bi += bm) add(bi, bj);
     }
   }
-  std::stable_sort(blocks.begin(), blocks.end(),
-                   [](const Block &x, const Block &y) { return x.cost > y.cost; });
+  // Costliest first; but a symmetric stage keeps each matrix's blocks
+  // together (ordered by the matrix's whole cost), so that its diagonal
+  // blocks run while its panels are still near, not after every matrix's
+  // full blocks
+  std::vector<int64_t> mat_cost(mats.size(), 0);
+  for (const Block &b : blocks) mat_cost[b.mat] += b.cost;
+  std::stable_sort(blocks.begin(), blocks.end(), [&](const Block &x, const Block &y) {
+    const bool sx = stages[x.mat] < 2, sy = stages[y.mat] < 2;
+    const int64_t cx = sx ? mat_cost[x.mat] : x.cost, cy = sy ? mat_cost[y.mat] : y.cost;
+    return cx > cy;
+  });
   std::vector<TileEntry> lists[kXcds];
   int64_t load[kXcds] = {0};
   for (const Block &b : blocks) {
