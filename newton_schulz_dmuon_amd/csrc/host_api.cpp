@@ -210,13 +210,18 @@ struct Plan {
 
 // Tile lists of one grouped GEMM launch, one per XCD; every matrix has its
 // stage (0 Gram, 1 Square, 2 Apply; a launch can hold Gram and Square
-// matrices).  Tiles are grouped into blocks that share operand panels: 4 x 4 tile
-// blocks of the upper triangle for the symmetric products (they read panels
-// ti and tj of one matrix), 4 x 8 blocks for Apply (B panel ti, X^T panel
-// tj).  Blocks go, costliest first (tiles x K depth, ties in matrix order),
-// to the XCD with the least work so far; each XCD's list keeps that order, so
-// its 32 CUs work through long-K tiles first and the tiles running together
-// on one XCD read few distinct panels through its L2.
+// matrices).  Tiles are grouped into 4 x 8 blocks that share operand panels
+// (the upper triangle's part of them for the symmetric products, which read
+// panels ti and tj of one matrix; B panel ti and X^T panel tj for Apply).
+// Blocks go, in order, to the XCD with the least work so far; each XCD's
+// list keeps that order, so the tiles running together on one XCD read few
+// distinct panels through its L2.  The order: a full stage's blocks
+// costliest first (tiles x K depth; ties in matrix order, each matrix's
+// blocks column by column, so that the XCDs starting together share the
+// X^T panels); a symmetric stage's blocks matrix by matrix, costliest matrix
+// first, each matrix's blocks together (its diagonal blocks, which hold
+// fewer tiles, would otherwise run after every matrix's full blocks, far
+// from the fetch of the panels they share).
 void build_stage_tiles(const std::vector<MatDev> &mats, const std::vector<int32_t> &passes,
                        const std::vector<int32_t> &stages, int32_t tile, std::vector<TileEntry> &out,
                        StageXcd &xcd) {
@@ -229,7 +234,7 @@ void build_stage_tiles(const std::vector<MatDev> &mats, const std::vector<int32_
     const MatDev &d = mats[i];
     const int32_t st = stages[i];
     const bool sym = st < 2;
-    const int bm = 4, bn = sym ? 4 : 8;
+    const int bm = 4, bn = 8;
     const int64_t depth = (st == 0 ? d.np : d.mp) * passes[i];
     const int32_t rows = static_cast<int32_t>(d.mp / tile), cols = static_cast<int32_t>((sym ? d.mp : d.np) / tile);
     auto add = [&](int32_t bi, int32_t bj) {
@@ -248,10 +253,7 @@ void build_stage_tiles(const std::vector<MatDev> &mats, const std::vector<int32_
         for (int32_t bi = 0; bi < rows; bi += bm) add(bi, bj);
     }
   }
-  // Costliest first; but a symmetric stage keeps each matrix's blocks
-  // together (ordered by the matrix's whole cost), so that its diagonal
-  // blocks run while its panels are still near, not after every matrix's
-  // full blocks
+  // costliest first; a symmetric stage by its matrices' whole cost (above)
   std::vector<int64_t> mat_cost(mats.size(), 0);
   for (const Block &b : blocks) mat_cost[b.mat] += b.cost;
   std::stable_sort(blocks.begin(), blocks.end(), [&](const Block &x, const Block &y) {
@@ -268,7 +270,7 @@ void build_stage_tiles(const std::vector<MatDev> &mats, const std::vector<int32_
     load[x] += b.cost;
     const MatDev &d = mats[b.mat];
     const bool sym = stages[b.mat] < 2;
-    const int bm = 4, bn = sym ? 4 : 8;
+    const int bm = 4, bn = 8;
     const int32_t rows = static_cast<int32_t>(d.mp / tile), cols = static_cast<int32_t>((sym ? d.mp : d.np) / tile);
     for (int32_t ti = b.ti0; ti < std::min(b.ti0 + bm, rows); ++ti)
       for (int32_t tj = b.tj0; tj < std::min(b.tj0 + bn, cols); ++tj)
