@@ -218,9 +218,13 @@ int dmuon_pack_offsets(const int64_t *numel, int32_t n, int64_t align,
 /* The launch sequence dmuon_muon_step runs for these matrices and flags, in
  * order (the events of dmuon_muon_step_traced follow it).  Writes the first
  * min(cap, count) entries of out[] and the total to *count.  Host-only;
- * validates like dmuon_workspace_bytes.
- * Errors: INVALID_ARG (count NULL, cap < 0, out NULL with cap > 0) and those
- * of dmuon_workspace_bytes. */
+ * validates like dmuon_workspace_bytes, and checks the plan beyond what a
+ * step checks: every GEMM launch computes each output tile of each of its
+ * matrices exactly once (split launches: its pieces cover the tile's K
+ * steps without gap or overlap).
+ * Errors: INVALID_ARG (count NULL, cap < 0, out NULL with cap > 0, or a plan
+ * that fails those checks, which is an internal error) and those of
+ * dmuon_workspace_bytes. */
 int dmuon_step_launches(const dmuon_matrix *mats, int32_t n,
                         const dmuon_step_config *cfg, dmuon_launch_info *out,
                         int32_t cap, int32_t *count);

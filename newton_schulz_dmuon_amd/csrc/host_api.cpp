@@ -1089,6 +1089,62 @@ bool plan_consistent(const Plan &p) {
   return true;
 }
 
+// Every GEMM launch computes each output tile of each of its table rows
+// exactly once: whole, chained and reduce entries once per tile (the upper
+// triangle for the symmetric products), and a split launch's pieces of a
+// tile cover its K steps without gap or overlap.  Checked by
+// dmuon_step_launches (the host tests), not on every step.
+bool plan_covers(const Plan &p) {
+  for (const Launch &l : p.prog) {
+    if (l.kind < kLkGram) continue;
+    std::vector<const MatDev *> rows;
+    std::vector<bool> row_sym;
+    for (const Part &pt : p.tables[l.table - 1])
+      for (int32_t i : p.groups[pt.group]) {
+        rows.push_back(&p.mats[i]);
+        row_sym.push_back(pt.kind == kLkGram || pt.kind == kLkSquare);
+      }
+    const std::vector<int64_t> rs = row_steps(p, l);
+    std::vector<int64_t> first(rows.size() + 1, 0);
+    for (size_t r = 0; r < rows.size(); ++r) {
+      const MatDev &d = *rows[r];
+      first[r + 1] = first[r] + (d.mp / l.tile) * ((row_sym[r] ? d.mp : d.np) / l.tile);
+    }
+    std::vector<int32_t> seen(static_cast<size_t>(first.back()), 0);
+    std::vector<std::vector<std::pair<int32_t, int32_t>>> pieces(l.role == 1 ? seen.size() : 0);
+    for (const TileEntry &e : p.lists[l.list]) {
+      const MatDev &d = *rows[e.mat];
+      const int64_t cols = (row_sym[e.mat] ? d.mp : d.np) / l.tile;
+      const int64_t at = first[e.mat] + e.ti * cols + e.tj;
+      if (l.role == 1)
+        pieces[at].emplace_back(e.k0, e.k1);
+      else if (seen[at]++)
+        return false;
+    }
+    for (size_t r = 0; r < rows.size(); ++r) {
+      const MatDev &d = *rows[r];
+      const int64_t nr = d.mp / l.tile, nc = (row_sym[r] ? d.mp : d.np) / l.tile;
+      for (int64_t ti = 0; ti < nr; ++ti)
+        for (int64_t tj = row_sym[r] ? ti : 0; tj < nc; ++tj) {
+          const int64_t at = first[r] + ti * nc + tj;
+          if (l.role != 1) {
+            if (seen[at] != 1) return false;
+            continue;
+          }
+          std::vector<std::pair<int32_t, int32_t>> &pc = pieces[at];
+          std::sort(pc.begin(), pc.end());
+          int64_t k = 0;
+          for (const auto &q : pc) {
+            if (q.first != k) return false;
+            k = q.second;
+          }
+          if (k != rs[r]) return false;
+        }
+    }
+  }
+  return true;
+}
+
 // The MatDev array of table t (0: every matrix; else, for each part of the
 // launch in turn, its group's matrices with the part's buffers, X^T order
 // and coefficients).
@@ -1531,6 +1587,7 @@ int dmuon_step_launches(const dmuon_matrix *mats, int32_t n, const dmuon_step_co
   Plan p;
   build_plan(mats, n, *cfg, nullptr, p);
   if (!plan_consistent(p)) return fail(DMUON_ERR_INVALID_ARG, "internal error: inconsistent launch plan");
+  if (!plan_covers(p)) return fail(DMUON_ERR_INVALID_ARG, "internal error: a launch misses or repeats a tile");
   *count = static_cast<int32_t>(p.prog.size());
   for (int32_t j = 0; j < cap && j < *count; ++j) {
     out[j].kind = p.prog[j].kind;

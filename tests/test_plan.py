@@ -182,9 +182,10 @@ def test_step_launches_errors():
 @pytest.mark.parametrize("seed", range(12))
 def test_random_plans_are_consistent(seed):
     """Random mixes of square, wide, tall and tiny matrices at every ns_steps
-    up to 10, both chains: the library's own consistency check of the plan
-    passes (every tile inside its launch's table and matrix) and the flop
-    count is the sum of the two chains' counts."""
+    up to 10, both chains: the library's own checks of the plan pass (every
+    tile inside its launch's table and matrix; every output tile computed
+    exactly once per launch, split tiles' pieces covering their K steps) and
+    the flop count is the sum of the two chains' counts."""
     import numpy as np
     rng = np.random.default_rng(seed)
     n = int(rng.integers(1, 30))
